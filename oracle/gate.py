@@ -1,0 +1,260 @@
+"""Numerics gate for target (kernel) outputs (test infrastructure only).
+
+Follows the torchtitan kernel-numerics-verifier page:
+
+* section "正确性判据" (correctness gate).  For each output tensor, in the
+  golden's float64::
+
+      reference_error = max|reference - golden|
+      target_error    = max|target - golden|
+      rounding_floor  = max|golden.to(target dtype).to(float64) - golden|
+      absolute_floor  = max(project_atol, rounding_floor)
+      threshold       = fudge_factor * reference_error + absolute_floor
+      PASS  iff  target_error <= threshold
+
+  The page's text lost its operators in extraction; the reading used here is
+  the one its prose supports ("the kernel error is at most fudge_factor times
+  the reference's, with the rounding floor added on top").
+* workflow step 3: structure first -- shape, dtype and the positions of NaN,
+  +Inf and -Inf must match before any number is compared.
+* section "先检查条件数" (conditioning first):
+  ``reference_error / max(max|golden|, absolute_floor)`` above
+  MAX_REFERENCE_RELATIVE_ERROR makes the gate invalid: no PASS/FAIL is given,
+  the verdict is INCONCLUSIVE.
+* section "结果报告规范" (report format): one row per tensor and one overall
+  verdict.
+
+The constants below were fixed before any kernel existed and are never raised
+to let a failing kernel through (same section of the page).
+
+Two checks are added on top of the page's gate and declared here with it:
+
+* rstd (the per-row inverse RMS the forward stores for the backward) must be
+  within RSTD_MAX_REL_ERROR of the golden r, relative, elementwise.
+* rounding bias: for bfloat16/float16 outputs the max-error gate cannot tell
+  round-to-nearest-even from truncation (truncation stays within one unit in
+  the last place), so the signed error measured along the sign of the golden,
+  ``sum(e * sign(golden)) / sum|e|``, must stay within ROUNDING_BIAS_MAX in
+  magnitude (truncation toward zero gives exactly -1; unbiased rounding ~0).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, asdict
+
+import numpy as np
+import torch
+
+# ---- constants, declared before any kernel ran -------------------------------
+FUDGE_FACTOR = 2.0
+PROJECT_ATOL = 0.0
+MAX_REFERENCE_RELATIVE_ERROR = 0.1
+RSTD_MAX_REL_ERROR = 1e-6
+ROUNDING_BIAS_MAX = 0.25
+ROUNDING_BIAS_MIN_ELEMENTS = 4096
+# ------------------------------------------------------------------------------
+
+_TORCH_DTYPES = {
+    "float32": torch.float32, "fp32": torch.float32, torch.float32: torch.float32,
+    "float16": torch.float16, "fp16": torch.float16, torch.float16: torch.float16,
+    "bfloat16": torch.bfloat16, "bf16": torch.bfloat16, torch.bfloat16: torch.bfloat16,
+}
+
+
+def _as_torch_dtype(d):
+    return _TORCH_DTYPES[d]
+
+
+def _to_f64(a):
+    if hasattr(a, "detach"):
+        return a.detach().to("cpu").double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def _dtype_name(a):
+    if hasattr(a, "dtype") and isinstance(a.dtype, torch.dtype):
+        return str(a.dtype).replace("torch.", "")
+    return str(np.asarray(a).dtype)
+
+
+def rounding_floor(golden, out_dtype):
+    """max|golden.to(out_dtype).to(float64) - golden| over finite elements."""
+    g = torch.from_numpy(np.ascontiguousarray(golden, dtype=np.float64))
+    finite = torch.isfinite(g)
+    if not bool(finite.any()):
+        return 0.0
+    rt = g.to(_as_torch_dtype(out_dtype)).double()
+    return float((rt - g).abs()[finite].max())
+
+
+def structure_mismatch(target, golden, expected_dtype=None):
+    """Returns None when the structure matches, else a description."""
+    t = _to_f64(target)
+    if t.shape != golden.shape:
+        return f"shape {t.shape} != golden {golden.shape}"
+    if expected_dtype is not None:
+        want = str(_as_torch_dtype(expected_dtype)).replace("torch.", "")
+        have = _dtype_name(target)
+        if have != want:
+            return f"dtype {have} != expected {want}"
+    for what, fn in (("NaN", np.isnan),
+                     ("+Inf", lambda a: np.isposinf(a)),
+                     ("-Inf", lambda a: np.isneginf(a))):
+        mt, mg = fn(t), fn(golden)
+        if not np.array_equal(mt, mg):
+            bad = int(np.count_nonzero(mt != mg))
+            return f"{what} positions differ at {bad} element(s)"
+    return None
+
+
+def _max_abs_err(a, golden):
+    mask = np.isfinite(golden)
+    if not mask.any():
+        return 0.0
+    return float(np.max(np.abs(a[mask] - golden[mask])))
+
+
+def rounding_bias(target, golden):
+    """sum(e*sign(golden))/sum|e| with e = target - golden (finite, e != 0)."""
+    t = _to_f64(target).ravel()
+    g = np.asarray(golden, dtype=np.float64).ravel()
+    mask = np.isfinite(g) & np.isfinite(t)
+    e = t[mask] - g[mask]
+    s = np.sign(g[mask])
+    keep = (e != 0) & (s != 0)
+    if np.count_nonzero(keep) < ROUNDING_BIAS_MIN_ELEMENTS:
+        return None
+    e, s = e[keep], s[keep]
+    return float(np.sum(e * s) / np.sum(np.abs(e)))
+
+
+@dataclass
+class GateRow:
+    tensor: str
+    dtype: str
+    shape: tuple
+    reference_error: float = float("nan")
+    target_error: float = float("nan")
+    rounding_floor: float = float("nan")
+    absolute_floor: float = float("nan")
+    threshold: float = float("nan")
+    golden_scale: float = float("nan")
+    reference_relative_error: float = float("nan")
+    condition: float | None = None
+    bias_target: float | None = None
+    bias_reference: float | None = None
+    gate_valid: bool = False
+    verdict: str = "FAIL"
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+    def as_dict(self):
+        d = asdict(self)
+        d["shape"] = list(self.shape)
+        return d
+
+
+def gate_tensor(name, target, reference, golden, out_dtype, condition=None,
+                fudge=FUDGE_FACTOR, project_atol=PROJECT_ATOL,
+                max_ref_rel=MAX_REFERENCE_RELATIVE_ERROR):
+    """Gate one output tensor.  ``golden`` is float64 NumPy."""
+    golden = np.asarray(golden, dtype=np.float64)
+    want = str(_as_torch_dtype(out_dtype)).replace("torch.", "")
+    row = GateRow(tensor=name, dtype=want, shape=tuple(golden.shape),
+                  condition=condition)
+    why = structure_mismatch(target, golden, out_dtype)
+    if why is not None:
+        row.verdict = "FAIL"
+        row.note = "structure: " + why
+        return row
+    why = structure_mismatch(reference, golden, out_dtype)
+    if why is not None:
+        row.verdict = "INCONCLUSIVE"
+        row.note = "reference structure: " + why
+        return row
+    t = _to_f64(target)
+    r = _to_f64(reference)
+    row.reference_error = _max_abs_err(r, golden)
+    row.target_error = _max_abs_err(t, golden)
+    row.rounding_floor = rounding_floor(golden, out_dtype)
+    row.absolute_floor = max(project_atol, row.rounding_floor)
+    row.threshold = fudge * row.reference_error + row.absolute_floor
+    fin = np.isfinite(golden)
+    row.golden_scale = float(np.max(np.abs(golden[fin]))) if fin.any() else 0.0
+    denom = max(row.golden_scale, row.absolute_floor)
+    if denom > 0:
+        row.reference_relative_error = row.reference_error / denom
+    else:
+        row.reference_relative_error = 0.0 if row.reference_error == 0 else float("inf")
+    row.gate_valid = row.reference_relative_error <= max_ref_rel
+    if not row.gate_valid:
+        row.verdict = "INCONCLUSIVE"
+        row.note = "reference is too inaccurate to gate the target"
+        return row
+    ok = row.target_error <= row.threshold
+    notes = []
+    if want in ("bfloat16", "float16"):
+        row.bias_target = rounding_bias(t, golden)
+        row.bias_reference = rounding_bias(r, golden)
+        if row.bias_target is not None:
+            lim = ROUNDING_BIAS_MAX
+            if row.bias_reference is not None:
+                lim = max(lim, 2.0 * abs(row.bias_reference))
+            if abs(row.bias_target) > lim:
+                ok = False
+                notes.append(f"rounding bias {row.bias_target:+.3f} beyond {lim:.3f}")
+    if row.target_error > row.threshold:
+        notes.append("target_error above threshold")
+    row.verdict = "PASS" if ok else "FAIL"
+    row.note = "; ".join(notes)
+    return row
+
+
+def gate_rstd(target_rstd, golden_r, reference_rstd=None,
+              max_rel=RSTD_MAX_REL_ERROR):
+    """rstd check: max_i |rstd_i - r_i| / r_i <= max_rel (float32 output)."""
+    g = np.asarray(golden_r, dtype=np.float64).ravel()
+    row = GateRow(tensor="rstd", dtype="float32", shape=tuple(g.shape))
+    why = structure_mismatch(np.asarray(_to_f64(target_rstd)).ravel(), g)
+    if why is None and _dtype_name(target_rstd) != "float32":
+        why = f"dtype {_dtype_name(target_rstd)} != expected float32"
+    if why is not None:
+        row.verdict, row.note = "FAIL", "structure: " + why
+        return row
+    t = _to_f64(target_rstd).ravel()
+    row.target_error = float(np.max(np.abs(t - g) / g)) if g.size else 0.0
+    if reference_rstd is not None and g.size:
+        rr = _to_f64(reference_rstd).ravel()
+        row.reference_error = float(np.max(np.abs(rr - g) / g))
+    row.threshold = max_rel
+    row.absolute_floor = 0.0
+    row.golden_scale = float(np.max(np.abs(g))) if g.size else 0.0
+    row.gate_valid = True
+    row.verdict = "PASS" if row.target_error <= max_rel else "FAIL"
+    row.note = "relative error, elementwise"
+    return row
+
+
+def overall_verdict(rows):
+    verdicts = [r.verdict for r in rows]
+    if any(v == "FAIL" for v in verdicts):
+        return "FAIL"
+    if any(v == "INCONCLUSIVE" for v in verdicts):
+        return "INCONCLUSIVE"
+    return "PASS"
+
+
+def report(rows, title=""):
+    """Markdown table in the page's report layout plus the overall verdict."""
+    lines = []
+    if title:
+        lines.append(f"### {title}")
+    lines.append("| Tensor | Ref/golden | Condition | Target error | Threshold | Gate valid | Verdict |")
+    lines.append("|---|---|---|---|---|---|---|")
+    for r in rows:
+        cond = "-" if r.condition is None else f"{r.condition:.3g}"
+        lines.append(
+            f"| {r.tensor} ({r.dtype}) | {r.reference_error:.3e} | {cond} | "
+            f"{r.target_error:.3e} | {r.threshold:.3e} | {r.gate_valid} | "
+            f"{r.verdict}{' — ' + r.note if r.note else ''} |")
+    lines.append(f"\nOverall: **{overall_verdict(rows)}**")
+    return "\n".join(lines)
