@@ -1,0 +1,242 @@
+"""MI355X (gfx950) RMSNorm forward/backward: Python binding of librmsnorm.so.
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+C ABI declared in ``include/rmsnorm.h``.  The functions named ``rmsnorm_*``
+mirror the C entry points one to one (tensors in place of pointers); ``fwd``
+and ``bwd`` allocate their outputs like the page's ``forward_op`` and
+``backward_rows`` + ``reduce_gamma_gradient`` launchers (page "Check an AI
+model calculation before accelerating it", sections "Triton forward: one row,
+one program" and "Reducing dgamma without a write race").
+
+There is no fallback: if the library is missing, or an argument is outside
+the contract, a ``RuntimeError`` (or ``ValueError`` for tensor checks) is
+raised.  Build the library with ``python -m backward_rmsnorm_fwd_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RMSNORM_F32", "RMSNORM_F16", "RMSNORM_BF16", "RMSNORM_FLAG_OFFSET",
+    "RmsnormError", "library_path", "load_library", "rmsnorm_status_string",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
+    "rmsnorm_bwd_workspace_bytes", "rmsnorm_query_plan", "fwd", "bwd",
+    "EXPORTED_SYMBOLS",
+]
+
+RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
+RMSNORM_FLAG_OFFSET = 1
+PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
+KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
+                5: "bwd_reduce"}
+
+EXPORTED_SYMBOLS = (
+    "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
+    "rmsnorm_bwd_workspace_bytes", "rmsnorm_status_string", "rmsnorm_query_plan",
+)
+
+_DTYPES = {torch.float32: RMSNORM_F32, torch.float16: RMSNORM_F16,
+           torch.bfloat16: RMSNORM_BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, func, status, text):
+        super().__init__(f"{func}: status {status}: {text}")
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("vec", ctypes.c_int32),
+                ("threads_per_row", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("chunks", ctypes.c_int32), ("x_in_lds", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("partials", ctypes.c_int64),
+                ("lds_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
+        return d
+
+
+def library_path():
+    return os.path.join(_HERE, "librmsnorm.so")
+
+
+def load_library():
+    """dlopen librmsnorm.so (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m backward_rmsnorm_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, u32, f32, sz, i32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                                  ctypes.c_float, ctypes.c_size_t, ctypes.c_int)
+    lib.rmsnorm_fwd.argtypes = [vp, vp, f32, i64, i64, i32, u32, vp, vp, vp]
+    lib.rmsnorm_fwd.restype = i32
+    lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, u32, vp, vp, vp, sz, vp]
+    lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, u32, vp, vp, sz, vp]
+    lib.rmsnorm_bwd_rows.restype = i32
+    lib.rmsnorm_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp]
+    lib.rmsnorm_bwd_reduce.restype = i32
+    lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64, i32, u32]
+    lib.rmsnorm_bwd_workspace_bytes.restype = sz
+    lib.rmsnorm_status_string.argtypes = [i32]
+    lib.rmsnorm_status_string.restype = ctypes.c_char_p
+    lib.rmsnorm_query_plan.argtypes = [i64, i64, i32, u32, i32, i32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_query_plan.restype = i32
+    _LIB = lib
+    return lib
+
+
+def rmsnorm_status_string(status):
+    return load_library().rmsnorm_status_string(int(status)).decode()
+
+
+def _check(func, status):
+    if status != 0:
+        raise RmsnormError(func, status, rmsnorm_status_string(status))
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _rows(x):
+    """[M, N] view of a contiguous tensor (leading dims flatten into M)."""
+    if x.dim() == 0:
+        raise ValueError("expected at least one dimension")
+    n = x.shape[-1]
+    m = x.numel() // n if n else 0
+    return m, n
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _flags(offset):
+    return RMSNORM_FLAG_OFFSET if offset else 0
+
+
+# ---- one-to-one wrappers of the C entry points ------------------------------
+
+def rmsnorm_query_plan(M, N, dtype, offset=False, which=PASS_FWD, align_bytes=16):
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    p = Plan()
+    _check("rmsnorm_query_plan", load_library().rmsnorm_query_plan(
+        int(M), int(N), code, _flags(offset), int(which), int(align_bytes), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def rmsnorm_bwd_workspace_bytes(M, N, dtype, offset=False):
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().rmsnorm_bwd_workspace_bytes(int(M), int(N), code, _flags(offset)))
+
+
+def rmsnorm_fwd(x, gamma, eps, y, rstd, offset=False, stream=None):
+    """y, rstd <- forward(x, gamma); tensors are [.., N] / [N] / [.., N] / [M]."""
+    m, n = _rows(x)
+    _check("rmsnorm_fwd", load_library().rmsnorm_fwd(
+        _ptr(x), _ptr(gamma), float(eps), m, n, _dtype_code(x), _flags(offset),
+        _ptr(y), _ptr(rstd), _stream(x.device, stream)))
+
+
+def rmsnorm_bwd_rows(dy, x, gamma, rstd, dx, workspace, offset=False, stream=None):
+    m, n = _rows(x)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_bwd_rows", load_library().rmsnorm_bwd_rows(
+        _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x), _flags(offset),
+        _ptr(dx), _ptr(workspace), ws_bytes, _stream(x.device, stream)))
+
+
+def rmsnorm_bwd_reduce(workspace, M, N, dtype, dgamma, offset=False, stream=None):
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_bwd_reduce", load_library().rmsnorm_bwd_reduce(
+        _ptr(workspace), ws_bytes, int(M), int(N), code, _flags(offset), _ptr(dgamma),
+        _stream(dgamma.device, stream)))
+
+
+def rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=None):
+    m, n = _rows(x)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_bwd", load_library().rmsnorm_bwd(
+        _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x), _flags(offset),
+        _ptr(dx), _ptr(dgamma), _ptr(workspace), ws_bytes, _stream(x.device, stream)))
+
+
+# ---- allocating front ends ----------------------------------------------------
+
+def _check_inputs(x, gamma):
+    _require(x.is_cuda and gamma.is_cuda, "x and gamma must be device tensors")
+    _require(x.device == gamma.device, "x and gamma must be on the same device")
+    _require(x.is_contiguous() and gamma.is_contiguous(), "x and gamma must be contiguous")
+    _require(gamma.dim() == 1 and gamma.shape[0] == x.shape[-1],
+             "gamma must be 1-D with the length of x's last dimension")
+    _require(x.dtype == gamma.dtype, "x and gamma must share a dtype")
+
+
+def fwd(x, gamma, eps=1e-6, offset=False, stream=None, poison=False):
+    """Returns ``(y, rstd)``: y like x, rstd float32 with one value per row.
+
+    ``poison`` fills the outputs with NaN first (tests use it to show every
+    element is written)."""
+    _check_inputs(x, gamma)
+    m, _ = _rows(x)
+    if poison:
+        y = torch.full_like(x, float("nan"))
+        rstd = torch.full((m,), float("nan"), device=x.device, dtype=torch.float32)
+    else:
+        y = torch.empty_like(x)
+        rstd = torch.empty((m,), device=x.device, dtype=torch.float32)
+    rmsnorm_fwd(x, gamma, eps, y, rstd, offset, stream)
+    return y, rstd
+
+
+def bwd(dy, x, gamma, rstd, offset=False, stream=None, poison=False, workspace=None):
+    """Returns ``(dx, dgamma)``: dx like x, dgamma float32 [N] (a row sum).
+
+    dy is made contiguous (as the page's autograd wrapper does); x and gamma
+    must already be."""
+    _check_inputs(x, gamma)
+    _require(dy.shape == x.shape and dy.dtype == x.dtype and dy.device == x.device,
+             "dy must match x in shape, dtype and device")
+    dy = dy.contiguous()
+    m, n = _rows(x)
+    _require(rstd.dtype == torch.float32 and rstd.numel() == m and rstd.is_contiguous(),
+             "rstd must be a contiguous float32 tensor with one value per row")
+    if poison:
+        dx = torch.full_like(x, float("nan"))
+        dgamma = torch.full((n,), float("nan"), device=x.device, dtype=torch.float32)
+    else:
+        dx = torch.empty_like(x)
+        dgamma = torch.empty((n,), device=x.device, dtype=torch.float32)
+    if workspace is None:
+        nbytes = rmsnorm_bwd_workspace_bytes(m, n, x.dtype, offset)
+        workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
+    rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset, stream)
+    return dx, dgamma

@@ -1,0 +1,220 @@
+"""Benchmark: RMSNorm forward + backward on one MI355X.
+
+A step is one pass of the whole path over one batch: the forward (rmsnorm_fwd)
+and both backward stages (rmsnorm_bwd_rows, rmsnorm_bwd_reduce), called
+through the C ABI on torch's current stream with inputs already in HBM.
+
+Workload: bf16, M = 32768 rows (8 sequences x 4096 tokens) x N = 4096 hidden,
+eps = 1e-6; x ~ N(0,1), gamma ~ U(0.5,1.5), dy ~ N(0,1e-2), seed 0.
+
+Printed: one JSON line.  ``value`` = algorithmic bytes of forward + backward
+per step / measured step time, in GB/s.  Algorithmic bytes (s = 2 bytes):
+forward 2*M*N*s + N*s + 4*M, backward 3*M*N*s + N*s + 4*M + 4*N (the dgamma
+partial-sum workspace is not counted).  ``roofline`` describes the kernel with
+the largest average duration, timed with events on its launch stream over the
+timed steps.  A cold-cache figure (each call preceded by a 1 GiB write that
+evicts L2 and the 256 MB Infinity Cache) is reported beside it, and the CPU
+oracle's throughput on a bounded sample of the same workload as
+``cpu_baseline``.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def alg_bytes(M, N, s):
+    fwd = 2 * M * N * s + N * s + 4 * M
+    bwd_rows = 3 * M * N * s + N * s + 4 * M
+    bwd_reduce = 4 * N
+    return fwd, bwd_rows, bwd_reduce
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
+    ap.add_argument("--cold-samples", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16384,
+                    help="rows of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the row-sharded multi-GPU path is a design, not code).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import backward_rmsnorm_fwd_amd as rn
+    from backward_rmsnorm_fwd_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    rn.load_library()
+    wl = workloads.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = workloads.make_inputs(args.workload)
+    M, N, T, off, eps = inp["M"], inp["N"], inp["dtype"], inp["offset"], inp["eps"]
+    s = torch.tensor([], dtype=T).element_size()
+    x, w, dy = (inp[k].to(dev) for k in ("x", "w", "dy"))
+    y = torch.empty_like(x)
+    rstd = torch.empty(M, device=dev, dtype=torch.float32)
+    dx = torch.empty_like(x)
+    dgamma = torch.empty(N, device=dev, dtype=torch.float32)
+    ws = torch.empty(max(4, rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)) // 4,
+                     device=dev, dtype=torch.float32)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def fwd():
+        rn.rmsnorm_fwd(x, w, eps, y, rstd, off)
+
+    def bwd_rows():
+        rn.rmsnorm_bwd_rows(dy, x, w, rstd, dx, ws, off)
+
+    def bwd_reduce():
+        rn.rmsnorm_bwd_reduce(ws, M, N, T, dgamma, off)
+
+    stages = [("fwd", fwd), ("bwd_rows", bwd_rows), ("bwd_reduce", bwd_reduce)]
+    for _ in range(args.warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+
+    # ---- timed steps (events around every launch on the launch stream) ----
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k, _ in stages}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        for k, f in stages:
+            a, b = ev[k][i]
+            a.record()
+            f()
+            b.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_kernel_us = {k: statistics.mean(a.elapsed_time(b) for a, b in ev[k]) * 1e3
+                     for k, _ in stages}
+
+    fb, rb, db = alg_bytes(M, N, s)
+    step_bytes = fb + rb + db
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kbytes = {"fwd": fb, "bwd_rows": rb, "bwd_reduce": db}
+    dom = max(per_kernel_us, key=per_kernel_us.get)
+    achieved = kbytes[dom] / (per_kernel_us[dom] * 1e-6) / 1e9
+
+    # ---- cold-cache per-call samples ----
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
+    cold = {}
+    for name, calls in (("fwd", [fwd]), ("bwd", [bwd_rows, bwd_reduce])):
+        samples = []
+        for _ in range(args.cold_samples):
+            flush.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for f in calls:
+                f()
+            b.record()
+            b.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3)
+        samples.sort()
+        med = statistics.median(samples)
+        nbytes = fb if name == "fwd" else rb + db
+        cold[name] = {"median_us": round(med, 2),
+                      "p10_us": round(samples[len(samples) // 10], 2),
+                      "p90_us": round(samples[(9 * len(samples)) // 10], 2),
+                      "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                      "pct_of_8TBps": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    del flush
+
+    # ---- plain device copy of 1 GiB, for an achievable-bandwidth reference ----
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
+    # ---- CPU oracle on a bounded sample ----
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        from oracle import golden
+        R = min(args.cpu_rows, M)
+        xs, dys = inp["x"][:R], inp["dy"][:R]
+        nthreads = torch.get_num_threads()
+        torch.set_num_threads(1)
+        t = time.perf_counter()
+        golden.golden_forward(xs, inp["w"], eps, off)
+        golden.golden_dx(dys, xs, inp["w"], eps, off)
+        golden.golden_dgamma(dys, xs, eps)
+        cpu_s = time.perf_counter() - t
+        torch.set_num_threads(nthreads)
+        sb = sum(alg_bytes(R, N, s))
+        cpu_baseline = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+                        "kind": "oracle",
+                        "sample": f"float64 NumPy golden forward+backward on the first {R} of "
+                                  f"{M} rows ({cpu_s:.1f} s, one thread)",
+                        "host_cores_available": len(os.sched_getaffinity(0))}
+
+    result = {
+        "metric": "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[T],
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl.description}", "M": M, "N": N,
+                   "eps": eps, "offset_weight": off, "seed": inp["seed"],
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+        "fwd": {"us": round(per_kernel_us["fwd"], 2),
+                "GBps": round(fb / (per_kernel_us["fwd"] * 1e-6) / 1e9, 1)},
+        "bwd": {"us": round(per_kernel_us["bwd_rows"] + per_kernel_us["bwd_reduce"], 2),
+                "GBps": round((rb + db) / ((per_kernel_us["bwd_rows"]
+                                            + per_kernel_us["bwd_reduce"]) * 1e-6) / 1e9, 1)},
+        "cold_cache": cold,
+        "device_copy_GBps": round(copy_gbs, 1),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": kbytes[dom]},
+        "cpu_baseline": cpu_baseline,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

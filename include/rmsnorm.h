@@ -1,0 +1,199 @@
+/*
+ * rmsnorm.h -- C ABI of the MI355X (gfx950) RMSNorm forward/backward library.
+ *
+ * The operation (page "Check an AI model calculation before accelerating it",
+ * partitech; sections "Problem and reference formula", "Input backward pass:
+ * keep the right N", "Where does the cube of r come from?" and "A sum is not
+ * an average"), for every row i of an M x N matrix:
+ *
+ *   forward   r_i  = 1 / sqrt( (1/N) * sum_j x_ij^2 + eps )
+ *             y_ij = x_ij * r_i * g_j
+ *   backward  u_ij = dy_ij * g_j
+ *             c_i  = (1/N) * sum_j u_ij * x_ij
+ *             dx_ij = r_i * u_ij - x_ij * r_i^3 * c_i
+ *             dgamma_j = sum_i dy_ij * x_ij * r_i        (a sum over rows)
+ *
+ * where g_j = gamma_j, or g_j = 1 + w_j when RMSNORM_FLAG_OFFSET is set
+ * (offset weight; torchtitan kernel-numerics-verifier page, section
+ * "仓库实例 OffsetRMSNorm").  The 1 is added in float32 after the weight is
+ * read.  dgamma has the same expression in both modes.
+ *
+ * Arithmetic: inputs are widened to float32 as they are loaded, before any
+ * square or product (section "Why convert before reducing?"); all reductions
+ * accumulate in float32 except the final column sum of dgamma, which adds the
+ * per-workgroup partial sums in float64.  The mean divides by the logical N
+ * (section "N and BLOCK: two sizes you must never confuse").  Outputs of type
+ * T are rounded to nearest even.
+ *
+ * Conventions shared by every entry point:
+ *  - x, gamma, dy, y and dx hold elements of one dtype T (rmsnorm_dtype_t);
+ *    rstd and dgamma are float32.
+ *  - Matrices are row-major and dense: row i starts at element i*N (the row
+ *    stride equals N).  Any leading dimensions are flattened into M by the
+ *    caller.
+ *  - All pointers are device pointers on the calling thread's current HIP
+ *    device; the stream belongs to that device (0 = the null stream).
+ *  - The caller owns and allocates every buffer.  The library allocates
+ *    nothing, keeps no state between calls and never synchronizes the host:
+ *    kernels are enqueued on `stream` and the call returns.  Calls on
+ *    different streams are independent.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns a negative status and writes nothing.  There is no
+ *    fallback path: an unsupported input is an error.
+ *  - Outputs must not overlap inputs or each other (RMSNORM_ERR_OVERLAP).
+ *  - Pointers must be aligned to their element size (RMSNORM_ERR_ALIGNMENT);
+ *    the workspace to 16 bytes.  Wider alignment lets the kernels use wider
+ *    (up to 16-byte) accesses.
+ *  - Bitwise reproducibility: the same inputs and (M, N, dtype, flags, and
+ *    pointer alignment modulo 16 bytes) give bitwise-identical outputs; no
+ *    atomics are used and every reduction has a fixed order.
+ *  - Limits: 1 <= N <= RMSNORM_MAX_N, 0 <= M <= RMSNORM_MAX_M.  M = 0 is a
+ *    no-op for the row outputs; the backward then writes dgamma = 0.
+ */
+#ifndef RMSNORM_H
+#define RMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RMSNORM_F32 = 0,
+  RMSNORM_F16 = 1,
+  RMSNORM_BF16 = 2
+} rmsnorm_dtype_t;
+
+/* flags */
+#define RMSNORM_FLAG_OFFSET 1u /* apply the weight as (1 + w) */
+
+#define RMSNORM_MAX_N 65536
+#define RMSNORM_MAX_M (((int64_t)1) << 40)
+
+/* status codes */
+#define RMSNORM_OK 0
+#define RMSNORM_ERR_NULL_POINTER (-1)
+#define RMSNORM_ERR_DTYPE (-2)
+#define RMSNORM_ERR_SHAPE (-3)
+#define RMSNORM_ERR_EPS (-4)
+#define RMSNORM_ERR_FLAGS (-5)
+#define RMSNORM_ERR_WORKSPACE (-6)
+#define RMSNORM_ERR_ALIGNMENT (-7)
+#define RMSNORM_ERR_OVERLAP (-8)
+#define RMSNORM_ERR_LAUNCH (-9)
+#define RMSNORM_ERR_ARGUMENT (-10)
+
+/*
+ * Forward: y = x * r * g per row, and rstd[i] = r_i (float32) kept for the
+ * backward (the page keeps the inverse RMS between the passes).
+ *   x     [M, N] T, read
+ *   gamma [N] T (gamma, or w in offset mode), read
+ *   eps   added to the mean square inside the square root; finite and > 0
+ *   y     [M, N] T, written (every element)
+ *   rstd  [M] float32, written
+ * Errors: NULL_POINTER (a needed pointer is NULL; pointers may be NULL only
+ * when M = 0), DTYPE, SHAPE, EPS, FLAGS, ALIGNMENT, OVERLAP, LAUNCH (the
+ * kernel launch failed; the HIP error is not cleared).
+ */
+int rmsnorm_fwd(const void* x, const void* gamma, float eps, int64_t M,
+                int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y,
+                float* rstd, hipStream_t stream);
+
+/*
+ * Bytes of device workspace the backward needs for (M, N, dtype, flags): the
+ * per-workgroup float32 partial sums of dgamma, [P, N] with P a fixed
+ * function of (M, N, dtype).  Returns 0 for M = 0 and for invalid arguments
+ * (which the backward then rejects).
+ */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                                   uint32_t flags);
+
+/*
+ * Backward, both stages on `stream`, in order: rmsnorm_bwd_rows then
+ * rmsnorm_bwd_reduce.
+ *   dy     [M, N] T, read (gradient of the loss with respect to y)
+ *   x      [M, N] T, read (the forward's input)
+ *   gamma  [N] T, read (gamma, or w in offset mode)
+ *   rstd   [M] float32, read (as written by rmsnorm_fwd for this x and eps)
+ *   dx     [M, N] T, written
+ *   dgamma [N] float32, written (sum over the M rows; zeros when M = 0)
+ *   workspace, workspace_bytes: device scratch of at least
+ *          rmsnorm_bwd_workspace_bytes(M, N, dtype, flags) bytes, 16-byte
+ *          aligned, owned by the caller; its contents on entry do not matter
+ *          and on return hold the partial sums.  It must not be shared with a
+ *          call that may run concurrently.
+ * Errors: as rmsnorm_fwd (no EPS: eps is already inside rstd), plus
+ * WORKSPACE (too small, or NULL when a non-zero size is needed).
+ */
+int rmsnorm_bwd(const void* dy, const void* x, const void* gamma,
+                const float* rstd, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                uint32_t flags, void* dx, float* dgamma, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward stage 1 alone (the page's per-row backward pass, section
+ * "Input backward pass: keep the right N"): writes dx and the [P, N] float32
+ * partial column sums of dy*x*r into the workspace, each workgroup summing a
+ * fixed block of rows (section "Reducing dgamma without a write race": each
+ * program writes its own area, a second pass adds them by column).
+ * Arguments as rmsnorm_bwd, without dgamma.
+ */
+int rmsnorm_bwd_rows(const void* dy, const void* x, const void* gamma,
+                     const float* rstd, int64_t M, int64_t N,
+                     rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * Backward stage 2 alone: dgamma[j] = sum over p = 0..P-1 of partial[p, j],
+ * added in float64 in a fixed order and rounded once to float32.  The
+ * workspace must hold what rmsnorm_bwd_rows wrote for the same
+ * (M, N, dtype, flags).
+ */
+int rmsnorm_bwd_reduce(const void* workspace, size_t workspace_bytes,
+                       int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                       uint32_t flags, float* dgamma, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char* rmsnorm_status_string(int status);
+
+/* Launch plan, for inspection by tests and benchmarks. */
+typedef struct {
+  int32_t kernel;          /* RMSNORM_KERNEL_* */
+  int32_t vec;             /* elements per vector access */
+  int32_t threads_per_row; /* lanes that share one row */
+  int32_t block_threads;   /* threads per workgroup */
+  int32_t chunks;          /* vector accesses per thread per row */
+  int32_t x_in_lds;        /* 1 when the row of x is staged in LDS */
+  int64_t grid;            /* workgroups launched */
+  int64_t partials;        /* P: rows of the dgamma partial-sum workspace */
+  int64_t lds_bytes;       /* dynamic LDS per workgroup */
+} rmsnorm_plan_t;
+
+#define RMSNORM_KERNEL_FWD_WAVE 1  /* forward, one wavefront per row */
+#define RMSNORM_KERNEL_FWD_BLOCK 2 /* forward, one workgroup per row */
+#define RMSNORM_KERNEL_BWD_WAVE 3  /* backward stage 1, one wavefront per row */
+#define RMSNORM_KERNEL_BWD_BLOCK 4 /* backward stage 1, one workgroup per row */
+#define RMSNORM_KERNEL_BWD_REDUCE 5
+
+#define RMSNORM_PASS_FWD 0
+#define RMSNORM_PASS_BWD_ROWS 1
+#define RMSNORM_PASS_BWD_REDUCE 2
+
+/*
+ * Fills *plan with the launch the given pass would use for (M, N, dtype,
+ * flags) when every pointer is `align_bytes`-aligned (16 for typical
+ * allocations).  Returns a status code; no device work.
+ */
+int rmsnorm_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                       uint32_t flags, int pass, int align_bytes,
+                       rmsnorm_plan_t* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_H */

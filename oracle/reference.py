@@ -61,6 +61,24 @@ def reference_backward(dy, x, weight, eps=DEFAULT_EPS, offset=False):
     return dx.to(x.dtype), dgamma
 
 
+def reference_dgamma(dy, x, eps=DEFAULT_EPS, cols=None):
+    """dgamma of ``reference_backward`` restricted to some columns.
+
+    Same float32 arithmetic: r from whole rows, then (dy*x*r) summed over
+    rows for the selected columns only."""
+    x2 = _rows2d(x.detach().to("cpu"))
+    dy2 = _rows2d(dy.detach().to("cpu"))
+    xf = x2.float()
+    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
+    if cols is not None:
+        idx = torch.as_tensor(cols, dtype=torch.long)
+        xf = xf[:, idx]
+        dyf = dy2[:, idx].float()
+    else:
+        dyf = dy2.float()
+    return (dyf * xf * r).sum(0)
+
+
 def reference_backward_autograd(dy, x, weight, eps=DEFAULT_EPS, offset=False):
     """Autograd of the float32 eager forward (informational only)."""
     x2 = _rows2d(x.detach().to("cpu"))

@@ -1,0 +1,97 @@
+"""Helpers that run the HIP path through the C ABI and gate it against the
+oracle (golden + reference) on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import backward_rmsnorm_fwd_amd as rn
+from oracle import gate, golden, reference
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_target(inp, device, offset=None, poison=True):
+    """Forward + backward on the GPU (outputs pre-poisoned with NaN)."""
+    off = inp["offset"] if offset is None else offset
+    x = inp["x"].to(device)
+    w = inp["w"].to(device)
+    dy = inp["dy"].to(device)
+    y, rstd = rn.fwd(x, w, inp["eps"], off, poison=poison)
+    dx, dg = rn.bwd(dy, x, w, rstd, off, poison=poison)
+    torch.cuda.synchronize()
+    return {"y": y, "rstd": rstd, "dx": dx, "dgamma": dg}
+
+
+def gate_full(inp, out):
+    """Gate every element (small inputs)."""
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    off, eps, T = inp["offset"], inp["eps"], inp["x"].dtype
+    n = x.shape[-1]
+    y_r, r_r = reference.reference_forward(x, w, eps, off)
+    dx_r, dg_r = reference.reference_backward(dy, x, w, eps, off)
+    y_g, r_g = golden.golden_forward(x, w, eps, off)
+    dx_g, dg_g = golden.golden_backward(dy, x, w, eps, off)
+    worst = int(np.argmax(np.abs(out["dgamma"].double().cpu().numpy() - dg_g))) if n else 0
+    cond = golden.dgamma_condition(dy, x, eps, worst) if x.numel() else None
+    return [
+        gate.gate_tensor("y", out["y"].cpu().reshape(-1, n), y_r, y_g, T),
+        gate.gate_rstd(out["rstd"].cpu(), r_g, r_r),
+        gate.gate_tensor("dx", out["dx"].cpu().reshape(-1, n), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32,
+                         condition=cond),
+    ]
+
+
+def sample_rows(inp, count, seed=1234):
+    """Random rows plus the first/last rows and any special rows of the recipe."""
+    M = inp["x"].shape[0]
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(count, M), replace=False).tolist())
+    rows.update([0, M - 1])
+    for key in ("zero_rows", "big_rows", "small_rows"):
+        if key in inp:
+            rows.update(np.asarray(inp[key])[:32].tolist())
+    return np.array(sorted(rows))
+
+
+def sample_cols(N, count, seed=4321):
+    rng = np.random.default_rng(seed)
+    cols = set(rng.choice(N, size=min(count, N), replace=False).tolist())
+    cols.update([0, N - 1])
+    return np.array(sorted(cols))
+
+
+def gate_sampled(inp, out, rows, cols):
+    """Gate sampled rows of y, rstd, dx and sampled columns of dgamma (the
+    dgamma columns are still sums over all M rows)."""
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    off, eps, T = inp["offset"], inp["eps"], inp["x"].dtype
+    rt = torch.as_tensor(rows, dtype=torch.long)
+    xs, dys = x[rt], dy[rt]
+    y_r, r_r = reference.reference_forward(xs, w, eps, off)
+    dx_r, _ = reference.reference_backward(dys, xs, w, eps, off)
+    y_g, r_g = golden.golden_forward(xs, w, eps, off)
+    dx_g = golden.golden_dx(dys, xs, w, eps, off)
+    dg_g = golden.golden_dgamma(dy, x, eps, cols=cols)
+    dg_r = reference.reference_dgamma(dy, x, eps, cols=cols)
+    dev_rows = rt.to(out["y"].device)
+    dev_cols = torch.as_tensor(cols, dtype=torch.long, device=out["y"].device)
+    return [
+        gate.gate_tensor("y[rows]", out["y"][dev_rows].cpu(), y_r, y_g, T),
+        gate.gate_rstd(out["rstd"][dev_rows].cpu(), r_g, r_r),
+        gate.gate_tensor("dx[rows]", out["dx"][dev_rows].cpu(), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma[cols]", out["dgamma"][dev_cols].cpu(), dg_r, dg_g,
+                         torch.float32),
+    ]
+
+
+def assert_pass(rows, title):
+    text = gate.report(rows, title)
+    log(text)
+    assert gate.overall_verdict(rows) == "PASS", text

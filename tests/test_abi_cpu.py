@@ -1,0 +1,175 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid calls before any device work.
+
+Every call here fails argument validation on the host (exactly one argument is
+wrong in each), so no kernel is ever launched: the pointers are fake addresses
+that are never dereferenced.  The contract follows the page "Check an AI model
+calculation before accelerating it", section "The memory contract is part of
+the computation" (reject before writing), with the domain of include/rmsnorm.h.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import backward_rmsnorm_fwd_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rn.library_path()),
+                                reason="librmsnorm.so not built")
+
+OK, ENULL, EDTYPE, ESHAPE, EEPS, EFLAGS, EWS, EALIGN, EOVL = 0, -1, -2, -3, -4, -5, -6, -7, -8
+A = 0x10000000  # fake, 16-byte aligned "device" addresses; never dereferenced
+
+
+def lib():
+    return rn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(rmsnorm_\w+)\(",
+                                 text, re.M)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert declared_functions() == sorted(rn.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in (OK, ENULL, EDTYPE, ESHAPE, EEPS, EFLAGS, EWS, EALIGN, EOVL, -9, -10):
+        s = rn.rmsnorm_status_string(code)
+        assert s and s != "unknown status"
+    assert rn.rmsnorm_status_string(12345) == "unknown status"
+
+
+def fwd_call(x=A, g=A + (1 << 24), eps=1e-6, M=4, N=256, dtype=2, flags=0,
+             y=A + (2 << 24), r=A + (3 << 24)):
+    return lib().rmsnorm_fwd(x, g, eps, M, N, dtype, flags, y, r, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 3}, EDTYPE), ({"dtype": -1}, EDTYPE),
+    ({"flags": 2}, EFLAGS),
+    ({"N": 0}, ESHAPE), ({"N": 65537}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"eps": 0.0}, EEPS), ({"eps": -1e-6}, EEPS), ({"eps": float("nan")}, EEPS),
+    ({"eps": float("inf")}, EEPS),
+    ({"x": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL), ({"r": None}, ENULL),
+    ({"x": A + 1}, EALIGN), ({"r": A + (3 << 24) + 2}, EALIGN),
+    ({"y": A + 8}, EOVL),                # y overlaps x
+    ({"r": A + (1 << 24) + 64}, EOVL),   # rstd overlaps gamma
+])
+def test_fwd_rejects(kw, code):
+    assert fwd_call(**kw) == code
+
+
+def test_fwd_alignment_is_per_element_size():
+    # bf16 at a 2-byte boundary is fine for alignment, so the call gets past
+    # alignment and is then rejected for the overlap planted with it.
+    assert fwd_call(x=A + 2, y=A + 2) == EOVL
+    assert fwd_call(x=A + 2, dtype=0) == EALIGN
+
+
+def test_fwd_m0_is_a_noop_and_needs_no_pointers():
+    assert fwd_call(M=0, x=None, g=None, y=None, r=None) == OK
+
+
+def bwd_call(dy=A, x=A + (1 << 24), g=A + (2 << 24), r=A + (3 << 24), M=4, N=256,
+             dtype=2, flags=0, dx=A + (4 << 24), dg=A + (5 << 24), ws=A + (6 << 24),
+             ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib().rmsnorm_bwd_workspace_bytes(M, N, dtype, flags)
+    return lib().rmsnorm_bwd(dy, x, g, r, M, N, dtype, flags, dx, dg, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 5}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": 70000}, ESHAPE),
+    ({"dy": None}, ENULL), ({"x": None}, ENULL), ({"g": None}, ENULL), ({"r": None}, ENULL),
+    ({"dx": None}, ENULL), ({"dg": None}, ENULL),
+    ({"ws": None}, EWS), ({"ws_bytes": 16}, EWS),
+    ({"ws": A + (6 << 24) + 4}, EALIGN), ({"dy": A + 1}, EALIGN),
+    ({"dx": A + 16}, EOVL),               # dx overlaps dy
+    ({"dg": A + (3 << 24) + 4}, EOVL),    # dgamma overlaps rstd
+    ({"ws": A + (4 << 24) + 256}, EOVL),  # workspace overlaps dx
+])
+def test_bwd_rejects(kw, code):
+    assert bwd_call(**kw) == code
+
+
+def test_bwd_stage_entry_points_reject():
+    L = lib()
+    ws = L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 0)
+    assert L.rmsnorm_bwd_rows(A, A + (1 << 24), A + (2 << 24), A + (3 << 24), 4, 256, 2, 0,
+                              None, A + (6 << 24), ws, None) == ENULL
+    assert L.rmsnorm_bwd_rows(A, A + (1 << 24), A + (2 << 24), A + (3 << 24), 4, 256, 2, 0,
+                              A + (4 << 24), A + (6 << 24), ws - 4, None) == EWS
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 0, None, None) == ENULL
+    assert L.rmsnorm_bwd_reduce(None, ws, 4, 256, 2, 0, A + (5 << 24), None) == EWS
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 0, A + 8, None) == EOVL
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 0, 2, 0, A + (5 << 24), None) == ESHAPE
+
+
+def test_workspace_bytes():
+    L = lib()
+    assert L.rmsnorm_bwd_workspace_bytes(0, 4096, 2, 0) == 0
+    assert L.rmsnorm_bwd_workspace_bytes(4, 0, 2, 0) == 0      # invalid -> 0
+    assert L.rmsnorm_bwd_workspace_bytes(4, 4096, 9, 0) == 0   # invalid -> 0
+    for (m, n, dt) in [(32768, 4096, 2), (262144, 1024, 1), (2048, 65536, 2),
+                       (65536, 5120, 2), (65, 128, 0), (1, 2, 0)]:
+        p = rn.rmsnorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)
+        ws = L.rmsnorm_bwd_workspace_bytes(m, n, dt, 0)
+        assert ws == p["partials"] * n * 4
+        assert 1 <= p["partials"] <= m
+        # the workspace is far below the page's M x N float32 partial array
+        assert ws <= m * n * 4
+
+
+def test_plans_for_the_workloads():
+    c2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_FWD)
+    assert c2["kernel_name"] == "fwd_wave" and c2["vec"] == 8 and c2["chunks"] == 8
+    c3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_FWD)
+    assert c3["kernel_name"] == "fwd_wave" and c3["vec"] == 8 and c3["chunks"] == 2
+    c4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_ROWS)
+    assert c4["kernel_name"] == "bwd_block" and c4["vec"] == 8
+    # odd N forces element-wide accesses; misaligned pointers narrow the vector
+    odd = rn.rmsnorm_query_plan(3, 257, 2, which=rn.PASS_FWD)
+    assert odd["vec"] == 1
+    mis = rn.rmsnorm_query_plan(8, 4096, 2, which=rn.PASS_FWD, align_bytes=4)
+    assert mis["vec"] == 2
+    red = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_REDUCE)
+    assert red["kernel_name"] == "bwd_reduce" and red["grid"] == 4096 // 64
+
+
+def test_plan_covers_every_n():
+    """Every N in the domain gets a plan whose threads cover the row."""
+    for dt in (0, 1, 2):
+        for n in list(range(1, 300)) + [1023, 1024, 1025, 4095, 4096, 4097, 5120, 8191,
+                                         8192, 8193, 16383, 16385, 32767, 32769,
+                                         65535, 65536]:
+            for which in (rn.PASS_FWD, rn.PASS_BWD_ROWS):
+                for align in (16, 8, 4, 2):
+                    if dt == 0 and align < 4:
+                        continue
+                    p = rn.rmsnorm_query_plan(7, n, dt, which=which, align_bytes=align)
+                    assert p["threads_per_row"] * p["chunks"] * p["vec"] >= n
+                    assert p["threads_per_row"] * (p["chunks"] - 1) * p["vec"] < n
+                    assert n % p["vec"] == 0
+                    assert p["chunks"] <= 64 and p["block_threads"] <= 1024
+                    assert p["lds_bytes"] <= 160 * 1024
+
+
+def test_query_plan_rejects():
+    L = lib()
+    p = rn.Plan()
+    assert L.rmsnorm_query_plan(4, 256, 2, 0, 7, 16, ctypes.byref(p)) == -10
+    assert L.rmsnorm_query_plan(4, 256, 2, 0, 0, 3, ctypes.byref(p)) == -10
+    assert L.rmsnorm_query_plan(4, 256, 2, 0, 0, 16, None) == ENULL

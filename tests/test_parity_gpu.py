@@ -1,0 +1,187 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+The gate (oracle.gate) is the torchtitan kernel-numerics-verifier criterion:
+target_error <= 2.0 * reference_error + rounding_floor(dtype) per tensor, with
+structure and conditioning checks, plus rstd within 1e-6 relative of the
+float64 golden.  Outputs are pre-filled with NaN so an unwritten element fails
+the structure check.  Shapes: the five workloads (small ones whole, the large
+ones at reduced M with ragged tails, and at full size on sampled rows and
+columns), the torchtitan page's tile-boundary and adversarial-variance cases
+(section "形状选择" and "对抗样本"), and the contract's edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import backward_rmsnorm_fwd_amd as rn
+from backward_rmsnorm_fwd_amd import workloads
+from parity import assert_pass, gate_full, gate_sampled, log, run_target, sample_cols, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1a", "c1b", "c1c"])
+def test_small_workloads(cuda, name):
+    inp = workloads.make_inputs(name)
+    log(f"case {name} M={inp['M']} N={inp['N']}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), name)
+
+
+def test_worked_example_values(cuda):
+    """The page's printed y and dx for x=[3,4] (section "Let's work through
+    two values" and "Input backward pass: keep the right N")."""
+    b = run_target(workloads.make_inputs("c1b"), cuda)
+    c = run_target(workloads.make_inputs("c1c"), cuda)
+    assert np.allclose(b["y"].cpu().numpy(), [[0.848528, 1.131371]], atol=6e-7)
+    assert np.allclose(c["y"].cpu().numpy(), [[1.697056, 0.565685]], atol=6e-7)
+    assert np.allclose(b["dx"].cpu().numpy(), [[-0.090510, 0.067882]], atol=6e-7)
+
+
+TILE_CASES = [((3, 255), torch.float32, 1), ((3, 256), torch.bfloat16, 2),
+              ((3, 257), torch.bfloat16, 3), ((3, 257), torch.float16, 10),
+              ((8, 6, 256), torch.bfloat16, 4), ((8, 4095), torch.bfloat16, 5),
+              ((8, 4096), torch.bfloat16, 6), ((8, 4097), torch.bfloat16, 7),
+              ((8, 5120), torch.bfloat16, 8)]
+
+
+@pytest.mark.parametrize("shape,dtype,seed", TILE_CASES)
+def test_tile_boundary_shapes(cuda, shape, dtype, seed):
+    inp = workloads.make_tile_case(shape, dtype, seed)
+    log(f"case tile {shape} {dtype} seed {seed}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"tile {shape} {dtype}")
+
+
+@pytest.mark.parametrize("seed,scale", [(9, 1e-5), (11, 0.0)])
+def test_adversarial_variance(cuda, seed, scale):
+    inp = workloads.make_tile_case((8, 5120), torch.bfloat16, seed, scale=scale)
+    log(f"case variance scale={scale}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"variance scale {scale}")
+
+
+# Each recipe at reduced M (several workgroups' row blocks and a ragged last
+# block) and, where the recipe's N is a multiple of the vector tile, also at
+# an N with a ragged last chunk.
+SCALED = [("c2", 2051, 4096), ("c2", 517, 4104), ("c3", 20011, 1024), ("c3", 3001, 1000),
+          ("c4", 37, 65536), ("c4", 9, 65528), ("c5", 1031, 5120), ("c5", 301, 5112)]
+
+
+@pytest.mark.parametrize("name,M,N", SCALED)
+def test_scaled_workloads(cuda, name, M, N):
+    inp = workloads.make_inputs(name, M=M, N=N)
+    log(f"case {name} recipe at M={M} N={N}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"{name} @ {M}x{N}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size_sampled(cuda, name):
+    """Full-size workload, default plan (the one bench.py times); y, rstd, dx
+    gated on sampled rows, dgamma on sampled columns summed over all rows."""
+    inp = workloads.make_inputs(name)
+    log(f"case {name} full size M={inp['M']} N={inp['N']} generated")
+    out = run_target(inp, cuda)
+    log(f"case {name} device run done")
+    rows = sample_rows(inp, 192)
+    cols = sample_cols(inp["N"], 48)
+    assert_pass(gate_sampled(inp, out, rows, cols), f"{name} full size, sampled")
+    for k in ("y", "dx", "rstd", "dgamma"):
+        assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
+def test_backward_is_bitwise_reproducible(cuda):
+    for name, M, N in [("c2", 4096, 4096), ("c5", 999, 5120), ("c4", 21, 65536)]:
+        inp = workloads.make_inputs(name, M=M, N=N)
+        x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+        y0, r0 = rn.fwd(x, w, inp["eps"], inp["offset"])
+        runs = [rn.bwd(dy, x, w, r0, inp["offset"]) for _ in range(3)]
+        y1, r1 = rn.fwd(x, w, inp["eps"], inp["offset"])
+        assert torch.equal(y0, y1) and torch.equal(r0, r1)
+        for dx, dg in runs[1:]:
+            assert torch.equal(dx, runs[0][0]) and torch.equal(dg, runs[0][1]), name
+
+
+def test_stage_entry_points_match_combined(cuda):
+    inp = workloads.make_inputs("c2", M=1500, N=4096)
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    _, r = rn.fwd(x, w)
+    dx, dg = rn.bwd(dy, x, w, r)
+    m, n = x.shape
+    ws = torch.empty(rn.rmsnorm_bwd_workspace_bytes(m, n, x.dtype) // 4, device=cuda)
+    dx2 = torch.empty_like(x)
+    dg2 = torch.empty(n, device=cuda)
+    rn.rmsnorm_bwd_rows(dy, x, w, r, dx2, ws)
+    rn.rmsnorm_bwd_reduce(ws, m, n, x.dtype, dg2)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2) and torch.equal(dg, dg2)
+
+
+def test_side_stream(cuda):
+    inp = workloads.make_inputs("c3", M=5000, N=1024)
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    y0, r0 = rn.fwd(x, w)
+    dx0, dg0 = rn.bwd(dy, x, w, r0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y1, r1 = rn.fwd(x, w, stream=s)
+        dx1, dg1 = rn.bwd(dy, x, w, r1, stream=s)
+    s.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(dx0, dx1) and torch.equal(dg0, dg1)
+
+
+@pytest.mark.parametrize("dtype,N", [(torch.float32, 1), (torch.bfloat16, 1), (torch.float16, 2),
+                                     (torch.float32, 65536), (torch.float32, 65535),
+                                     (torch.bfloat16, 65535), (torch.float16, 32769),
+                                     (torch.bfloat16, 16385)])
+def test_edge_shapes(cuda, dtype, N):
+    M = 5
+    inp = workloads.make_tile_case((M, N), dtype, 17)
+    log(f"case edge {dtype} N={N}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"edge {dtype} N={N}")
+
+
+def test_m_zero(cuda):
+    x = torch.empty((0, 64), device=cuda, dtype=torch.bfloat16)
+    w = torch.ones(64, device=cuda, dtype=torch.bfloat16)
+    y, r = rn.fwd(x, w)
+    dx, dg = rn.bwd(x, x, w, r, poison=True)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and dx.shape == (0, 64)
+    assert torch.equal(dg.cpu(), torch.zeros(64))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_misaligned_pointers(cuda, dtype):
+    """Buffers starting one element past an aligned address: narrower vectors."""
+    M, N = 33, 4096
+    inp = workloads.make_inputs("c2", M=M, N=N, dtype=dtype)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=cuda)
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to(cuda))
+        return v
+
+    x, w, dy = shifted(inp["x"]), shifted(inp["w"]), shifted(inp["dy"])
+    y = shifted(torch.full_like(inp["x"], float("nan")))
+    rstd = torch.empty(M, device=cuda)
+    rn.rmsnorm_fwd(x, w, inp["eps"], y, rstd)
+    dx, dg = rn.bwd(dy, x, w, rstd, poison=True)
+    torch.cuda.synchronize()
+    out = {"y": y, "rstd": rstd, "dx": dx, "dgamma": dg}
+    assert_pass(gate_full(inp, out), f"misaligned {dtype}")
+
+
+def test_binding_rejects_bad_tensors(cuda):
+    x = torch.randn(8, 64, device=cuda).to(torch.bfloat16)
+    w = torch.ones(64, device=cuda, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rn.fwd(x.t(), torch.ones(8, device=cuda, dtype=torch.bfloat16))  # non-contiguous
+    with pytest.raises(ValueError):
+        rn.fwd(x, w.float())                                            # dtype mismatch
+    with pytest.raises(ValueError):
+        rn.fwd(x.double(), w.double())                                  # unsupported dtype
+    with pytest.raises(rn.RmsnormError):
+        rn.fwd(x, w, eps=0.0)
+    with pytest.raises(rn.RmsnormError):
+        rn.fwd(torch.empty(2, 70000, device=cuda, dtype=torch.bfloat16),
+               torch.ones(70000, device=cuda, dtype=torch.bfloat16))
