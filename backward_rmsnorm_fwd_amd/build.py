@@ -9,12 +9,15 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "rmsnorm_api.hip")]
-DEPENDS = SOURCES + [os.path.join(HERE, "csrc", "rmsnorm_kernels.hpp"),
-                     os.path.join(ROOT, "include", "rmsnorm.h")]
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in (
+    "rmsnorm_api.hip", "rmsnorm_fast_f32.hip", "rmsnorm_fast_f16.hip",
+    "rmsnorm_fast_bf16.hip")]
 LIB = os.path.join(HERE, "librmsnorm.so")
 ARCH = "gfx950"
 
@@ -23,7 +26,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # IEEE-correct float32 division and square root in device code.
     "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -38,21 +40,40 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose=False, resource_usage=False):
-    """Compile the library (always; never skipped when one already exists)."""
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES,
-           "-o", LIB + ".tmp"]
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = res.stdout + res.stderr
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    return res.returncode, res.stdout + res.stderr
+
+
+def build(verbose=False, resource_usage=False, jobs=None):
+    """Compile the library (always; never skipped when one already exists).
+
+    Each translation unit compiles in its own hipcc process (in parallel);
+    the objects are then linked into one shared library."""
+    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+    inc = ["-I", os.path.join(ROOT, "include")]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    with tempfile.TemporaryDirectory(prefix="rmsnorm_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *FLAGS, *extra, *inc, "-c", src, "-o", obj]
+                for src, obj in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda c: _run(c, verbose), cmds))
+        logs = []
+        for cmd, (rc, out) in zip(cmds, results):
+            logs.append(out)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-3]}:\n{out}")
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+                "-o", LIB + ".tmp"]
+        rc, out = _run(link, verbose)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{out}")
     os.replace(LIB + ".tmp", LIB)
     if resource_usage or verbose:
-        print(out)
+        print("\n".join(logs))
     return LIB
 
 

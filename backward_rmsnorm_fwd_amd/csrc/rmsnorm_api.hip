@@ -17,7 +17,9 @@
 #include <initializer_list>
 
 #include "../../include/rmsnorm.h"
-#include "rmsnorm_kernels.hpp"
+#include "rmsnorm_fast.hpp"
+#include "rmsnorm_fast_table.hpp"
+#include "rmsnorm_launch.hpp"
 
 namespace {
 
@@ -32,9 +34,15 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 
 int elem_bytes(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
-int pow2_at_least(int v) {
+int pow2_at_least(int64_t v) {
   int p = 1;
   while (p < v) p <<= 1;
+  return p;
+}
+
+int pow2_at_most(int64_t v) {
+  int p = 1;
+  while (2 * static_cast<int64_t>(p) <= v) p <<= 1;
   return p;
 }
 
@@ -57,6 +65,87 @@ int pointer_alignment(std::initializer_list<const void*> ptrs) {
   return a;
 }
 
+// ---- full-width (16-byte vector) configurations ----------------------------
+//
+// Chosen by measurement on MI355X, timing the whole forward -> backward rows
+// -> backward reduce sequence (the order a training step runs them in, which
+// differs from timing each kernel alone because each kernel inherits the
+// previous one's dirty cache lines), nontemporal accesses throughout:
+//  forward   few chunks per thread and several wavefronts per row keep the
+//            most rows' loads in flight: 4 wavefronts x 2 chunks at N=4096,
+//            1 x 2 at N=1024 (fp16), 4 x 3 at N=5120.
+//  backward  x arrives in LDS by DMA (no VGPRs while in flight), 1-2 chunks
+//            per thread, 1024-thread workgroups, P = 512 row blocks:
+//            4 x 2 at N=4096 (step 225.1 us vs 230.2 us for 1 wavefront x 8
+//            chunks), 2 x 1 at N=1024 fp16 (441.8 us vs 465.3 us), 8 x 2 at
+//            N=5120 (592.8 us vs 616.6 us).  Staging dy in LDS as well was
+//            slower everywhere.  Rows needing more than 3 chunks at 16
+//            wavefronts keep only the dgamma accumulators in registers (x in
+//            LDS, weight re-read from cache).
+struct Cfg {
+  bool ok;
+  int wpr, ch, block, greg, xlds;
+};
+
+#define RMSNORM_IS_LISTED_FWD(W, C, B, GR) \
+  if (c.wpr == W && c.ch == C && c.block == B && c.greg == GR) return true;
+bool listed_fwd(const Cfg& c) {
+  RMSNORM_FWD_FAST_LIST(RMSNORM_IS_LISTED_FWD)
+  return false;
+}
+#undef RMSNORM_IS_LISTED_FWD
+
+#define RMSNORM_IS_LISTED_BWD(W, C, B, GR, XL) \
+  if (c.wpr == W && c.ch == C && c.block == B && c.greg == GR && c.xlds == XL) return true;
+bool listed_bwd(const Cfg& c) {
+  RMSNORM_BWD_FAST_LIST(RMSNORM_IS_LISTED_BWD)
+  return false;
+}
+#undef RMSNORM_IS_LISTED_BWD
+
+Cfg plan_fast_fwd(int64_t nvec) {
+  Cfg c{true, 1, 1, 256, 1, 0};
+  c.wpr = std::min(8, pow2_at_most(std::max<int64_t>(1, nvec / 128)));
+  c.ch = static_cast<int>(ceil_div(nvec, 64 * c.wpr));
+  if (c.ch > 16) {
+    c.wpr = 16;
+    c.ch = static_cast<int>(ceil_div(nvec, 1024));
+  }
+  c.block = c.wpr <= 2 ? 256 : (c.wpr <= 8 ? 512 : 1024);
+  c.greg = (c.block == 1024 && c.ch > 8) ? 0 : 1;
+  c.ok = listed_fwd(c);
+  return c;
+}
+
+Cfg plan_fast_bwd(int64_t nvec) {
+  Cfg c{true, 1, 1, 1024, 1, 1};
+  if (nvec < 256) {
+    c.wpr = pow2_at_least(ceil_div(nvec, 64));
+  } else {
+    c.wpr = std::min(16, pow2_at_least(ceil_div(nvec, 128)));
+  }
+  c.ch = static_cast<int>(ceil_div(nvec, 64 * c.wpr));
+  if (c.ch >= 4) c.greg = 0;  // long rows: weight re-read, x in LDS
+  c.ok = listed_bwd(c);
+  return c;
+}
+
+int64_t fast_bwd_partials(int64_t M, const Cfg& c) {
+  const int64_t groups = c.block / (64 * c.wpr);
+  const int64_t cap = c.greg ? 512 : 256;
+  return std::min<int64_t>(ceil_div(M, groups), cap);
+}
+
+int64_t fast_bwd_lds(const Cfg& c, int64_t N, int es) {
+  const int64_t groups = c.block / (64 * c.wpr);
+  const int64_t sweep = 64 * c.wpr * (16 / es);
+  const int64_t stage = c.xlds ? groups * N * es : 0;
+  const int64_t comb = groups > 1 ? groups * sweep * 4 : 0;
+  return std::max(stage, comb);
+}
+
+// ---- generic (any alignment) configurations --------------------------------
+
 struct Rows {
   int tpr;     // threads per row
   int chunks;  // vector accesses per thread
@@ -74,15 +163,11 @@ Rows pick_rows(int64_t N, int vec) {
   return {1024, static_cast<int>(ceil_div(nvec, 1024))};
 }
 
-// Backward workgroup count P: a function of (M, N, dtype) only, computed
-// with the vector width that N alone allows.
-int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
-  if (M <= 0) return 0;
-  const int vec = pick_vec(N, elem_bytes(dtype), 16);
+int64_t generic_bwd_partials(int64_t M, int64_t N, int vec) {
   const Rows rw = pick_rows(N, vec);
   if (rw.tpr == kWave) {
     const int maxc = pow2_at_least(rw.chunks);
-    const int groups = 8;                     // wavefronts (rows) per workgroup
+    const int groups = 8;  // wavefronts (rows) per workgroup
     const int per_cu = maxc <= 2 ? 4 : (maxc <= 4 ? 2 : 1);
     return std::min<int64_t>(ceil_div(M, groups), static_cast<int64_t>(kCUs) * per_cu);
   }
@@ -90,16 +175,73 @@ int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
   return std::min<int64_t>(M, static_cast<int64_t>(kCUs) * per_cu);
 }
 
-void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align,
-               rmsnorm_plan_t* p) {
+// Backward workgroup count P: a function of (M, N, dtype) only, computed
+// with the vector width that N alone allows (pointer alignment can only
+// change which kernel runs, never P).
+int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
+  if (M <= 0) return 0;
+  const int es = elem_bytes(dtype);
+  const int vec = pick_vec(N, es, 16);
+  if (vec * es == 16) {
+    const Cfg c = plan_fast_bwd(N / vec);
+    if (c.ok) return fast_bwd_partials(M, c);
+  }
+  return generic_bwd_partials(M, N, vec);
+}
+
+void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   const int es = elem_bytes(dtype);
   const int vec = pick_vec(N, es, align);
-  const Rows rw = pick_rows(N, vec);
+  const bool full = vec * es == 16;
+  if (pass == RMSNORM_PASS_BWD_REDUCE) {
+    p->partials = bwd_partials(M, N, dtype);
+    if (N % 4 == 0 && N <= 8192) {
+      p->kernel = RMSNORM_KERNEL_BWD_REDUCE16;
+      p->block_threads = 256;
+      p->grid = ceil_div(N, 16);
+    } else {
+      p->kernel = RMSNORM_KERNEL_BWD_REDUCE;
+      p->block_threads = 1024;
+      p->grid = ceil_div(N, kWave);
+    }
+    p->vec = 1;
+    return;
+  }
   p->vec = vec;
+  if (pass == RMSNORM_PASS_FWD && full) {
+    const Cfg c = plan_fast_fwd(N / vec);
+    if (c.ok) {
+      p->kernel = RMSNORM_KERNEL_FWD_ROWS;
+      p->threads_per_row = 64 * c.wpr;
+      p->chunks = c.ch;
+      p->block_threads = c.block;
+      p->weight_in_regs = c.greg;
+      const int64_t groups = c.block / (64 * c.wpr);
+      p->grid = std::min<int64_t>(ceil_div(M, groups), int64_t(1) << 20);
+      return;
+    }
+  }
+  if (pass == RMSNORM_PASS_BWD_ROWS && full) {
+    const Cfg c = plan_fast_bwd(N / vec);
+    if (c.ok) {
+      p->kernel = RMSNORM_KERNEL_BWD_ROWS;
+      p->threads_per_row = 64 * c.wpr;
+      p->chunks = c.ch;
+      p->block_threads = c.block;
+      p->weight_in_regs = c.greg;
+      p->x_in_lds = c.xlds;
+      p->partials = bwd_partials(M, N, dtype);
+      p->grid = p->partials;
+      p->lds_bytes = fast_bwd_lds(c, N, es);
+      return;
+    }
+  }
+  const Rows rw = pick_rows(N, vec);
   p->chunks = rw.chunks;
   p->threads_per_row = rw.tpr;
   if (pass == RMSNORM_PASS_FWD) {
+    p->weight_in_regs = rw.tpr == kWave ? 1 : 0;
     if (rw.tpr == kWave) {
       p->kernel = RMSNORM_KERNEL_FWD_WAVE;
       p->block_threads = 256;
@@ -110,12 +252,13 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align,
       p->block_threads = rw.tpr;
       p->grid = std::min<int64_t>(M, static_cast<int64_t>(kCUs) * std::max(1, 2048 / rw.tpr));
     }
-  } else if (pass == RMSNORM_PASS_BWD_ROWS) {
+  } else {
     p->partials = bwd_partials(M, N, dtype);
     p->grid = p->partials;
     if (rw.tpr == kWave) {
       p->kernel = RMSNORM_KERNEL_BWD_WAVE;
       p->block_threads = 512;
+      p->weight_in_regs = 1;
       p->lds_bytes = N * 4;
     } else {
       p->kernel = RMSNORM_KERNEL_BWD_BLOCK;
@@ -124,38 +267,7 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align,
       p->x_in_lds = (xbytes + 1024 <= kMaxLdsBytes) ? 1 : 0;
       p->lds_bytes = p->x_in_lds ? xbytes : 0;
     }
-  } else {
-    p->kernel = RMSNORM_KERNEL_BWD_REDUCE;
-    p->partials = bwd_partials(M, N, dtype);
-    p->block_threads = 1024;
-    p->grid = ceil_div(N, kWave);
-    p->threads_per_row = 0;
-    p->chunks = 0;
-    p->vec = 1;
   }
-}
-
-template <typename... KArgs>
-hipError_t launch_exact(void (*kernel)(KArgs...), int64_t grid, int block,
-                        size_t lds, hipStream_t stream, KArgs... args) {
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel),
-                         dim3(static_cast<unsigned>(grid)), dim3(block), argv, lds,
-                         stream);
-}
-
-// Converts each argument to the kernel's parameter type, then launches.
-template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kernel)(KArgs...), int64_t grid, int block, size_t lds,
-                  hipStream_t stream, Args... args) {
-  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
-  return launch_exact(kernel, grid, block, lds, stream, static_cast<KArgs>(args)...);
 }
 
 // ---- dispatch over the compile-time (dtype, vec, maxc) instantiations ----
@@ -219,6 +331,11 @@ hipError_t fwd_by_vec(const rmsnorm_plan_t& p, const void* x, const void* g, voi
                       float* rstd, int64_t M, int N, float eps, int offset,
                       hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
+  if (p.kernel == RMSNORM_KERNEL_FWD_ROWS) {
+    const FastFwdArgs a{x, g, y, rstd, M, N, eps, offset};
+    return fast_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
+                               p.weight_in_regs, p.grid, a, s);
+  }
   switch (p.vec * es) {
     case 16: return fwd_dispatch<DT, 16 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
     case 8: return fwd_dispatch<DT, 8 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
@@ -236,6 +353,11 @@ hipError_t bwd_rows_by_vec(const rmsnorm_plan_t& p, const void* dy, const void* 
                            const void* g, const float* rstd, void* dx, float* part,
                            int64_t M, int N, int offset, hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
+  if (p.kernel == RMSNORM_KERNEL_BWD_ROWS) {
+    const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
+    return fast_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
+                               p.weight_in_regs, p.x_in_lds, p.lds_bytes, a, s);
+  }
   switch (p.vec * es) {
     case 16: return bwd_rows_dispatch<DT, 16 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
     case 8: return bwd_rows_dispatch<DT, 8 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
@@ -415,6 +537,9 @@ int rmsnorm_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M,
   fill_plan(M, N, dtype, RMSNORM_PASS_BWD_REDUCE, 16, &p);
   const float* part = static_cast<const float*>(workspace);
   const int n = static_cast<int>(N);
+  if (p.kernel == RMSNORM_KERNEL_BWD_REDUCE16)
+    return status_of(launch(bwd_reduce16_kernel, p.grid, p.block_threads, 0, stream, part,
+                            dgamma, p.partials, n));
   return status_of(launch(bwd_reduce_kernel, p.grid, p.block_threads, 0, stream, part,
                           dgamma, p.partials, n));
 }

@@ -1,0 +1,702 @@
+// Full-width (16-byte vector) RMSNorm kernels for gfx950.
+//
+// Same arithmetic as rmsnorm_kernels.hpp (page "Check an AI model
+// calculation before accelerating it": r = 1/sqrt(mean(x^2) + eps),
+// y = x*r*g; dx = r*u - x*r^3*mean(u*x) with u = dy*g; dgamma = sum over rows
+// of dy*x*r), with the row geometry fixed at compile time:
+//
+//   VEC  = 16 / sizeof(T)   elements per 16-byte access
+//   WPR  wavefronts per row (1 = wavefront per row; up to 16 = a 1024-thread
+//        workgroup per row), TPR = 64*WPR threads per row
+//   CH   accesses per thread per row: thread t of a row owns elements
+//        (c*TPR + t)*VEC .. +VEC-1 for c < CH; only the last chunk can be
+//        partial, so only it carries a bounds test
+//   G    = BLOCK/TPR rows processed side by side by one workgroup
+//
+// Rows are addressed through buffer resources (one descriptor per row, a
+// per-thread byte offset t*16 in a VGPR and the chunk offset c*TPR*16 as a
+// scalar offset), so the chunks of a row cost no per-chunk 64-bit addresses
+// in VGPRs.  Streaming accesses carry the cache-policy bit "nt" (no temporal
+// reuse expected).
+//
+// The kernels are picked by the host plan when N*sizeof(T) and every pointer
+// are 16-byte aligned; rmsnorm_kernels.hpp covers all other cases.
+#pragma once
+
+#include "rmsnorm_kernels.hpp"
+
+namespace rmsnorm_hip {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kPolicyNT = 2;            // cache policy: nt (non-temporal)
+
+// Buffer resource over `bytes` bytes at `base` (base must be uniform).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? kPolicyNT : 0);
+}
+
+template <bool NT>
+__device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                         uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, NT ? kPolicyNT : 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wavefront
+// lands at lds_wave_base + 16*i (checked on the device).
+__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                            uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Access to one row (or one vector) of 16-byte elements at byte offsets
+// voff (per thread) + soff (uniform).  BUF selects buffer-resource addressing
+// (no per-chunk 64-bit addresses in VGPRs); otherwise plain global addresses.
+template <bool BUF>
+struct RowAccess;
+
+template <>
+struct RowAccess<true> {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ RowAccess(const void* base, uint32_t bytes) : r(buffer_of(base, bytes)) {}
+  template <bool NT>
+  __device__ __forceinline__ u32x4 load(uint32_t voff, uint32_t soff) const {
+    return bload16<NT>(r, voff, soff);
+  }
+  template <bool NT>
+  __device__ __forceinline__ void store(u32x4 v, uint32_t voff, uint32_t soff) const {
+    bstore16<NT>(v, r, voff, soff);
+  }
+  __device__ __forceinline__ void to_lds(void* lds_wave_base, uint32_t voff, uint32_t soff) const {
+    bload16_lds(r, lds_wave_base, voff, soff);
+  }
+};
+
+template <>
+struct RowAccess<false> {
+  char* p;
+  __device__ __forceinline__ RowAccess(const void* base, uint32_t) : p(static_cast<char*>(const_cast<void*>(base))) {}
+  template <bool NT>
+  __device__ __forceinline__ u32x4 load(uint32_t voff, uint32_t soff) const {
+    const u32x4* a = reinterpret_cast<const u32x4*>(p + soff + voff);
+    if constexpr (NT) return __builtin_nontemporal_load(a);
+    else return *a;
+  }
+  template <bool NT>
+  __device__ __forceinline__ void store(u32x4 v, uint32_t voff, uint32_t soff) const {
+    u32x4* a = reinterpret_cast<u32x4*>(p + soff + voff);
+    if constexpr (NT) __builtin_nontemporal_store(v, a);
+    else *a = v;
+  }
+  __device__ __forceinline__ void to_lds(void* lds_wave_base, uint32_t voff, uint32_t soff) const {
+    __builtin_amdgcn_global_load_lds(p + soff + voff, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  }
+};
+
+// Scheduling fence: no instruction moves across it.  Placed between the
+// chunks of a sweep so the scheduler does not widen every chunk at once
+// (which multiplies the live float32 temporaries and spills).
+__device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int DT, int CH, int WPR, int BLOCK>
+struct Geometry {
+  static constexpr int VEC = 16 / ElemBytes<DT>::value;
+  static constexpr int TPR = kWave * WPR;
+  static constexpr int G = BLOCK / TPR;
+  static constexpr int SWEEP = TPR * VEC;  // elements covered by one chunk
+  static_assert(BLOCK % TPR == 0 && G >= 1, "block must hold whole rows");
+  static_assert(CH >= 1 && CH <= 16, "chunks per thread");
+};
+
+// Row sum across the WPR wavefronts of a row group.  All threads of the
+// workgroup call it the same number of times (the row loops below have a
+// workgroup-uniform trip count), since WPR > 1 needs a workgroup barrier.
+// slots: [2][G][WPR] floats in LDS; parity alternates between calls.
+template <int WPR, int G>
+__device__ __forceinline__ float group_sum(float v, float* slots, int& parity, int group,
+                                           int wave_in_row, int lane) {
+  v = wave_sum(v);
+  if constexpr (WPR == 1) {
+    return v;
+  } else {
+    float* s = slots + (parity * G + group) * WPR;
+    if (lane == 0) s[wave_in_row] = v;
+    __syncthreads();
+    float t = s[0];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i) t += s[i];
+    parity ^= 1;
+    return t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  Workgroup b handles rows b*G + g, then strides by gridDim.x*G.
+// GREG keeps the weight in registers across rows (else it is re-read from
+// cache each row); NT marks x loads and y stores as streaming.
+// ---------------------------------------------------------------------------
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool NT, int MINW = 1, bool BUF = false>
+__global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
+    const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
+    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G;
+  constexpr uint32_t kChunk = TPR * 16;  // bytes per chunk sweep
+  using PK = Pack<DT, VEC>;
+  __shared__ float slots[WPR > 1 ? 2 * G * WPR : 1];
+  const int t = threadIdx.x % TPR;
+  const int group = uniform(static_cast<int>(threadIdx.x / TPR));
+  const int wave_in_row = uniform(t / kWave);
+  const int lane = threadIdx.x % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  int parity = 0;
+  const float n_f = static_cast<float>(N);
+  const RowAccess<BUF> gbuf(gamma, row_bytes);
+
+  PK g[GREG ? CH : 1];
+  if constexpr (GREG) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) g[c].raw = gbuf.template load<false>(voff, c * kChunk);
+      else g[c].zero();
+    }
+  }
+
+  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * G; row0 < M;
+       row0 += static_cast<int64_t>(gridDim.x) * G) {
+    const int64_t row = row0 + group;
+    const bool active = row < M;
+    if constexpr (GREG) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) g[c].opaque();
+    }
+    PK xv[CH];
+    if (active) {
+      const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) xv[c].raw = xb.template load<NT>(voff, c * kChunk);
+        else xv[c].zero();
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) xv[c].zero();
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const float f = xv[c].get(k);
+        ss = fmaf(f, f, ss);
+      }
+    ss = group_sum<WPR, G>(ss, slots, parity, group, wave_in_row, lane);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) xv[c].opaque();
+    const float r = 1.0f / sqrtf(ss / n_f + eps);
+    if (active) {
+      if (t == 0) rstd[row] = r;
+      const RowAccess<BUF> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          PK gv;
+          if constexpr (GREG) gv = g[c];
+          else gv.raw = gbuf.template load<false>(voff, c * kChunk);
+          float o[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k)
+            o[k] = (xv[c].get(k) * r) * weight_of(gv.get(k), offset);
+          PK out;
+          out.set(o);
+          yb.template store<NT>(out.raw, voff, c * kChunk);
+        }
+        chunk_fence();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward for long rows with the row of x staged in LDS by DMA
+// (buffer_load ... lds) and read back for the sum of squares and for the
+// scale pass; one 1024-thread workgroup per row.  The register-staged
+// fwd_fast_kernel<.., WPR=16, ..> is the alternative it is measured against.
+// ---------------------------------------------------------------------------
+template <int DT, int CH, bool NT, bool BUF = false>
+__global__ __launch_bounds__(1024) void fwd_xlds_kernel(
+    const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
+    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
+  using Geo = Geometry<DT, CH, 16, 1024>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
+  constexpr uint32_t kChunk = TPR * 16;
+  using PK = Pack<DT, VEC>;
+  extern __shared__ __align__(16) char xrow[];
+  __shared__ float slots[2 * 16];
+  const int t = threadIdx.x;
+  const int wave = uniform(t / kWave);
+  const int lane = t % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  int parity = 0;
+  const float n_f = static_cast<float>(N);
+  const RowAccess<BUF> gbuf(gamma, row_bytes);
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < CH - 1 || voff + c * kChunk < row_bytes)
+        xb.to_lds(xrow + c * kChunk + wave * kWave * 16, voff, c * kChunk);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+        PK xc;
+        xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float f = xc.get(k);
+          ss = fmaf(f, f, ss);
+        }
+      }
+    }
+    ss = group_sum<16, 1>(ss, slots, parity, 0, wave, lane);
+    const float r = 1.0f / sqrtf(ss / n_f + eps);
+    if (t == 0) rstd[row] = r;
+    const RowAccess<BUF> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+        PK xc, gv;
+        xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+        gv.raw = gbuf.template load<false>(voff, c * kChunk);
+        float o[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k)
+          o[k] = (xc.get(k) * r) * weight_of(gv.get(k), offset);
+        PK out;
+        out.set(o);
+        yb.template store<NT>(out.raw, voff, c * kChunk);
+      }
+      chunk_fence();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward stage 1.  Workgroup w owns rows [w*M/P, (w+1)*M/P); its G row
+// groups take them in turn (row = r0 + it*G + g), all groups running the same
+// number of iterations.  Per row: dot = sum(dy*g*x) over the row, then one
+// sweep computes dx = r*u - x*(r^3*dot/N) and acc_j += (dy_j*x_j)*r.  Then the
+// G accumulators are added in group order, one chunk-wide slice at a time
+// through LDS, and the workgroup writes its partial row part[w, :].
+//
+// XLDS: x arrives by DMA straight into LDS (one row per group, no VGPRs while
+// in flight) and is read back for both sweeps.
+// GREG: the weight lives in registers; otherwise it is re-read from cache.
+// ---------------------------------------------------------------------------
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool XLDS, bool NT, int MINW = 1,
+          bool BUF = false, bool DLDS = false>
+__global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
+    const void* __restrict__ dy, const void* __restrict__ x,
+    const void* __restrict__ gamma, const float* __restrict__ rstd,
+    void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
+    int64_t P) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G, SWEEP = Geo::SWEEP;
+  constexpr uint32_t kChunk = TPR * 16;
+  using PK = Pack<DT, VEC>;
+  static_assert(XLDS || !DLDS, "dy staging sits behind the staged rows of x");
+  // XLDS: [G][N] elements of x (then, with DLDS, [G][N] elements of dy); after
+  // the row loop: [G][SWEEP] float32 for the combine (G > 1).
+  extern __shared__ __align__(16) char dyn[];
+  __shared__ float slots[WPR > 1 ? 2 * G * WPR : 1];
+  const int t = threadIdx.x % TPR;
+  const int group = uniform(static_cast<int>(threadIdx.x / TPR));
+  const int wave_in_row = uniform(t / kWave);
+  const int lane = threadIdx.x % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  int parity = 0;
+  const int64_t w = blockIdx.x;
+  const int64_t r0 = block_row_begin(w, M, P);
+  const int64_t r1 = block_row_begin(w + 1, M, P);
+  const int64_t iters = (r1 - r0 + G - 1) / G;
+  const float n_f = static_cast<float>(N);
+  char* xrow = dyn + static_cast<int64_t>(group) * row_bytes;
+  char* dyrow = dyn + static_cast<int64_t>(G + group) * row_bytes;  // DLDS only
+  const RowAccess<BUF> gbuf(gamma, row_bytes);
+
+  PK g[GREG ? CH : 1];
+  if constexpr (GREG) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) g[c].raw = gbuf.template load<false>(voff, c * kChunk);
+      else g[c].zero();
+    }
+  }
+  float acc[CH][VEC];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t row = r0 + it * G + group;
+    const bool active = row < r1;
+    if constexpr (GREG) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) g[c].opaque();
+    }
+    PK xv[XLDS ? 1 : CH], dv[CH];
+    float r = 0.f;
+    if (active) {
+      r = rstd[row];
+      const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+      const RowAccess<BUF> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          if constexpr (DLDS) db.to_lds(dyrow + c * kChunk + wave_in_row * kWave * 16, voff, c * kChunk);
+          else dv[c].raw = db.template load<NT>(voff, c * kChunk);
+          if constexpr (XLDS) xb.to_lds(xrow + c * kChunk + wave_in_row * kWave * 16, voff, c * kChunk);
+          else xv[c].raw = xb.template load<NT>(voff, c * kChunk);
+        } else {
+          dv[c].zero();
+          if constexpr (!XLDS) xv[c].zero();
+        }
+      }
+      if constexpr (XLDS || DLDS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (DLDS) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          if (c < CH - 1 || voff + c * kChunk < row_bytes)
+            dv[c].raw = *reinterpret_cast<const u32x4*>(dyrow + c * kChunk + voff);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        dv[c].zero();
+        if constexpr (!XLDS) xv[c].zero();
+      }
+    }
+    float dot = 0.f;
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          PK xc, gv;
+          if constexpr (XLDS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+          else xc = xv[c];
+          if constexpr (GREG) gv = g[c];
+          else gv.raw = gbuf.template load<false>(voff, c * kChunk);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k)
+            dot = fmaf(dv[c].get(k) * weight_of(gv.get(k), offset), xc.get(k), dot);
+        }
+        chunk_fence();
+      }
+    }
+    dot = group_sum<WPR, G>(dot, slots, parity, group, wave_in_row, lane);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      dv[c].opaque();
+      if constexpr (!XLDS) xv[c].opaque();
+      if constexpr (GREG) g[c].opaque();
+    }
+    const float r3c = ((r * r) * r) * (dot / n_f);
+    if (active) {
+      const RowAccess<BUF> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          PK xc, gv;
+          if constexpr (XLDS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+          else xc = xv[c];
+          if constexpr (GREG) gv = g[c];
+          else gv.raw = gbuf.template load<false>(voff, c * kChunk);
+          float o[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float xf = xc.get(k);
+            const float dyf = dv[c].get(k);
+            const float u = dyf * weight_of(gv.get(k), offset);
+            o[k] = fmaf(-xf, r3c, r * u);
+            acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
+          }
+          PK out;
+          out.set(o);
+          ob.template store<NT>(out.raw, voff, c * kChunk);
+        }
+        chunk_fence();
+      }
+    }
+  }
+
+  float* dst = part + w * static_cast<int64_t>(N);
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e = (c * TPR + t) * VEC;
+      if (c < CH - 1 || e < N) store_f32<VEC>(dst + e, acc[c]);
+    }
+  } else {
+    // Fixed-order combine of the G groups, one chunk sweep (SWEEP columns) at
+    // a time: part[w, col] = ((acc_0 + acc_1) + acc_2) + ...
+    float* comb = reinterpret_cast<float*>(dyn);
+    __syncthreads();  // the LDS area may still hold staged rows
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      store_f32<VEC>(comb + group * SWEEP + t * VEC, acc[c]);
+      __syncthreads();
+      for (int j = threadIdx.x; j < SWEEP; j += BLOCK) {
+        const int col = c * SWEEP + j;
+        if (col < N) {
+          float s = comb[j];
+#pragma unroll
+          for (int gi = 1; gi < G; ++gi) s += comb[gi * SWEEP + j];
+          dst[col] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward stage 1 for long rows: one workgroup (64*WPR threads) per row.  At
+// N = 65536 a row of x and dy plus the dgamma accumulators would need more
+// than the CU's register file, so only the accumulators persist across the
+// row reduction:
+//   pass A  streams the row once: dot += dy*g*x and acc += (dy*x)*r
+//           (r comes from the forward, so the dgamma term needs no reduction)
+//   pass B  re-reads x, dy and g and writes dx = r*u - x*(r^3*dot/N).
+// Both passes are software-pipelined over batches of D chunks: the loads of
+// batch b+1 are in flight while batch b is computed, and scheduling fences
+// keep the compiler from hoisting more than that.
+// XS: x reaches LDS by DMA in pass A and pass B reads it there (else pass B
+//     re-reads x through the cache hierarchy).
+// GS: gamma is copied to LDS once per workgroup (else read through cache).
+// XS and GS together need 2*N*sizeof(T) bytes of LDS.
+// ---------------------------------------------------------------------------
+template <int DT, int CH, bool XS, bool GS, bool NT, int D = 2, int WPR = 16, bool BUF = false>
+__global__ __launch_bounds__(64 * WPR) void bwd_long_kernel(
+    const void* __restrict__ dy, const void* __restrict__ x,
+    const void* __restrict__ gamma, const float* __restrict__ rstd,
+    void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
+    int64_t P) {
+  using Geo = Geometry<DT, CH, WPR, 64 * WPR>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
+  constexpr uint32_t kChunk = TPR * 16;
+  constexpr int NB = (CH + D - 1) / D;  // batches per pass
+  using PK = Pack<DT, VEC>;
+  extern __shared__ __align__(16) char dyn[];
+  __shared__ float slots[2 * WPR];
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  char* xrow = dyn;                                // [N] when XS
+  char* grow = dyn + (XS ? row_bytes : 0);         // [N] when GS
+  const int t = threadIdx.x;
+  const int wave = uniform(t / kWave);
+  const int lane = t % kWave;
+  const uint32_t voff = t * 16;
+  int parity = 0;
+  const int64_t w = blockIdx.x;
+  const int64_t r0 = block_row_begin(w, M, P);
+  const int64_t r1 = block_row_begin(w + 1, M, P);
+  const float n_f = static_cast<float>(N);
+  const RowAccess<BUF> gbuf(gamma, row_bytes);
+
+  if constexpr (GS) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < CH - 1 || voff + c * kChunk < row_bytes)
+        *reinterpret_cast<u32x4*>(grow + c * kChunk + voff) = gbuf.template load<false>(voff, c * kChunk);
+    // each thread later reads back only the bytes it wrote: no barrier
+  }
+
+  float acc[CH][VEC];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+
+  PK bx[2][D], bd[2][D], bg[2][D];  // register buffers of two batches
+
+  for (int64_t row = r0; row < r1; ++row) {
+    const float r = rstd[row];
+    const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+    const RowAccess<BUF> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
+    const RowAccess<BUF> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
+
+    // Loads of batch b into buffer b&1: cached in pass A (read again in
+    // pass B), streaming in pass B (last use).  `vo` is the thread's byte
+    // offset routed through `after`, a value the previous batch computed, so
+    // the loads cannot be hoisted ahead of that work (which would make every
+    // batch's registers live at once).
+    uint32_t vo = voff;
+    auto load_batch = [&](int b, bool last_use, float after) {
+      asm volatile("" : "+v"(vo) : "v"(after));
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int c = b * D + i;
+        if (c < CH) {
+          if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+            if constexpr (!XS) {
+              bx[b & 1][i].raw = last_use ? xb.template load<NT>(vo, c * kChunk)
+                                          : xb.template load<false>(vo, c * kChunk);
+            }
+            bd[b & 1][i].raw = last_use ? db.template load<NT>(vo, c * kChunk)
+                                        : db.template load<false>(vo, c * kChunk);
+            if constexpr (!GS) bg[b & 1][i].raw = gbuf.template load<false>(vo, c * kChunk);
+          } else {
+            if constexpr (!XS) bx[b & 1][i].zero();
+            bd[b & 1][i].zero();
+            if constexpr (!GS) bg[b & 1][i].zero();
+          }
+        }
+      }
+    };
+
+    // ---- pass A ----
+    if constexpr (XS) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c < CH - 1 || voff + c * kChunk < row_bytes)
+          xb.to_lds(xrow + c * kChunk + wave * kWave * 16, voff, c * kChunk);
+    }
+    float dot = 0.f;
+    load_batch(0, false, r);
+    if constexpr (XS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) load_batch(b + 1, false, dot);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int c = b * D + i;
+        if (c < CH && (c < CH - 1 || voff + c * kChunk < row_bytes)) {
+          PK xc, gv;
+          if constexpr (XS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+          else xc = bx[b & 1][i];
+          if constexpr (GS) gv.raw = *reinterpret_cast<const u32x4*>(grow + c * kChunk + voff);
+          else gv = bg[b & 1][i];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float xf = xc.get(k);
+            const float dyf = bd[b & 1][i].get(k);
+            dot = fmaf(dyf * weight_of(gv.get(k), offset), xf, dot);
+            acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
+          }
+        }
+      }
+      chunk_fence();
+    }
+    dot = group_sum<WPR, 1>(dot, slots, parity, 0, wave, lane);
+    const float r3c = ((r * r) * r) * (dot / n_f);
+
+    // ---- pass B ----
+    float last = r3c;
+    load_batch(0, true, last);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) load_batch(b + 1, true, last);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int c = b * D + i;
+        if (c < CH && (c < CH - 1 || voff + c * kChunk < row_bytes)) {
+          PK xc, gv;
+          if constexpr (XS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
+          else xc = bx[b & 1][i];
+          if constexpr (GS) gv.raw = *reinterpret_cast<const u32x4*>(grow + c * kChunk + voff);
+          else gv = bg[b & 1][i];
+          float o[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float u = bd[b & 1][i].get(k) * weight_of(gv.get(k), offset);
+            o[k] = fmaf(-xc.get(k), r3c, r * u);
+          }
+          PK out;
+          out.set(o);
+          ob.template store<NT>(out.raw, voff, c * kChunk);
+          last = o[0];
+        }
+      }
+      chunk_fence();
+    }
+  }
+
+  float* dst = part + w * static_cast<int64_t>(N);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = (c * TPR + t) * VEC;
+    if (c < CH - 1 || e < N) store_f32<VEC>(dst + e, acc[c]);
+  }
+}
+
+template <int DT, bool XS, bool GS>
+constexpr int64_t bwd_long_lds_bytes(int N) {
+  return static_cast<int64_t>((XS ? 1 : 0) + (GS ? 1 : 0)) * N * ElemBytes<DT>::value;
+}
+
+// LDS bytes the backward kernel needs for a given N.
+template <int DT, int CH, int WPR, int BLOCK, bool XLDS, bool DLDS = false>
+constexpr int64_t bwd_fast_lds_bytes(int N) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  const int64_t stage = static_cast<int64_t>((XLDS ? 1 : 0) + (DLDS ? 1 : 0)) * Geo::G * N *
+                        ElemBytes<DT>::value;
+  const int64_t comb = Geo::G > 1 ? static_cast<int64_t>(Geo::G) * Geo::SWEEP * 4 : 0;
+  return stage > comb ? stage : comb;
+}
+
+// ---------------------------------------------------------------------------
+// Backward stage 2 over a 16-column tile per workgroup: 4 float4 column
+// quads x 64 slices of partial rows; slice s adds rows s, s+64, ... in
+// float64, then 16 threads add the 64 slice sums in slice order.  Needs
+// N % 4 == 0 (16-byte partial rows).
+// ---------------------------------------------------------------------------
+static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce16_kernel(
+    const float* __restrict__ part, float* __restrict__ dgamma, int64_t P, int N) {
+  constexpr int kQuads = 4, kSlices = 64;
+  __shared__ double sums[kSlices][kQuads * 4 + 1];
+  const int q = threadIdx.x % kQuads;
+  const int s = threadIdx.x / kQuads;
+  const int col = blockIdx.x * (kQuads * 4) + q * 4;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  if (col < N) {
+    for (int64_t p = s; p < P; p += kSlices) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + p * N + col);
+      a0 += v[0];
+      a1 += v[1];
+      a2 += v[2];
+      a3 += v[3];
+    }
+  }
+  sums[s][q * 4 + 0] = a0;
+  sums[s][q * 4 + 1] = a1;
+  sums[s][q * 4 + 2] = a2;
+  sums[s][q * 4 + 3] = a3;
+  __syncthreads();
+  if (threadIdx.x < kQuads * 4) {
+    const int c = blockIdx.x * (kQuads * 4) + threadIdx.x;
+    if (c < N) {
+      double tot = 0.0;
+      for (int i = 0; i < kSlices; ++i) tot += sums[i][threadIdx.x];
+      dgamma[c] = static_cast<float>(tot);
+    }
+  }
+}
+
+}  // namespace rmsnorm_hip

@@ -1,0 +1,34 @@
+// Full-width kernel instantiations for one dtype (split by dtype so the
+// library's translation units compile in parallel).
+#include "rmsnorm_fast.hpp"
+#include "rmsnorm_fast_table.hpp"
+#include "rmsnorm_launch.hpp"
+
+namespace rmsnorm_hip {
+
+template <>
+hipError_t fast_fwd_launch<kF16>(int wpr, int ch, int block, int greg, int64_t grid,
+                                 const FastFwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(W, C, B, GR)                                                              \
+  if (wpr == W && ch == C && block == B && greg == GR)                                      \
+    return launch(fwd_fast_kernel<kF16, C, W, B, GR != 0, true>, grid, B, 0, s, a.x, a.gamma, \
+                  a.y, a.rstd, a.M, a.N, a.eps, a.offset);
+  RMSNORM_FWD_FAST_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t fast_bwd_launch<kF16>(int wpr, int ch, int block, int greg, int xlds, int64_t lds,
+                                 const FastBwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(W, C, B, GR, XL)                                                          \
+  if (wpr == W && ch == C && block == B && greg == GR && xlds == XL)                        \
+    return launch(bwd_fast_kernel<kF16, C, W, B, GR != 0, XL != 0, true>, a.P, B,             \
+                  static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
+                  a.M, a.N, a.offset, a.P);
+  RMSNORM_BWD_FAST_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rmsnorm_hip

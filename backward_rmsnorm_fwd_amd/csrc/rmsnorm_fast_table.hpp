@@ -1,0 +1,30 @@
+// Instantiated full-width (16-byte vector) kernel configurations, shared by
+// the host plan (which may only pick a listed configuration) and by the
+// per-dtype translation units that instantiate them.
+//
+// Forward entries:  X(WPR, CH, BLOCK, GREG)
+// Backward entries: X(WPR, CH, BLOCK, GREG, XLDS)
+//   WPR  wavefronts per row, CH 16-byte chunks per thread and row,
+//   BLOCK threads per workgroup, GREG weight held in registers across rows,
+//   XLDS x staged in LDS by DMA.
+// The choice rules live in rmsnorm_api.hip (plan_fast_fwd / plan_fast_bwd);
+// the measurements behind them are summarised next to those rules.
+#pragma once
+
+#define RMSNORM_FWD_FAST_LIST(X)                                                  \
+  X(1, 1, 256, 1) X(1, 2, 256, 1) X(1, 3, 256, 1) X(1, 4, 256, 1)                 \
+  X(2, 2, 256, 1) X(2, 3, 256, 1) X(2, 4, 256, 1)                                 \
+  X(4, 2, 512, 1) X(4, 3, 512, 1) X(4, 4, 512, 1)                                 \
+  X(8, 2, 512, 1) X(8, 3, 512, 1) X(8, 4, 512, 1) X(8, 5, 512, 1) X(8, 6, 512, 1) \
+  X(8, 7, 512, 1) X(8, 8, 512, 1) X(8, 9, 512, 1) X(8, 10, 512, 1)                \
+  X(8, 11, 512, 1) X(8, 12, 512, 1) X(8, 13, 512, 1) X(8, 14, 512, 1)             \
+  X(8, 15, 512, 1) X(8, 16, 512, 1)                                               \
+  X(16, 9, 1024, 0) X(16, 10, 1024, 0) X(16, 11, 1024, 0) X(16, 12, 1024, 0)      \
+  X(16, 13, 1024, 0) X(16, 14, 1024, 0) X(16, 15, 1024, 0) X(16, 16, 1024, 0)
+
+#define RMSNORM_BWD_FAST_LIST(X)                                                  \
+  X(1, 1, 1024, 1, 1) X(2, 1, 1024, 1, 1) X(4, 1, 1024, 1, 1)                     \
+  X(2, 2, 1024, 1, 1) X(4, 2, 1024, 1, 1) X(8, 2, 1024, 1, 1) X(16, 2, 1024, 1, 1) \
+  X(16, 3, 1024, 1, 1)                                                            \
+  X(16, 4, 1024, 0, 1) X(16, 5, 1024, 0, 1) X(16, 6, 1024, 0, 1)                  \
+  X(16, 7, 1024, 0, 1) X(16, 8, 1024, 0, 1)

@@ -82,6 +82,22 @@ struct Pack {
     *reinterpret_cast<raw_t*>(static_cast<char*>(base) +
                               elem * ElemBytes<DT>::value) = raw;
   }
+  // Streaming variants: the data is touched once, so hint the caches not to
+  // keep it (nontemporal loads/stores).
+  template <bool NT>
+  __device__ __forceinline__ void load_s(const void* base, int64_t elem) {
+    const raw_t* p = reinterpret_cast<const raw_t*>(
+        static_cast<const char*>(base) + elem * ElemBytes<DT>::value);
+    if constexpr (NT) raw = __builtin_nontemporal_load(p);
+    else raw = *p;
+  }
+  template <bool NT>
+  __device__ __forceinline__ void store_s(void* base, int64_t elem) const {
+    raw_t* p = reinterpret_cast<raw_t*>(static_cast<char*>(base) +
+                                        elem * ElemBytes<DT>::value);
+    if constexpr (NT) __builtin_nontemporal_store(raw, p);
+    else *p = raw;
+  }
 
   __device__ __forceinline__ u32 word(int w) const {
     if constexpr (kBytes >= 8) return raw[w];
@@ -577,7 +593,7 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
 // A workgroup covers 64 columns; its S = blockDim.x/64 slices take partial
 // rows p = s, s+S, ...; the slices are then added in slice order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void bwd_reduce_kernel(
+static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduce_kernel(
     const float* __restrict__ part, float* __restrict__ dgamma, int64_t P, int N) {
   __shared__ double sums[kMaxWavesPerBlock][kWave];
   const int lane = threadIdx.x & (kWave - 1);

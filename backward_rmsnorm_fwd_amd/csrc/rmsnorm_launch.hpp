@@ -1,0 +1,65 @@
+// Host-side launch helpers shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rmsnorm_hip {
+
+template <typename... KArgs>
+hipError_t launch_exact(void (*kernel)(KArgs...), int64_t grid, int block, size_t lds,
+                        hipStream_t stream, KArgs... args) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel),
+                         dim3(static_cast<unsigned>(grid)), dim3(block), argv, lds, stream);
+}
+
+// Converts each argument to the kernel's parameter type, then launches.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), int64_t grid, int block, size_t lds,
+                  hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  return launch_exact(kernel, grid, block, lds, stream, static_cast<KArgs>(args)...);
+}
+
+struct FastFwdArgs {
+  const void* x;
+  const void* gamma;
+  void* y;
+  float* rstd;
+  int64_t M;
+  int N;
+  float eps;
+  int offset;
+};
+
+struct FastBwdArgs {
+  const void* dy;
+  const void* x;
+  const void* gamma;
+  const float* rstd;
+  void* dx;
+  float* part;
+  int64_t M;
+  int N;
+  int offset;
+  int64_t P;
+};
+
+// Launch a listed full-width configuration (rmsnorm_fast_table.hpp) for
+// dtype DT.  Returns hipErrorInvalidValue for a configuration not listed.
+template <int DT>
+hipError_t fast_fwd_launch(int wpr, int ch, int block, int greg, int64_t grid,
+                           const FastFwdArgs& a, hipStream_t s);
+template <int DT>
+hipError_t fast_bwd_launch(int wpr, int ch, int block, int greg, int xlds, int64_t lds,
+                           const FastBwdArgs& a, hipStream_t s);
+
+}  // namespace rmsnorm_hip

@@ -10,14 +10,15 @@ eps = 1e-6; x ~ N(0,1), gamma ~ U(0.5,1.5), dy ~ N(0,1e-2), seed 0.
 Printed: one JSON line.  ``value`` = algorithmic bytes of forward + backward
 per step / measured step time, in GB/s.  Algorithmic bytes (s = 2 bytes):
 forward 2*M*N*s + N*s + 4*M, backward 3*M*N*s + N*s + 4*M + 4*N (the dgamma
-partial-sum workspace is not counted).  ``roofline`` describes the kernel with
-the largest average duration, timed with events on its launch stream over the
-timed steps.  A cold-cache figure (each call preceded by a 1 GiB write that
-evicts L2 and the 256 MB Infinity Cache) is reported beside it, and the CPU
-oracle's throughput on a bounded sample of the same workload as
-``cpu_baseline``.
+partial-sum workspace is not counted).  ``roofline`` describes the dominant
+kernel, backward stage 1, timed with events on its launch stream inside the
+timed steps.  A cold-cache figure (each call preceded by a 1 GiB read that
+evicts L2 and the 256 MB Infinity Cache) is reported beside it, a 1 GiB
+device copy as an achievable-bandwidth reference, and the CPU oracle's
+throughput on the same workload as ``cpu_baseline``.
 """
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -30,6 +31,37 @@ sys.path.insert(0, ROOT)
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_NOTE = os.path.join(ROOT, "profiles", "bwd_rows_c2_bf16_32768x4096_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel and host sources (sorted by name)."""
+    csrc = os.path.join(ROOT, "backward_rmsnorm_fwd_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per backward-stage-1 launch from the committed counter
+    summary, or None when it covers another workload or the kernels changed
+    since the counters were taken."""
+    if workload != "c2" or not os.path.exists(TRAFFIC_NOTE):
+        return None
+    fields = {}
+    with open(TRAFFIC_NOTE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("|", "#", " ")):
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def alg_bytes(M, N, s):
@@ -47,7 +79,7 @@ def parse():
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
     ap.add_argument("--cold-samples", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=16384,
+    ap.add_argument("--cpu-rows", type=int, default=1 << 62,
                     help="rows of the workload the CPU oracle is timed on")
     return ap.parse_args()
 
@@ -97,37 +129,64 @@ def main():
             f()
     torch.cuda.synchronize()
 
-    # ---- timed steps (events around every launch on the launch stream) ----
-    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k, _ in stages}
+    # ---- timed steps ----
+    # Events bracket only the dominant kernel (backward stage 1) on the stream
+    # it is launched on; the step time comes from the host clock around K
+    # steps bracketed by device synchronization.
+    # An event pair costs a few microseconds of queue time, so only every
+    # `every`-th step carries one (about ten samples per run).
+    every = max(1, args.steps // 10)
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for i in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        for k, f in stages:
-            a, b = ev[k][i]
-            a.record()
-            f()
-            b.record()
+        fwd()
+        if i in ev:
+            ev[i][0].record()
+        bwd_rows()
+        if i in ev:
+            ev[i][1].record()
+        bwd_reduce()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
-    per_kernel_us = {k: statistics.mean(a.elapsed_time(b) for a, b in ev[k]) * 1e3
-                     for k, _ in stages}
+    dominant_us = statistics.mean(a.elapsed_time(b) for a, b in ev.values()) * 1e3
+
+    # ---- per-kernel averages, in the same order, outside the timed region ----
+    per_kernel_us = {}
+    for k in ("fwd", "bwd_rows", "bwd_reduce"):
+        evs = []
+        for _ in range(max(5, args.steps // 2)):
+            for name, f in stages:
+                if name == k:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    f()
+                    b.record()
+                    evs.append((a, b))
+                else:
+                    f()
+        torch.cuda.synchronize()
+        per_kernel_us[k] = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
 
     fb, rb, db = alg_bytes(M, N, s)
     step_bytes = fb + rb + db
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kbytes = {"fwd": fb, "bwd_rows": rb, "bwd_reduce": db}
-    dom = max(per_kernel_us, key=per_kernel_us.get)
-    achieved = kbytes[dom] / (per_kernel_us[dom] * 1e-6) / 1e9
+    achieved = rb / (dominant_us * 1e-6) / 1e9
 
     # ---- cold-cache per-call samples ----
-    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
+    # Before each sample a 1 GiB buffer is read (not written), so L2 and the
+    # 256 MB Infinity Cache hold only clean, unrelated lines.
+    flush = torch.ones(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
     cold = {}
     for name, calls in (("fwd", [fwd]), ("bwd", [bwd_rows, bwd_reduce])):
+        if args.cold_samples <= 0:
+            break
         samples = []
         for _ in range(args.cold_samples):
-            flush.fill_(1.0)
+            flush.sum()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -161,7 +220,7 @@ def main():
     copy_gbs = 2 * src.numel() * 4 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
 
-    # ---- CPU oracle on a bounded sample ----
+    # ---- CPU oracle on the same workload ----
     cpu_baseline = None
     if not args.no_cpu_baseline:
         from oracle import golden
@@ -169,17 +228,21 @@ def main():
         xs, dys = inp["x"][:R], inp["dy"][:R]
         nthreads = torch.get_num_threads()
         torch.set_num_threads(1)
-        t = time.perf_counter()
-        golden.golden_forward(xs, inp["w"], eps, off)
-        golden.golden_dx(dys, xs, inp["w"], eps, off)
-        golden.golden_dgamma(dys, xs, eps)
-        cpu_s = time.perf_counter() - t
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            golden.golden_forward(xs, inp["w"], eps, off)
+            golden.golden_dx(dys, xs, inp["w"], eps, off)
+            golden.golden_dgamma(dys, xs, eps)
+            times.append(time.perf_counter() - t)
         torch.set_num_threads(nthreads)
+        cpu_s = statistics.median(times)
         sb = sum(alg_bytes(R, N, s))
         cpu_baseline = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
                         "kind": "oracle",
-                        "sample": f"float64 NumPy golden forward+backward on the first {R} of "
-                                  f"{M} rows ({cpu_s:.1f} s, one thread)",
+                        "sample": f"float64 NumPy golden forward+backward over {R} of {M} rows "
+                                  f"(all of them by default), median of 3 runs of {cpu_s:.1f} s, "
+                                  "one thread",
                         "host_cores_available": len(os.sched_getaffinity(0))}
 
     result = {
@@ -200,6 +263,7 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+        "dominant_kernel_us_in_timed_steps": round(dominant_us, 2),
         "fwd": {"us": round(per_kernel_us["fwd"], 2),
                 "GBps": round(fb / (per_kernel_us["fwd"] * 1e-6) / 1e9, 1)},
         "bwd": {"us": round(per_kernel_us["bwd_rows"] + per_kernel_us["bwd_reduce"], 2),
@@ -207,10 +271,11 @@ def main():
                                             + per_kernel_us["bwd_reduce"]) * 1e-6) / 1e9, 1)},
         "cold_cache": cold,
         "device_copy_GBps": round(copy_gbs, 1),
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "bwd_rows", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": kbytes[dom]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "alg_bytes_per_launch": rb},
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(result), flush=True)

@@ -168,16 +168,24 @@ typedef struct {
   int32_t block_threads;   /* threads per workgroup */
   int32_t chunks;          /* vector accesses per thread per row */
   int32_t x_in_lds;        /* 1 when the row of x is staged in LDS */
+  int32_t weight_in_regs;  /* 1 when the weight stays in registers across rows */
+  int32_t reserved;
   int64_t grid;            /* workgroups launched */
   int64_t partials;        /* P: rows of the dgamma partial-sum workspace */
   int64_t lds_bytes;       /* dynamic LDS per workgroup */
 } rmsnorm_plan_t;
 
+/* Kernels.  The *_ROWS kernels use 16-byte accesses with the row geometry
+ * fixed at compile time and are used whenever N*sizeof(T) and every pointer
+ * are 16-byte aligned; the others take any alignment. */
 #define RMSNORM_KERNEL_FWD_WAVE 1  /* forward, one wavefront per row */
 #define RMSNORM_KERNEL_FWD_BLOCK 2 /* forward, one workgroup per row */
 #define RMSNORM_KERNEL_BWD_WAVE 3  /* backward stage 1, one wavefront per row */
 #define RMSNORM_KERNEL_BWD_BLOCK 4 /* backward stage 1, one workgroup per row */
 #define RMSNORM_KERNEL_BWD_REDUCE 5
+#define RMSNORM_KERNEL_FWD_ROWS 6  /* forward, full-width rows */
+#define RMSNORM_KERNEL_BWD_ROWS 7  /* backward stage 1, full-width rows */
+#define RMSNORM_KERNEL_BWD_REDUCE16 8 /* backward stage 2, 16-column tiles */
 
 #define RMSNORM_PASS_FWD 0
 #define RMSNORM_PASS_BWD_ROWS 1

@@ -134,19 +134,53 @@ def test_workspace_bytes():
 
 
 def test_plans_for_the_workloads():
+    """The full-width kernels serve the five workloads (aligned pointers)."""
     c2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_FWD)
-    assert c2["kernel_name"] == "fwd_wave" and c2["vec"] == 8 and c2["chunks"] == 8
+    assert c2["kernel_name"] == "fwd_rows" and c2["vec"] == 8
+    assert (c2["threads_per_row"], c2["chunks"]) == (256, 2)
+    b2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_ROWS)
+    assert b2["kernel_name"] == "bwd_rows" and b2["x_in_lds"] == 1
+    assert (b2["threads_per_row"], b2["chunks"], b2["partials"]) == (256, 2, 512)
+    b3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_BWD_ROWS)
+    assert (b3["threads_per_row"], b3["chunks"], b3["partials"]) == (128, 1, 512)
     c3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_FWD)
-    assert c3["kernel_name"] == "fwd_wave" and c3["vec"] == 8 and c3["chunks"] == 2
+    assert c3["kernel_name"] == "fwd_rows" and (c3["threads_per_row"], c3["chunks"]) == (64, 2)
     c4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_ROWS)
-    assert c4["kernel_name"] == "bwd_block" and c4["vec"] == 8
+    assert c4["kernel_name"] == "bwd_rows" and c4["threads_per_row"] == 1024
+    assert c4["x_in_lds"] == 1 and c4["lds_bytes"] == 65536 * 2
+    c5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_BWD_ROWS)
+    assert c5["kernel_name"] == "bwd_rows" and (c5["threads_per_row"], c5["chunks"]) == (512, 2)
     # odd N forces element-wide accesses; misaligned pointers narrow the vector
     odd = rn.rmsnorm_query_plan(3, 257, 2, which=rn.PASS_FWD)
-    assert odd["vec"] == 1
+    assert odd["vec"] == 1 and odd["kernel_name"] == "fwd_wave"
     mis = rn.rmsnorm_query_plan(8, 4096, 2, which=rn.PASS_FWD, align_bytes=4)
-    assert mis["vec"] == 2
+    assert mis["vec"] == 2 and mis["kernel_name"] in ("fwd_wave", "fwd_block")
     red = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_REDUCE)
-    assert red["kernel_name"] == "bwd_reduce" and red["grid"] == 4096 // 64
+    assert red["kernel_name"] == "bwd_reduce16" and red["grid"] == 4096 // 16
+    red4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_REDUCE)
+    assert red4["kernel_name"] == "bwd_reduce" and red4["grid"] == 65536 // 64
+
+
+def test_partials_do_not_depend_on_alignment():
+    for (m, n, dt) in [(32768, 4096, 2), (999, 5120, 2), (5, 4104, 2), (7, 2048, 0)]:
+        ps = {rn.rmsnorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS, align_bytes=a)["partials"]
+              for a in (16, 8, 4)}
+        assert len(ps) == 1, (m, n, dt, ps)
+
+
+def test_full_width_plan_used_for_aligned_rows():
+    """Every N whose rows are 16-byte multiples gets a listed full-width
+    kernel, except float32 rows beyond 32768 in the backward (generic)."""
+    for dt, es in ((0, 4), (1, 2), (2, 2)):
+        vec = 16 // es
+        for n in range(vec, 65537, vec * 7):
+            f = rn.rmsnorm_query_plan(5, n, dt, which=rn.PASS_FWD)
+            assert f["kernel_name"] == "fwd_rows", (dt, n)
+            b = rn.rmsnorm_query_plan(5, n, dt, which=rn.PASS_BWD_ROWS)
+            if dt == 0 and n > 32768:
+                assert b["kernel_name"] in ("bwd_wave", "bwd_block"), (dt, n)
+            else:
+                assert b["kernel_name"] == "bwd_rows", (dt, n)
 
 
 def test_plan_covers_every_n():
