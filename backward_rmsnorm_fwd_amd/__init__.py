@@ -31,7 +31,8 @@ RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
 RMSNORM_FLAG_OFFSET = 1
 PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
 KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
-                5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16"}
+                5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
+                9: "fwd_pipe", 10: "bwd_pipe"}
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
@@ -55,7 +56,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("vec", ctypes.c_int32),
                 ("threads_per_row", ctypes.c_int32), ("block_threads", ctypes.c_int32),
                 ("chunks", ctypes.c_int32), ("x_in_lds", ctypes.c_int32),
-                ("weight_in_regs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("weight_in_regs", ctypes.c_int32), ("dy_in_lds", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("partials", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int64)]
 

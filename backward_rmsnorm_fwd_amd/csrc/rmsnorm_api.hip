@@ -144,6 +144,84 @@ int64_t fast_bwd_lds(const Cfg& c, int64_t N, int es) {
   return std::max(stage, comb);
 }
 
+// ---- software-pipelined full-width configurations --------------------------
+//
+// Measured the same way (whole step, same GPU, same session; step medians):
+//  forward   rows of 4-8 KiB: x staged in LDS by DMA one row ahead, rows
+//            interleaved across 512 workgroups of 1024 threads, 2 wavefronts
+//            x 4 chunks per row: 207.8 us per bf16 32768x4096 step against
+//            238.4 us with fwd_fast 4 x 2 (the backward unchanged).  Shorter
+//            and longer rows (fp16 N=1024, bf16 N=5120) measured slower
+//            pipelined than fwd_fast and keep it.
+//  backward  rows up to 4 KiB: one chunk per thread, dy prefetched into
+//            registers, x into LDS, 256 interleaving workgroups: 443.2 us per
+//            fp16 262144x1024 step against 462.5 us with bwd_fast;
+//            rows of 8-16 KiB: one chunk per thread over 16 wavefronts, x and
+//            dy both prefetched into LDS: 542.0 us per bf16 65536x5120 step
+//            against 602.0 us.  Rows of 4-8 KiB keep bwd_fast (the pipelined
+//            variants measured 214-241 us against 207.8 us per step).
+struct PipeCfg {
+  bool ok;
+  int wpr, ch, block, lds_flag;  // lds_flag: XL (forward) or DLDS (backward)
+};
+
+#define RMSNORM_IS_LISTED_PIPE(W, C, B, F) \
+  if (c.wpr == W && c.ch == C && c.block == B && c.lds_flag == F) return true;
+bool listed_pipe_fwd(const PipeCfg& c) {
+  RMSNORM_FWD_PIPE_LIST(RMSNORM_IS_LISTED_PIPE)
+  return false;
+}
+bool listed_pipe_bwd(const PipeCfg& c) {
+  RMSNORM_BWD_PIPE_LIST(RMSNORM_IS_LISTED_PIPE)
+  return false;
+}
+#undef RMSNORM_IS_LISTED_PIPE
+
+constexpr int64_t kPipeFwdWorkgroups = 512;
+constexpr int64_t kPipeBwdWorkgroups = 256;
+
+PipeCfg plan_pipe_fwd(int64_t nvec) {
+  PipeCfg c{false, 2, 1, 1024, 1};
+  if (nvec <= 256 || nvec > 512) return c;
+  c.ch = static_cast<int>(ceil_div(nvec, 128));
+  c.ok = listed_pipe_fwd(c);
+  return c;
+}
+
+PipeCfg plan_pipe_bwd(int64_t nvec) {
+  PipeCfg c{false, 1, 1, 1024, 0};
+  if (nvec <= 256) {
+    c.wpr = pow2_at_least(ceil_div(nvec, 64));
+  } else if (nvec > 512 && nvec <= 1024) {
+    c.wpr = 16;
+    c.lds_flag = 1;
+  } else {
+    return c;
+  }
+  c.ok = listed_pipe_bwd(c);
+  return c;
+}
+
+int64_t pipe_groups(const PipeCfg& c) { return c.block / (64 * c.wpr); }
+
+int64_t pipe_fwd_grid(int64_t M, const PipeCfg& c) {
+  return std::min<int64_t>(ceil_div(M, pipe_groups(c)), kPipeFwdWorkgroups);
+}
+
+int64_t pipe_bwd_partials(int64_t M, const PipeCfg& c) {
+  return std::min<int64_t>(ceil_div(M, pipe_groups(c)), kPipeBwdWorkgroups);
+}
+
+// Two stage buffers of G rows of x (and of dy with DLDS); the backward reuses
+// the area for its [G][chunk sweep] float32 combine at the end.
+int64_t pipe_lds(const PipeCfg& c, int64_t N, int es, bool backward) {
+  const int64_t groups = pipe_groups(c);
+  const int64_t sets = (backward && c.lds_flag) ? 2 : 1;
+  const int64_t stage = (backward || c.lds_flag) ? 2 * sets * groups * N * es : 0;
+  const int64_t comb = (backward && groups > 1) ? groups * 64 * c.wpr * (16 / es) * 4 : 0;
+  return std::max(stage, comb);
+}
+
 // ---- generic (any alignment) configurations --------------------------------
 
 struct Rows {
@@ -183,6 +261,8 @@ int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
   const int es = elem_bytes(dtype);
   const int vec = pick_vec(N, es, 16);
   if (vec * es == 16) {
+    const PipeCfg pc = plan_pipe_bwd(N / vec);
+    if (pc.ok) return pipe_bwd_partials(M, pc);
     const Cfg c = plan_fast_bwd(N / vec);
     if (c.ok) return fast_bwd_partials(M, c);
   }
@@ -209,6 +289,36 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
     return;
   }
   p->vec = vec;
+  if (pass == RMSNORM_PASS_FWD && full) {
+    const PipeCfg pc = plan_pipe_fwd(N / vec);
+    if (pc.ok) {
+      p->kernel = RMSNORM_KERNEL_FWD_PIPE;
+      p->threads_per_row = 64 * pc.wpr;
+      p->chunks = pc.ch;
+      p->block_threads = pc.block;
+      p->weight_in_regs = 1;
+      p->x_in_lds = pc.lds_flag;
+      p->grid = pipe_fwd_grid(M, pc);
+      p->lds_bytes = pipe_lds(pc, N, es, false);
+      return;
+    }
+  }
+  if (pass == RMSNORM_PASS_BWD_ROWS && full) {
+    const PipeCfg pc = plan_pipe_bwd(N / vec);
+    if (pc.ok) {
+      p->kernel = RMSNORM_KERNEL_BWD_PIPE;
+      p->threads_per_row = 64 * pc.wpr;
+      p->chunks = pc.ch;
+      p->block_threads = pc.block;
+      p->weight_in_regs = 1;
+      p->x_in_lds = 1;
+      p->dy_in_lds = pc.lds_flag;
+      p->partials = bwd_partials(M, N, dtype);
+      p->grid = p->partials;
+      p->lds_bytes = pipe_lds(pc, N, es, true);
+      return;
+    }
+  }
   if (pass == RMSNORM_PASS_FWD && full) {
     const Cfg c = plan_fast_fwd(N / vec);
     if (c.ok) {
@@ -336,6 +446,11 @@ hipError_t fwd_by_vec(const rmsnorm_plan_t& p, const void* x, const void* g, voi
     return fast_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
                                p.weight_in_regs, p.grid, a, s);
   }
+  if (p.kernel == RMSNORM_KERNEL_FWD_PIPE) {
+    const FastFwdArgs a{x, g, y, rstd, M, N, eps, offset};
+    return pipe_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads, p.x_in_lds,
+                               p.grid, p.lds_bytes, a, s);
+  }
   switch (p.vec * es) {
     case 16: return fwd_dispatch<DT, 16 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
     case 8: return fwd_dispatch<DT, 8 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
@@ -357,6 +472,11 @@ hipError_t bwd_rows_by_vec(const rmsnorm_plan_t& p, const void* dy, const void* 
     const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
     return fast_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
                                p.weight_in_regs, p.x_in_lds, p.lds_bytes, a, s);
+  }
+  if (p.kernel == RMSNORM_KERNEL_BWD_PIPE) {
+    const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
+    return pipe_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads, p.dy_in_lds,
+                               p.lds_bytes, a, s);
   }
   switch (p.vec * es) {
     case 16: return bwd_rows_dispatch<DT, 16 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);

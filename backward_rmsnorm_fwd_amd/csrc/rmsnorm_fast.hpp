@@ -478,6 +478,455 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined row kernels.
+//
+// On gfx9 one counter tracks every outstanding vector memory operation, loads
+// and stores alike, and they retire in issue order.  A row loop that loads
+// row i, reduces, then stores row i makes each wavefront wait for its own
+// stores of row i-1 before the loads of row i can be consumed; a workgroup
+// barrier that also orders global memory (__syncthreads) waits for them too.
+// The pipelined kernels below instead
+//   * issue the loads of row i+1 right after the row-i reduction, before
+//     the row-i stores, so those stores stay in flight while row i+1 arrives,
+//   * exchange the partial row sums with a barrier that orders LDS only.
+// The two register sets (rows i and i+1) alternate by unrolling the row loop
+// twice, so no register copy ever waits on a load in flight.
+// ---------------------------------------------------------------------------
+
+// Wait until at most N vector memory operations of this wavefront are
+// outstanding.  The "memory" clobber keeps the compiler from moving memory
+// accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Compiler-only fence: no memory access and no instruction is moved across
+// it (so the number of operations issued after a group of loads is exactly
+// what the source says).
+__device__ __forceinline__ void order_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier for the row-sum exchange: this wavefront's LDS
+// instructions complete (lgkmcnt), then every wavefront meets.  Unlike
+// __syncthreads (or an LDS-scoped fence, which also covers DMA writes into
+// LDS) it does not wait for vector memory operations in flight: global
+// stores and prefetches keep streaming across it.  The memory clobber keeps
+// the compiler from moving any access across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// group_sum with the LDS-only barrier (same slots, parity and result).
+template <int WPR, int G>
+__device__ __forceinline__ float group_sum_lds(float v, float* slots, int& parity, int group,
+                                               int wave_in_row, int lane) {
+  v = wave_sum(v);
+  if constexpr (WPR == 1) {
+    return v;
+  } else {
+    float* s = slots + (parity * G + group) * WPR;
+    if (lane == 0) s[wave_in_row] = v;
+    lds_barrier();
+    float t = s[0];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i) t += s[i];
+    parity ^= 1;
+    return t;
+  }
+}
+
+// Rows of workgroup w (of P) for the pipelined kernels, in processing order;
+// row group `group` of the G in a workgroup takes row base + it*stride + group.
+//   blocked (CYC = false): the contiguous rows [w*M/P, (w+1)*M/P)
+//   cyclic  (CYC = true):  row groups w, w+P, w+2P, ... (all workgroups sweep
+//                          the tensor together, front to back)
+// Either way the rows of a workgroup are a fixed function of (M, P), and
+// rows only grow with `it`, so a row beyond `limit` is followed by no row.
+template <bool CYC>
+struct RowSched {
+  int64_t base, stride, limit, iters;
+  __device__ __forceinline__ RowSched(int64_t w, int64_t M, int64_t P, int G) {
+    if constexpr (CYC) {
+      const int64_t groups = (M + G - 1) / G;
+      base = w * G;
+      stride = P * G;
+      limit = M;
+      iters = w < groups ? (groups - w + P - 1) / P : 0;
+    } else {
+      const int64_t r0 = block_row_begin(w, M, P), r1 = block_row_begin(w + 1, M, P);
+      base = r0;
+      stride = G;
+      limit = r1;
+      iters = (r1 - r0 + G - 1) / G;
+    }
+  }
+};
+
+// 16 bytes from LDS, complete on return.  Written as one asm statement (read
+// and wait together) so the compiler neither sees an LDS read it would guard
+// with a wait for every DMA in flight, nor can touch the destination
+// registers before the data has arrived.
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// Forward, pipelined.  Workgroup w owns the contiguous rows
+// [block_row_begin(w), block_row_begin(w+1)) of a P = gridDim.x split; its G
+// row groups take rows r0 + it*G + group.  The weight stays in registers for
+// the whole launch.  x is prefetched one row ahead either into LDS by DMA (XL,
+// two stage buffers of [G][N] elements, read back with lds_read16 after an
+// explicit wait) or into the second of two register sets.
+template <int DT, int CH, int WPR, int BLOCK, bool NT, bool XL, bool CYC, int MINW = 1>
+__global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
+    const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
+    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G;
+  constexpr uint32_t kChunk = TPR * 16;
+  using PK = Pack<DT, VEC>;
+  extern __shared__ __align__(16) char dyn[];
+  __shared__ float slots[WPR > 1 ? 2 * G * WPR : 1];
+  const int t = threadIdx.x % TPR;
+  const int group = uniform(static_cast<int>(threadIdx.x / TPR));
+  const int wave_in_row = uniform(t / kWave);
+  const int lane = threadIdx.x % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  int parity = 0;
+  const float n_f = static_cast<float>(N);
+  const RowSched<CYC> rs(blockIdx.x, M, gridDim.x, G);
+  const int64_t iters = rs.iters;
+  char* const xstage = dyn + static_cast<int64_t>(group) * row_bytes;
+  const int64_t stage_stride = static_cast<int64_t>(G) * row_bytes;
+  const uint32_t dma_off = wave_in_row * kWave * 16;
+  const RowAccess<false> gbuf(gamma, row_bytes);
+
+  PK g[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c < CH - 1 || voff + c * kChunk < row_bytes) g[c].raw = gbuf.template load<false>(voff, c * kChunk);
+    else g[c].zero();
+  }
+
+  auto issue = [&](int64_t row, int64_t it, PK(&xv)[CH]) __attribute__((always_inline)) {
+    const RowAccess<false> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+    char* xs = xstage + (it & 1) * stage_stride;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+        if constexpr (XL) xb.to_lds(xs + c * kChunk + dma_off, voff, c * kChunk);
+        else xv[c].raw = xb.template load<NT>(voff, c * kChunk);
+      } else if constexpr (!XL) {
+        xv[c].zero();
+      }
+    }
+  };
+
+  // Lower bound on the vector memory operations issued after a row's loads:
+  // the previous row's y stores (the rstd store is not counted).
+  const bool has_last = uniform(static_cast<uint32_t>(wave_in_row * kWave * 16) +
+                                (CH - 1) * kChunk) < row_bytes;
+
+  auto step = [&](int64_t it, PK(&xc)[CH], PK(&xn)[CH]) __attribute__((always_inline)) {
+    const int64_t row = rs.base + it * rs.stride + group;
+    const bool active = row < rs.limit;
+    if constexpr (XL) {
+      if (active) {
+        if (has_last) wait_vmem<CH>();
+        else wait_vmem<CH - 1>();
+      }
+    }
+    // Prefetch row it+1; it has the whole of this step to arrive.
+    order_fence();
+    if (it + 1 < iters && row + rs.stride < rs.limit) issue(row + rs.stride, it + 1, xn);
+    order_fence();
+    PK xv[CH];
+    float ss = 0.f;
+    if (active) {
+      const char* xs = xstage + (it & 1) * stage_stride;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if constexpr (XL) {
+          if (c < CH - 1 || voff + c * kChunk < row_bytes) xv[c].raw = lds_read16(xs + c * kChunk + voff);
+          else xv[c].zero();
+        } else {
+          xv[c] = xc[c];
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float f = xv[c].get(k);
+          ss = fmaf(f, f, ss);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) xv[c].zero();
+    }
+    ss = group_sum_lds<WPR, G>(ss, slots, parity, group, wave_in_row, lane);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      xv[c].opaque();
+      g[c].opaque();
+    }
+    const float r = 1.0f / sqrtf(ss / n_f + eps);
+    if (active) {
+      if (t == 0) rstd[row] = r;
+      const RowAccess<false> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          float o[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) o[k] = (xv[c].get(k) * r) * weight_of(g[c].get(k), offset);
+          PK out;
+          out.set(o);
+          yb.template store<NT>(out.raw, voff, c * kChunk);
+        }
+        chunk_fence();
+      }
+    }
+  };
+
+  PK xa[CH], xb2[CH];  // register sets (unused with XL)
+  if (iters > 0 && rs.base + group < rs.limit) issue(rs.base + group, 0, xa);
+  else if constexpr (!XL) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) xa[c].zero();
+  }
+  // Settle the first row's loads (and the weight) before the loop, so the
+  // loop body's waits count only its own operations.
+  wait_vmem<0>();
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if constexpr (!XL) xa[c].opaque();
+    g[c].opaque();
+  }
+  int64_t it = 0;
+  for (; it + 1 < iters; it += 2) {
+    step(it, xa, xb2);
+    step(it + 1, xb2, xa);
+  }
+  if (it < iters) step(it, xa, xb2);
+}
+
+template <int DT, int CH, int WPR, int BLOCK, bool XL>
+inline int64_t fwd_pipe_lds_bytes(int N) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  return XL ? 2 * static_cast<int64_t>(Geo::G) * N * ElemBytes<DT>::value : 0;
+}
+
+// Backward stage 1, pipelined.  Rows split as in bwd_fast_kernel (P = gridDim.x
+// workgroups, fixed row blocks, one fp32 dgamma partial row each).  x (and,
+// with DLDS, dy) reaches LDS by DMA into one of two stage buffers
+// ([2][DLDS ? 2 : 1][G][N] elements); without DLDS dy is loaded into one of
+// two register sets.  Each wavefront reads back exactly the bytes its own DMA
+// wrote, so the staging needs no barrier; the wait for row it's data is an
+// explicit count (see `step`).
+template <int DT, int CH, int WPR, int BLOCK, bool NT, bool DLDS, bool CYC, int MINW = 1>
+__global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
+    const void* __restrict__ dy, const void* __restrict__ x,
+    const void* __restrict__ gamma, const float* __restrict__ rstd,
+    void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
+    int64_t P) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G, SWEEP = Geo::SWEEP;
+  constexpr uint32_t kChunk = TPR * 16;
+  constexpr int kSets = DLDS ? 2 : 1;  // staged tensors per buffer
+  using PK = Pack<DT, VEC>;
+  extern __shared__ __align__(16) char dyn[];
+  __shared__ float slots[WPR > 1 ? 2 * G * WPR : 1];
+  const int t = threadIdx.x % TPR;
+  const int group = uniform(static_cast<int>(threadIdx.x / TPR));
+  const int wave_in_row = uniform(t / kWave);
+  const int lane = threadIdx.x % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  int parity = 0;
+  const int64_t w = blockIdx.x;
+  const RowSched<CYC> rs(w, M, P, G);
+  const int64_t iters = rs.iters;
+  const float n_f = static_cast<float>(N);
+  // Stage buffer b: x row of this group at xstage + b*stage_stride, dy row
+  // (DLDS) G rows further.
+  char* const xstage = dyn + static_cast<int64_t>(group) * row_bytes;
+  const int64_t stage_stride = static_cast<int64_t>(kSets) * G * row_bytes;
+  const int64_t dy_off = static_cast<int64_t>(G) * row_bytes;
+  const uint32_t dma_off = wave_in_row * kWave * 16;
+  const RowAccess<false> gbuf(gamma, row_bytes);
+
+  PK g[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c < CH - 1 || voff + c * kChunk < row_bytes) g[c].raw = gbuf.template load<false>(voff, c * kChunk);
+    else g[c].zero();
+  }
+  float acc[CH][VEC];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+
+  auto issue = [&](int64_t row, int64_t it, PK(&dv)[CH]) __attribute__((always_inline)) {
+    char* xs = xstage + (it & 1) * stage_stride;
+    const RowAccess<false> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+    const RowAccess<false> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+        xb.to_lds(xs + c * kChunk + dma_off, voff, c * kChunk);
+        if constexpr (DLDS) db.to_lds(xs + dy_off + c * kChunk + dma_off, voff, c * kChunk);
+        else dv[c].raw = db.template load<NT>(voff, c * kChunk);
+      } else if constexpr (!DLDS) {
+        dv[c].zero();
+      }
+    }
+  };
+
+  // Vector memory operations this wavefront issues after the loads of a row:
+  // the stores of the previous row, CH of them, or CH-1 when no lane of the
+  // wavefront reaches the last chunk (that store is branched around).
+  const bool has_last = uniform(static_cast<uint32_t>(wave_in_row * kWave * 16) +
+                                (CH - 1) * kChunk) < row_bytes;
+
+  auto step = [&](int64_t it, PK(&dc)[CH], PK(&dn)[CH]) __attribute__((always_inline)) {
+    const int64_t row = rs.base + it * rs.stride + group;
+    const bool active = row < rs.limit;
+    const char* xs = xstage + (it & 1) * stage_stride;
+    if (active) {
+      // Row it's DMA (and dy loads) were issued before the previous row's
+      // stores: wait for them only, the stores may stay in flight.  The
+      // count is a lower bound on the operations issued since, so the wait
+      // is never too short.  (Row it active implies row it-1 was.)
+      if (has_last) wait_vmem<CH>();
+      else wait_vmem<CH - 1>();
+    }
+    // Prefetch row it+1 into the other stage buffer (and register set); it
+    // has the whole of this step to arrive.
+    order_fence();
+    if (it + 1 < iters && row + rs.stride < rs.limit) issue(row + rs.stride, it + 1, dn);
+    order_fence();
+    float r = 0.f;
+    PK xv[CH], dv[CH];
+    float dot = 0.f;
+    if (active) {
+      r = rstd[row];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          xv[c].raw = lds_read16(xs + c * kChunk + voff);
+          if constexpr (DLDS) dv[c].raw = lds_read16(xs + dy_off + c * kChunk + voff);
+          else dv[c] = dc[c];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k)
+            dot = fmaf(dv[c].get(k) * weight_of(g[c].get(k), offset), xv[c].get(k), dot);
+        } else {
+          xv[c].zero();
+          dv[c].zero();
+        }
+        chunk_fence();
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        xv[c].zero();
+        dv[c].zero();
+      }
+    }
+    dot = group_sum_lds<WPR, G>(dot, slots, parity, group, wave_in_row, lane);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      xv[c].opaque();
+      dv[c].opaque();
+      g[c].opaque();
+    }
+    const float r3c = ((r * r) * r) * (dot / n_f);
+    if (active) {
+      const RowAccess<false> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c < CH - 1 || voff + c * kChunk < row_bytes) {
+          float o[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float xf = xv[c].get(k);
+            const float dyf = dv[c].get(k);
+            const float u = dyf * weight_of(g[c].get(k), offset);
+            o[k] = fmaf(-xf, r3c, r * u);
+            acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
+          }
+          PK out;
+          out.set(o);
+          ob.template store<NT>(out.raw, voff, c * kChunk);
+        }
+        chunk_fence();
+      }
+    }
+  };
+
+  PK da[CH], db2[CH];  // dy register sets (unused with DLDS)
+  if (iters > 0 && rs.base + group < rs.limit) issue(rs.base + group, 0, da);
+  else if constexpr (!DLDS) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) da[c].zero();
+  }
+  // Settle the first row's loads (and the weight) before the loop.
+  wait_vmem<0>();
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if constexpr (!DLDS) da[c].opaque();
+    g[c].opaque();
+  }
+  int64_t it = 0;
+  for (; it + 1 < iters; it += 2) {
+    step(it, da, db2);
+    step(it + 1, db2, da);
+  }
+  if (it < iters) step(it, da, db2);
+
+  float* dst = part + w * static_cast<int64_t>(N);
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int e = (c * TPR + t) * VEC;
+      if (c < CH - 1 || e < N) store_f32<VEC>(dst + e, acc[c]);
+    }
+  } else {
+    float* comb = reinterpret_cast<float*>(dyn);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      store_f32<VEC>(comb + group * SWEEP + t * VEC, acc[c]);
+      __syncthreads();
+      for (int j = threadIdx.x; j < SWEEP; j += BLOCK) {
+        const int col = c * SWEEP + j;
+        if (col < N) {
+          float s = comb[j];
+#pragma unroll
+          for (int gi = 1; gi < G; ++gi) s += comb[gi * SWEEP + j];
+          dst[col] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int DT, int CH, int WPR, int BLOCK, bool DLDS>
+inline int64_t bwd_pipe_lds_bytes(int N) {
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  const int64_t stage = 2 * (DLDS ? 2 : 1) * static_cast<int64_t>(Geo::G) * N * ElemBytes<DT>::value;
+  const int64_t comb = Geo::G > 1 ? static_cast<int64_t>(Geo::G) * Geo::SWEEP * 4 : 0;
+  return stage > comb ? stage : comb;
+}
+
+// ---------------------------------------------------------------------------
 // Backward stage 1 for long rows: one workgroup (64*WPR threads) per row.  At
 // N = 65536 a row of x and dy plus the dgamma accumulators would need more
 // than the CU's register file, so only the accumulators persist across the

@@ -31,4 +31,30 @@ hipError_t fast_bwd_launch<kBF16>(int wpr, int ch, int block, int greg, int xlds
   return hipErrorInvalidValue;
 }
 
+template <>
+hipError_t pipe_fwd_launch<kBF16>(int wpr, int ch, int block, int xl, int64_t grid, int64_t lds,
+                                const FastFwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(W, C, B, XL)                                                              \
+  if (wpr == W && ch == C && block == B && xl == XL)                                        \
+    return launch(fwd_pipe_kernel<kBF16, C, W, B, true, XL != 0, true>, grid, B,              \
+                  static_cast<size_t>(lds), s, a.x, a.gamma, a.y, a.rstd, a.M, a.N, a.eps,  \
+                  a.offset);
+  RMSNORM_FWD_PIPE_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t pipe_bwd_launch<kBF16>(int wpr, int ch, int block, int dlds, int64_t lds,
+                                const FastBwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(W, C, B, DL)                                                              \
+  if (wpr == W && ch == C && block == B && dlds == DL)                                      \
+    return launch(bwd_pipe_kernel<kBF16, C, W, B, true, DL != 0, true>, a.P, B,               \
+                  static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
+                  a.M, a.N, a.offset, a.P);
+  RMSNORM_BWD_PIPE_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
 }  // namespace rmsnorm_hip

@@ -4,9 +4,12 @@
 //
 // Forward entries:  X(WPR, CH, BLOCK, GREG)
 // Backward entries: X(WPR, CH, BLOCK, GREG, XLDS)
+// Pipelined forward entries:  X(WPR, CH, BLOCK, XL)
+// Pipelined backward entries: X(WPR, CH, BLOCK, DLDS)
 //   WPR  wavefronts per row, CH 16-byte chunks per thread and row,
 //   BLOCK threads per workgroup, GREG weight held in registers across rows,
-//   XLDS x staged in LDS by DMA.
+//   XLDS / XL x staged in LDS by DMA, DLDS dy staged in LDS too.  The
+//   pipelined kernels always keep the weight in registers.
 // The choice rules live in rmsnorm_api.hip (plan_fast_fwd / plan_fast_bwd);
 // the measurements behind them are summarised next to those rules.
 #pragma once
@@ -28,3 +31,8 @@
   X(16, 3, 1024, 1, 1)                                                            \
   X(16, 4, 1024, 0, 1) X(16, 5, 1024, 0, 1) X(16, 6, 1024, 0, 1)                  \
   X(16, 7, 1024, 0, 1) X(16, 8, 1024, 0, 1)
+
+#define RMSNORM_FWD_PIPE_LIST(X) X(2, 3, 1024, 1) X(2, 4, 1024, 1)
+
+#define RMSNORM_BWD_PIPE_LIST(X) \
+  X(1, 1, 1024, 0) X(2, 1, 1024, 0) X(4, 1, 1024, 0) X(16, 1, 1024, 1)

@@ -10,7 +10,9 @@ namespace rmsnorm_hip {
 template <typename... KArgs>
 hipError_t launch_exact(void (*kernel)(KArgs...), int64_t grid, int block, size_t lds,
                         hipStream_t stream, KArgs... args) {
-  if (lds > 64 * 1024) {
+  // Dynamic LDS beyond the default limit (64 KiB including the kernel's
+  // static LDS, at most a few KiB here) must be allowed explicitly.
+  if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -60,6 +62,12 @@ hipError_t fast_fwd_launch(int wpr, int ch, int block, int greg, int64_t grid,
                            const FastFwdArgs& a, hipStream_t s);
 template <int DT>
 hipError_t fast_bwd_launch(int wpr, int ch, int block, int greg, int xlds, int64_t lds,
+                           const FastBwdArgs& a, hipStream_t s);
+template <int DT>
+hipError_t pipe_fwd_launch(int wpr, int ch, int block, int xl, int64_t grid, int64_t lds,
+                           const FastFwdArgs& a, hipStream_t s);
+template <int DT>
+hipError_t pipe_bwd_launch(int wpr, int ch, int block, int dlds, int64_t lds,
                            const FastBwdArgs& a, hipStream_t s);
 
 }  // namespace rmsnorm_hip

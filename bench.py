@@ -74,8 +74,10 @@ def alg_bytes(M, N, s):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Defaults: about 0.1 s of timed GPU work at the headline workload, after
+    # a warmup long enough for clocks and caches to settle.
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
     ap.add_argument("--cold-samples", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,7 +159,7 @@ def main():
     per_kernel_us = {}
     for k in ("fwd", "bwd_rows", "bwd_reduce"):
         evs = []
-        for _ in range(max(5, args.steps // 2)):
+        for _ in range(max(5, min(100, args.steps // 2))):
             for name, f in stages:
                 if name == k:
                     a = torch.cuda.Event(enable_timing=True)

@@ -169,7 +169,7 @@ typedef struct {
   int32_t chunks;          /* vector accesses per thread per row */
   int32_t x_in_lds;        /* 1 when the row of x is staged in LDS */
   int32_t weight_in_regs;  /* 1 when the weight stays in registers across rows */
-  int32_t reserved;
+  int32_t dy_in_lds;       /* 1 when the row of dy is staged in LDS */
   int64_t grid;            /* workgroups launched */
   int64_t partials;        /* P: rows of the dgamma partial-sum workspace */
   int64_t lds_bytes;       /* dynamic LDS per workgroup */
@@ -186,6 +186,11 @@ typedef struct {
 #define RMSNORM_KERNEL_FWD_ROWS 6  /* forward, full-width rows */
 #define RMSNORM_KERNEL_BWD_ROWS 7  /* backward stage 1, full-width rows */
 #define RMSNORM_KERNEL_BWD_REDUCE16 8 /* backward stage 2, 16-column tiles */
+/* Software-pipelined full-width kernels: each workgroup loops over rows
+ * interleaved with the other workgroups (row groups w, w+P, ...) and
+ * prefetches the next row while it computes the current one. */
+#define RMSNORM_KERNEL_FWD_PIPE 9  /* forward */
+#define RMSNORM_KERNEL_BWD_PIPE 10 /* backward stage 1 */
 
 #define RMSNORM_PASS_FWD 0
 #define RMSNORM_PASS_BWD_ROWS 1

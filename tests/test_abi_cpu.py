@@ -136,20 +136,26 @@ def test_workspace_bytes():
 def test_plans_for_the_workloads():
     """The full-width kernels serve the five workloads (aligned pointers)."""
     c2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_FWD)
-    assert c2["kernel_name"] == "fwd_rows" and c2["vec"] == 8
-    assert (c2["threads_per_row"], c2["chunks"]) == (256, 2)
+    assert c2["kernel_name"] == "fwd_pipe" and c2["vec"] == 8 and c2["x_in_lds"] == 1
+    assert (c2["threads_per_row"], c2["chunks"], c2["block_threads"]) == (128, 4, 1024)
+    assert c2["grid"] == 512 and c2["lds_bytes"] == 2 * 8 * 4096 * 2
     b2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_ROWS)
     assert b2["kernel_name"] == "bwd_rows" and b2["x_in_lds"] == 1
     assert (b2["threads_per_row"], b2["chunks"], b2["partials"]) == (256, 2, 512)
     b3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_BWD_ROWS)
-    assert (b3["threads_per_row"], b3["chunks"], b3["partials"]) == (128, 1, 512)
+    assert b3["kernel_name"] == "bwd_pipe" and b3["dy_in_lds"] == 0
+    assert (b3["threads_per_row"], b3["chunks"], b3["partials"]) == (128, 1, 256)
+    assert b3["lds_bytes"] == 2 * 8 * 1024 * 2
     c3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_FWD)
     assert c3["kernel_name"] == "fwd_rows" and (c3["threads_per_row"], c3["chunks"]) == (64, 2)
     c4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_ROWS)
     assert c4["kernel_name"] == "bwd_rows" and c4["threads_per_row"] == 1024
     assert c4["x_in_lds"] == 1 and c4["lds_bytes"] == 65536 * 2
     c5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_BWD_ROWS)
-    assert c5["kernel_name"] == "bwd_rows" and (c5["threads_per_row"], c5["chunks"]) == (512, 2)
+    assert c5["kernel_name"] == "bwd_pipe" and (c5["threads_per_row"], c5["chunks"]) == (1024, 1)
+    assert c5["dy_in_lds"] == 1 and c5["partials"] == 256 and c5["lds_bytes"] == 2 * 2 * 5120 * 2
+    f5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_FWD)
+    assert f5["kernel_name"] == "fwd_rows" and (f5["threads_per_row"], f5["chunks"]) == (256, 3)
     # odd N forces element-wide accesses; misaligned pointers narrow the vector
     odd = rn.rmsnorm_query_plan(3, 257, 2, which=rn.PASS_FWD)
     assert odd["vec"] == 1 and odd["kernel_name"] == "fwd_wave"
@@ -175,12 +181,15 @@ def test_full_width_plan_used_for_aligned_rows():
         vec = 16 // es
         for n in range(vec, 65537, vec * 7):
             f = rn.rmsnorm_query_plan(5, n, dt, which=rn.PASS_FWD)
-            assert f["kernel_name"] == "fwd_rows", (dt, n)
+            assert f["kernel_name"] in ("fwd_rows", "fwd_pipe"), (dt, n)
+            assert (f["kernel_name"] == "fwd_pipe") == (4096 < n * es <= 8192), (dt, n)
             b = rn.rmsnorm_query_plan(5, n, dt, which=rn.PASS_BWD_ROWS)
             if dt == 0 and n > 32768:
                 assert b["kernel_name"] in ("bwd_wave", "bwd_block"), (dt, n)
             else:
-                assert b["kernel_name"] == "bwd_rows", (dt, n)
+                assert b["kernel_name"] in ("bwd_rows", "bwd_pipe"), (dt, n)
+                pipe = n * es <= 4096 or 8192 < n * es <= 16384
+                assert (b["kernel_name"] == "bwd_pipe") == pipe, (dt, n)
 
 
 def test_plan_covers_every_n():

@@ -41,7 +41,8 @@ TILE_CASES = [((3, 255), torch.float32, 1), ((3, 256), torch.bfloat16, 2),
               ((3, 257), torch.bfloat16, 3), ((3, 257), torch.float16, 10),
               ((8, 6, 256), torch.bfloat16, 4), ((8, 4095), torch.bfloat16, 5),
               ((8, 4096), torch.bfloat16, 6), ((8, 4097), torch.bfloat16, 7),
-              ((8, 5120), torch.bfloat16, 8)]
+              ((8, 5120), torch.bfloat16, 8), ((37, 2048), torch.float32, 12),
+              ((13, 1100), torch.float32, 13), ((11, 3000), torch.float16, 14)]
 
 
 @pytest.mark.parametrize("shape,dtype,seed", TILE_CASES)
@@ -61,8 +62,12 @@ def test_adversarial_variance(cuda, seed, scale):
 # Each recipe at reduced M (several workgroups' row blocks and a ragged last
 # block) and, where the recipe's N is a multiple of the vector tile, also at
 # an N with a ragged last chunk.
-SCALED = [("c2", 2051, 4096), ("c2", 517, 4104), ("c3", 20011, 1024), ("c3", 3001, 1000),
-          ("c4", 37, 65536), ("c4", 9, 65528), ("c5", 1031, 5120), ("c5", 301, 5112)]
+# The pipelined kernels interleave row groups over workgroups; 12293 rows of
+# 4096 give workgroups 4 or 3 steps (both loop tails) and a last row group
+# with 5 of 8 rows.
+SCALED = [("c2", 2051, 4096), ("c2", 12293, 4096), ("c2", 517, 4104), ("c3", 20011, 1024),
+          ("c3", 3001, 1000), ("c4", 37, 65536), ("c4", 9, 65528), ("c5", 1031, 5120),
+          ("c5", 301, 5112)]
 
 
 @pytest.mark.parametrize("name,M,N", SCALED)
