@@ -32,7 +32,7 @@ RMSNORM_FLAG_OFFSET = 1
 PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
 KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
-                9: "fwd_pipe", 10: "bwd_pipe"}
+                9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long"}
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",

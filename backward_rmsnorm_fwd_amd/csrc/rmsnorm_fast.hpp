@@ -104,6 +104,38 @@ struct RowAccess<false> {
   }
 };
 
+// Row access in the scalar-base form: the row base is wave-uniform (kernel
+// argument plus a uniform row offset, held in SGPRs) and each lane adds one
+// 32-bit byte offset, so no chunk costs a 64-bit address in VGPRs.  The lane
+// offset is made opaque per use: the compiler can then neither hoist a load
+// out of the row loop nor merge two loads of one address (either would keep
+// values live across a whole row and exhaust the register file).
+struct URow {
+  const char* p;
+  __device__ __forceinline__ explicit URow(const void* base) : p(static_cast<const char*>(base)) {}
+  __device__ __forceinline__ const char* at(uint32_t voff, uint32_t soff) const {
+    uint32_t o = voff + soff;
+    asm volatile("" : "+v"(o));
+    return p + o;
+  }
+  template <bool NT>
+  __device__ __forceinline__ u32x4 load(uint32_t voff, uint32_t soff) const {
+    const u32x4* a = reinterpret_cast<const u32x4*>(at(voff, soff));
+    if constexpr (NT) return __builtin_nontemporal_load(a);
+    else return *a;
+  }
+  template <bool NT>
+  __device__ __forceinline__ void store(u32x4 v, uint32_t voff, uint32_t soff) const {
+    u32x4* a = reinterpret_cast<u32x4*>(const_cast<char*>(at(voff, soff)));
+    if constexpr (NT) __builtin_nontemporal_store(v, a);
+    else *a = v;
+  }
+  __device__ __forceinline__ void to_lds(void* lds_wave_base, uint32_t voff, uint32_t soff) const {
+    __builtin_amdgcn_global_load_lds(const_cast<char*>(at(voff, soff)),
+                                     (lds_void_t*)lds_wave_base, 16, 0, 0);
+  }
+};
+
 // Scheduling fence: no instruction moves across it.  Placed between the
 // chunks of a sweep so the scheduler does not widen every chunk at once
 // (which multiplies the live float32 temporaries and spills).
@@ -924,6 +956,163 @@ inline int64_t bwd_pipe_lds_bytes(int N) {
   const int64_t stage = 2 * (DLDS ? 2 : 1) * static_cast<int64_t>(Geo::G) * N * ElemBytes<DT>::value;
   const int64_t comb = Geo::G > 1 ? static_cast<int64_t>(Geo::G) * Geo::SWEEP * 4 : 0;
   return stage > comb ? stage : comb;
+}
+
+// ---------------------------------------------------------------------------
+// Backward stage 1 for long rows (16 KiB < row <= 128 KiB): one 512-thread
+// workgroup streams whole rows, CH = ceil(row / 8 KiB) chunks per lane.
+//
+// Per row, x sits in LDS (DMA) and dy in registers, so x, dy and the dgamma
+// accumulators of a 128 KiB row stay on chip: 8 wavefronts of 512 threads
+// may hold 256 VGPRs each (dy: 4*CH, accumulators: VEC*CH).
+//   pass A  dot = sum(dy*g*x)               (x read back from LDS)
+//   reduce  across the 8 wavefronts (LDS-only barrier)
+//   pass B  dx = r*u - x*(r^3*dot/N), acc += (dy*x)*r; after chunk c is done
+//           its LDS slot and dy registers take the next row's chunk c, so the
+//           next row streams in behind the current row's dx stores.
+// The weight is read from cache one chunk ahead of its use, so its wait
+// never covers a store issued after it (one in-order counter for all vector
+// memory operations).  An LDS read of x waits, through an operand
+// dependency, for the dy load of the same chunk; that load was issued right
+// after the chunk's DMA, so its completion implies the DMA's.
+// ---------------------------------------------------------------------------
+
+// Pins a value at this point of the program: its computation cannot be
+// sunk below (or hoisted above) the statement, so a chunk's arithmetic stays
+// with its chunk and dead inputs free their registers.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
+// 16 bytes from LDS once `dep` (a register loaded after the DMA that filled
+// this LDS address) has arrived; complete on return.
+__device__ __forceinline__ u32x4 lds_read16_after(const void* p, const u32x4& dep) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a), "v"(dep) : "memory");
+  return v;
+}
+
+template <int DT, int CH, bool NT>
+__global__ __launch_bounds__(512) void bwd_longrow_kernel(
+    const void* __restrict__ dy, const void* __restrict__ x,
+    const void* __restrict__ gamma, const float* __restrict__ rstd,
+    void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
+    int64_t P) {
+  constexpr int WPR = 8, BLOCK = 512;
+  using Geo = Geometry<DT, CH, WPR, BLOCK>;
+  constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
+  constexpr uint32_t kChunk = TPR * 16;
+  using PK = Pack<DT, VEC>;
+  extern __shared__ __align__(16) char dyn[];  // [N] elements of x
+  __shared__ float slots[2 * WPR];
+  const int t = threadIdx.x;
+  const int wave = uniform(t / kWave);
+  const int lane = t % kWave;
+  const uint32_t voff = t * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
+  const uint32_t dma_off = wave * kWave * 16;
+  int parity = 0;
+  const int64_t w = blockIdx.x;
+  const RowSched<true> rs(w, M, P, 1);
+  const float n_f = static_cast<float>(N);
+  const URow gbuf(gamma);
+
+  PK dv[CH];
+  float acc[CH][VEC];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
+
+  auto in_row = [&](int c) __attribute__((always_inline)) {
+    return c < CH - 1 || voff + c * kChunk < row_bytes;
+  };
+  auto issue_chunk = [&](int64_t row, int c) __attribute__((always_inline)) {
+    if (in_row(c)) {
+      const URow xb(static_cast<const char*>(x) + row * row_bytes);
+      const URow db(static_cast<const char*>(dy) + row * row_bytes);
+      xb.to_lds(dyn + c * kChunk + dma_off, voff, c * kChunk);  // DMA first,
+      dv[c].raw = db.template load<NT>(voff, c * kChunk);        // then dy
+    } else {
+      dv[c].zero();
+    }
+  };
+  auto load_g = [&](int c) __attribute__((always_inline)) {
+    PK g;
+    if (in_row(c)) g.raw = gbuf.template load<false>(voff, c * kChunk);
+    else g.zero();
+    return g;
+  };
+
+  if (rs.iters > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) issue_chunk(rs.base, c);
+  }
+  for (int64_t it = 0; it < rs.iters; ++it) {
+    const int64_t row = rs.base + it * rs.stride;  // always < M here
+    const bool has_next = it + 1 < rs.iters;
+    const float r = rstd[row];
+
+    // pass A
+    float dot = 0.f;
+    PK gc = load_g(0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      PK gn;
+      if (c + 1 < CH) gn = load_g(c + 1);
+      dv[c].opaque();  // widen this chunk here, not where it was loaded
+      if (in_row(c)) {
+        PK xv;
+        xv.raw = lds_read16_after(dyn + c * kChunk + voff, dv[c].raw);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k)
+          dot = fmaf(dv[c].get(k) * weight_of(gc.get(k), offset), xv.get(k), dot);
+      }
+      pin(dot);
+      if (c + 1 < CH) gc = gn;
+      chunk_fence();
+    }
+    dot = group_sum_lds<WPR, 1>(dot, slots, parity, 0, wave, lane);
+    const float r3c = ((r * r) * r) * (dot / n_f);
+
+    // pass B
+    const URow ob(static_cast<char*>(dx) + row * row_bytes);
+    gc = load_g(0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      PK gn;
+      if (c + 1 < CH) gn = load_g(c + 1);
+      dv[c].opaque();  // re-widen here rather than keep pass A's floats
+      if (in_row(c)) {
+        PK xv;
+        xv.raw = lds_read16_after(dyn + c * kChunk + voff, dv[c].raw);
+        float o[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float xf = xv.get(k);
+          const float dyf = dv[c].get(k);
+          const float u = dyf * weight_of(gc.get(k), offset);
+          o[k] = fmaf(-xf, r3c, r * u);
+          acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
+        }
+        PK out;
+        out.set(o);
+        ob.template store<NT>(out.raw, voff, c * kChunk);
+      }
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) pin(acc[c][k]);
+      order_fence();
+      if (has_next) issue_chunk(row + rs.stride, c);
+      order_fence();
+      if (c + 1 < CH) gc = gn;
+    }
+  }
+
+  float* dst = part + w * static_cast<int64_t>(N);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int e = (c * TPR + t) * VEC;
+    if (c < CH - 1 || e < N) store_f32<VEC>(dst + e, acc[c]);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -57,4 +57,15 @@ hipError_t pipe_bwd_launch<kF32>(int wpr, int ch, int block, int dlds, int64_t l
   return hipErrorInvalidValue;
 }
 
+template <>
+hipError_t long_bwd_launch<kF32>(int ch, int64_t lds, const FastBwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(C)                                                                        \
+  if (ch == C)                                                                              \
+    return launch(bwd_longrow_kernel<kF32, C, true>, a.P, 512, static_cast<size_t>(lds), s,   \
+                  a.dy, a.x, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, a.P);
+  RMSNORM_BWD_LONG_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
 }  // namespace rmsnorm_hip

@@ -6,6 +6,7 @@
 // Backward entries: X(WPR, CH, BLOCK, GREG, XLDS)
 // Pipelined forward entries:  X(WPR, CH, BLOCK, XL)
 // Pipelined backward entries: X(WPR, CH, BLOCK, DLDS)
+// Long-row backward entries: X(CH), 512 threads per row
 //   WPR  wavefronts per row, CH 16-byte chunks per thread and row,
 //   BLOCK threads per workgroup, GREG weight held in registers across rows,
 //   XLDS / XL x staged in LDS by DMA, DLDS dy staged in LDS too.  The
@@ -25,14 +26,12 @@
   X(16, 9, 1024, 0) X(16, 10, 1024, 0) X(16, 11, 1024, 0) X(16, 12, 1024, 0)      \
   X(16, 13, 1024, 0) X(16, 14, 1024, 0) X(16, 15, 1024, 0) X(16, 16, 1024, 0)
 
-#define RMSNORM_BWD_FAST_LIST(X)                                                  \
-  X(1, 1, 1024, 1, 1) X(2, 1, 1024, 1, 1) X(4, 1, 1024, 1, 1)                     \
-  X(2, 2, 1024, 1, 1) X(4, 2, 1024, 1, 1) X(8, 2, 1024, 1, 1) X(16, 2, 1024, 1, 1) \
-  X(16, 3, 1024, 1, 1)                                                            \
-  X(16, 4, 1024, 0, 1) X(16, 5, 1024, 0, 1) X(16, 6, 1024, 0, 1)                  \
-  X(16, 7, 1024, 0, 1) X(16, 8, 1024, 0, 1)
+#define RMSNORM_BWD_FAST_LIST(X) X(4, 2, 1024, 1, 1)
 
 #define RMSNORM_FWD_PIPE_LIST(X) X(2, 3, 1024, 1) X(2, 4, 1024, 1)
 
 #define RMSNORM_BWD_PIPE_LIST(X) \
   X(1, 1, 1024, 0) X(2, 1, 1024, 0) X(4, 1, 1024, 0) X(16, 1, 1024, 1)
+
+#define RMSNORM_BWD_LONG_LIST(X) \
+  X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)

@@ -69,5 +69,7 @@ hipError_t pipe_fwd_launch(int wpr, int ch, int block, int xl, int64_t grid, int
 template <int DT>
 hipError_t pipe_bwd_launch(int wpr, int ch, int block, int dlds, int64_t lds,
                            const FastBwdArgs& a, hipStream_t s);
+template <int DT>
+hipError_t long_bwd_launch(int ch, int64_t lds, const FastBwdArgs& a, hipStream_t s);
 
 }  // namespace rmsnorm_hip

@@ -191,6 +191,10 @@ typedef struct {
  * prefetches the next row while it computes the current one. */
 #define RMSNORM_KERNEL_FWD_PIPE 9  /* forward */
 #define RMSNORM_KERNEL_BWD_PIPE 10 /* backward stage 1 */
+/* Backward stage 1 for rows of 16-128 KiB: one 512-thread workgroup per
+ * row, x staged in LDS and dy in registers for the whole row, the next
+ * row's chunks loaded behind the current row's dx stores. */
+#define RMSNORM_KERNEL_BWD_LONG 11
 
 #define RMSNORM_PASS_FWD 0
 #define RMSNORM_PASS_BWD_ROWS 1

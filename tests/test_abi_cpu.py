@@ -149,7 +149,8 @@ def test_plans_for_the_workloads():
     c3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_FWD)
     assert c3["kernel_name"] == "fwd_rows" and (c3["threads_per_row"], c3["chunks"]) == (64, 2)
     c4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_ROWS)
-    assert c4["kernel_name"] == "bwd_rows" and c4["threads_per_row"] == 1024
+    assert c4["kernel_name"] == "bwd_long" and c4["threads_per_row"] == 512
+    assert c4["chunks"] == 16 and c4["partials"] == 256
     assert c4["x_in_lds"] == 1 and c4["lds_bytes"] == 65536 * 2
     c5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_BWD_ROWS)
     assert c5["kernel_name"] == "bwd_pipe" and (c5["threads_per_row"], c5["chunks"]) == (1024, 1)
@@ -187,9 +188,10 @@ def test_full_width_plan_used_for_aligned_rows():
             if dt == 0 and n > 32768:
                 assert b["kernel_name"] in ("bwd_wave", "bwd_block"), (dt, n)
             else:
-                assert b["kernel_name"] in ("bwd_rows", "bwd_pipe"), (dt, n)
+                assert b["kernel_name"] in ("bwd_rows", "bwd_pipe", "bwd_long"), (dt, n)
                 pipe = n * es <= 4096 or 8192 < n * es <= 16384
                 assert (b["kernel_name"] == "bwd_pipe") == pipe, (dt, n)
+                assert (b["kernel_name"] == "bwd_long") == (n * es > 16384), (dt, n)
 
 
 def test_plan_covers_every_n():
