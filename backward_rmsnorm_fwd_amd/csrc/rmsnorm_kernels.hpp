@@ -190,7 +190,10 @@ __device__ __forceinline__ float block_sum(float v, float* slots, int& parity,
 }
 
 __device__ __forceinline__ float weight_of(float w, int offset) {
-  return offset ? 1.0f + w : w;
+  // One add per use: the uniform bias (1 or 0) is selected once per kernel.
+  // w + 0 equals w except that a weight of -0 is read as +0, so the zero
+  // products it scales may come out with the other sign (equal in value).
+  return w + (offset ? 1.0f : 0.0f);
 }
 
 // ---------------------------------------------------------------------------
