@@ -21,14 +21,16 @@ import torch
 
 __all__ = [
     "RMSNORM_F32", "RMSNORM_F16", "RMSNORM_BF16", "RMSNORM_FLAG_OFFSET",
+    "RMSNORM_FLAG_DGAMMA_IN_DTYPE",
     "RmsnormError", "library_path", "load_library", "rmsnorm_status_string",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
-    "rmsnorm_bwd_workspace_bytes", "rmsnorm_query_plan", "fwd", "bwd",
-    "EXPORTED_SYMBOLS",
+    "rmsnorm_bwd_workspace_bytes", "rmsnorm_query_plan", "rmsnorm_fwd_strided",
+    "rmsnorm_bwd_strided", "row_layout", "fwd", "bwd", "EXPORTED_SYMBOLS",
 ]
 
 RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
 RMSNORM_FLAG_OFFSET = 1
+RMSNORM_FLAG_DGAMMA_IN_DTYPE = 2
 PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
 KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
@@ -37,6 +39,7 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_status_string", "rmsnorm_query_plan",
+    "rmsnorm_fwd_strided", "rmsnorm_bwd_strided",
 )
 
 _DTYPES = {torch.float32: RMSNORM_F32, torch.float16: RMSNORM_F16,
@@ -96,6 +99,11 @@ def load_library():
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     lib.rmsnorm_query_plan.argtypes = [i64, i64, i32, u32, i32, i32, ctypes.POINTER(Plan)]
     lib.rmsnorm_query_plan.restype = i32
+    lib.rmsnorm_fwd_strided.argtypes = [vp, i64, vp, f32, i64, i64, i32, u32, vp, i64, vp, vp]
+    lib.rmsnorm_fwd_strided.restype = i32
+    lib.rmsnorm_bwd_strided.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, u32, vp, i64,
+                                        vp, vp, sz, vp]
+    lib.rmsnorm_bwd_strided.restype = i32
     _LIB = lib
     return lib
 
@@ -135,13 +143,41 @@ def _rows(x):
     return m, n
 
 
+def row_layout(t):
+    """``(M, N, ld)`` when ``t`` is M rows of N unit-stride elements whose
+    starts are ``ld`` elements apart (leading dims flatten into M), else None."""
+    if t.dim() == 0:
+        return None
+    n = t.shape[-1]
+    if n > 1 and t.stride(-1) != 1:
+        return None
+    m = t.numel() // n if n else 0
+    ld = None
+    expect = None
+    for size, stride in zip(reversed(t.shape[:-1]), reversed(t.stride()[:-1])):
+        if size == 1:
+            continue
+        if ld is None:
+            ld, expect = stride, stride * size
+        elif stride != expect:
+            return None
+        else:
+            expect = stride * size
+    if ld is None:
+        ld = n
+    if ld < n:
+        return None
+    return m, n, ld
+
+
 def _require(cond, msg):
     if not cond:
         raise ValueError(msg)
 
 
-def _flags(offset):
-    return RMSNORM_FLAG_OFFSET if offset else 0
+def _flags(offset, dgamma_in_dtype=False):
+    return ((RMSNORM_FLAG_OFFSET if offset else 0)
+            | (RMSNORM_FLAG_DGAMMA_IN_DTYPE if dgamma_in_dtype else 0))
 
 
 # ---- one-to-one wrappers of the C entry points ------------------------------
@@ -176,19 +212,54 @@ def rmsnorm_bwd_rows(dy, x, gamma, rstd, dx, workspace, offset=False, stream=Non
 
 
 def rmsnorm_bwd_reduce(workspace, M, N, dtype, dgamma, offset=False, stream=None):
+    """dgamma float32, or of ``dtype`` (RMSNORM_FLAG_DGAMMA_IN_DTYPE) when the
+    dgamma tensor has that dtype."""
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    in_dtype = dgamma.dtype != torch.float32
     _check("rmsnorm_bwd_reduce", load_library().rmsnorm_bwd_reduce(
-        _ptr(workspace), ws_bytes, int(M), int(N), code, _flags(offset), _ptr(dgamma),
-        _stream(dgamma.device, stream)))
+        _ptr(workspace), ws_bytes, int(M), int(N), code, _flags(offset, in_dtype),
+        _ptr(dgamma), _stream(dgamma.device, stream)))
+
+
+def _layout(t, name):
+    lay = row_layout(t)
+    _require(lay is not None, f"{name} must be rows of unit-stride elements at one row stride")
+    return lay
+
+
+def rmsnorm_fwd_strided(x, gamma, eps, y, rstd, offset=False, stream=None):
+    """rmsnorm_fwd with the row strides of x and y taken from the tensors."""
+    m, n, ldx = _layout(x, "x")
+    _, _, ldy = _layout(y, "y")
+    _check("rmsnorm_fwd_strided", load_library().rmsnorm_fwd_strided(
+        _ptr(x), ldx, _ptr(gamma), float(eps), m, n, _dtype_code(x), _flags(offset),
+        _ptr(y), ldy, _ptr(rstd), _stream(x.device, stream)))
+
+
+def rmsnorm_bwd_strided(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=None):
+    """rmsnorm_bwd with the row strides of dy, x and dx taken from the tensors."""
+    m, n, ldx = _layout(x, "x")
+    _, _, lddy = _layout(dy, "dy")
+    _, _, lddx = _layout(dx, "dx")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    in_dtype = dgamma.dtype != torch.float32
+    _check("rmsnorm_bwd_strided", load_library().rmsnorm_bwd_strided(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
+        _flags(offset, in_dtype), _ptr(dx), lddx, _ptr(dgamma), _ptr(workspace), ws_bytes,
+        _stream(x.device, stream)))
 
 
 def rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=None):
+    """As rmsnorm_bwd_reduce, dgamma may be float32 or of x's dtype."""
     m, n = _rows(x)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    in_dtype = dgamma.dtype != torch.float32
+    _require(not in_dtype or dgamma.dtype == x.dtype, "dgamma must be float32 or x's dtype")
     _check("rmsnorm_bwd", load_library().rmsnorm_bwd(
-        _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x), _flags(offset),
-        _ptr(dx), _ptr(dgamma), _ptr(workspace), ws_bytes, _stream(x.device, stream)))
+        _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
+        _flags(offset, in_dtype), _ptr(dx), _ptr(dgamma), _ptr(workspace), ws_bytes,
+        _stream(x.device, stream)))
 
 
 # ---- allocating front ends ----------------------------------------------------
@@ -196,7 +267,9 @@ def rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=
 def _check_inputs(x, gamma):
     _require(x.is_cuda and gamma.is_cuda, "x and gamma must be device tensors")
     _require(x.device == gamma.device, "x and gamma must be on the same device")
-    _require(x.is_contiguous() and gamma.is_contiguous(), "x and gamma must be contiguous")
+    _require(gamma.is_contiguous(), "gamma must be contiguous")
+    _require(row_layout(x) is not None,
+             "x must be rows of unit-stride elements at one row stride")
     _require(gamma.dim() == 1 and gamma.shape[0] == x.shape[-1],
              "gamma must be 1-D with the length of x's last dimension")
     _require(x.dtype == gamma.dtype, "x and gamma must share a dtype")
@@ -208,37 +281,35 @@ def fwd(x, gamma, eps=1e-6, offset=False, stream=None, poison=False):
     ``poison`` fills the outputs with NaN first (tests use it to show every
     element is written)."""
     _check_inputs(x, gamma)
-    m, _ = _rows(x)
-    if poison:
-        y = torch.full_like(x, float("nan"))
-        rstd = torch.full((m,), float("nan"), device=x.device, dtype=torch.float32)
-    else:
-        y = torch.empty_like(x)
-        rstd = torch.empty((m,), device=x.device, dtype=torch.float32)
-    rmsnorm_fwd(x, gamma, eps, y, rstd, offset, stream)
+    m, _, _ = row_layout(x)
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    y = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)  # dense rows
+    rstd = fill((m,), float("nan"), device=x.device, dtype=torch.float32)
+    rmsnorm_fwd_strided(x, gamma, eps, y, rstd, offset, stream)
     return y, rstd
 
 
-def bwd(dy, x, gamma, rstd, offset=False, stream=None, poison=False, workspace=None):
-    """Returns ``(dx, dgamma)``: dx like x, dgamma float32 [N] (a row sum).
+def bwd(dy, x, gamma, rstd, offset=False, stream=None, poison=False, workspace=None,
+        dgamma_dtype=torch.float32):
+    """Returns ``(dx, dgamma)``: dx like x, dgamma [N] (a row sum) in
+    ``dgamma_dtype``: float32 (default) or x's dtype.
 
-    dy is made contiguous (as the page's autograd wrapper does); x and gamma
-    must already be."""
+    x and dy may have any row stride; dy in another layout is made
+    contiguous (as the page's autograd wrapper does)."""
     _check_inputs(x, gamma)
     _require(dy.shape == x.shape and dy.dtype == x.dtype and dy.device == x.device,
              "dy must match x in shape, dtype and device")
-    dy = dy.contiguous()
-    m, n = _rows(x)
+    if row_layout(dy) is None:
+        dy = dy.contiguous()
+    m, n, _ = row_layout(x)
     _require(rstd.dtype == torch.float32 and rstd.numel() == m and rstd.is_contiguous(),
              "rstd must be a contiguous float32 tensor with one value per row")
-    if poison:
-        dx = torch.full_like(x, float("nan"))
-        dgamma = torch.full((n,), float("nan"), device=x.device, dtype=torch.float32)
-    else:
-        dx = torch.empty_like(x)
-        dgamma = torch.empty((n,), device=x.device, dtype=torch.float32)
+    _require(dgamma_dtype in (torch.float32, x.dtype), "dgamma_dtype must be float32 or x's dtype")
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    dx = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)  # dense rows
+    dgamma = fill((n,), float("nan"), device=x.device, dtype=dgamma_dtype)
     if workspace is None:
         nbytes = rmsnorm_bwd_workspace_bytes(m, n, x.dtype, offset)
         workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
-    rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset, stream)
+    rmsnorm_bwd_strided(dy, x, gamma, rstd, dx, dgamma, workspace, offset, stream)
     return dx, dgamma

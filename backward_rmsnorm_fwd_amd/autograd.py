@@ -5,9 +5,10 @@ accelerating it", section "Connecting Autograd and actually training":
 
 * the forward keeps x, the weight and the per-row inverse RMS for the
   backward, so eps is not needed again;
-* the backward takes dy made contiguous, computes dx and the weight gradient
-  with the library's two backward stages, and casts the weight gradient to
-  the weight's dtype;
+* the backward takes dy (made contiguous unless its rows are evenly
+  strided), computes dx and the weight gradient
+  with the library's two backward stages; the weight gradient comes out in
+  the weight's dtype (the library rounds its float32 sum once);
 * eps and the offset flag are not differentiated.
 
 Both passes run the HIP kernels through ``rmsnorm_fwd`` / ``rmsnorm_bwd``.
@@ -23,6 +24,7 @@ import torch
 
 from . import bwd as _bwd
 from . import fwd as _fwd
+from . import row_layout
 
 __all__ = ["CALLS", "RMSNormFunction", "rmsnorm", "RMSNorm"]
 
@@ -35,9 +37,9 @@ class RMSNormFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, weight, eps, offset):
-        # The library reads rows at a stride of N elements; other layouts are
-        # copied once here.
-        xc = x.contiguous()
+        # The library reads rows at any row stride; other layouts are copied
+        # once here.
+        xc = x if row_layout(x) is not None else x.contiguous()
         y, rstd = _fwd(xc, weight, eps, offset)
         ctx.save_for_backward(xc, weight, rstd)
         ctx.offset = bool(offset)
@@ -47,10 +49,9 @@ class RMSNormFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         xc, weight, rstd = ctx.saved_tensors
-        dx, dgamma = _bwd(dy.contiguous(), xc, weight, rstd, ctx.offset)
+        dx, dgamma = _bwd(dy, xc, weight, rstd, ctx.offset, dgamma_dtype=weight.dtype)
         CALLS["backward"] += 1
-        dw = dgamma.to(weight.dtype) if ctx.needs_input_grad[1] else None
-        return dx, dw, None, None
+        return dx, (dgamma if ctx.needs_input_grad[1] else None), None, None
 
 
 def rmsnorm(x, weight, eps=1e-6, offset=False):

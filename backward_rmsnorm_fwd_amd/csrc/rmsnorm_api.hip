@@ -413,6 +413,12 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
   }
 }
 
+// Elements between the starts of consecutive rows of each matrix (N for a
+// dense matrix).
+struct RowStrides {
+  int64_t x, y, dy, dx;
+};
+
 // ---- dispatch over the compile-time (dtype, vec, maxc) instantiations ----
 // maxc (register chunk slots) is the next power of two >= chunks: up to 16
 // for every vector width, and beyond that only where a 65536-wide row over
@@ -430,15 +436,15 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
 template <int DT, int VEC>
 hipError_t fwd_dispatch(const rmsnorm_plan_t& p, const void* x, const void* g,
                         void* y, float* rstd, int64_t M, int N, float eps,
-                        int offset, hipStream_t s) {
+                        int offset, const RowStrides& ld, hipStream_t s) {
   hipError_t err = hipErrorInvalidValue;
   const int maxc = pow2_at_least(p.chunks);
 #define FWD_LAUNCH(DT_, VEC_, MAXC_)                                              \
   err = (p.kernel == RMSNORM_KERNEL_FWD_WAVE)                                     \
             ? launch(fwd_wave_kernel<DT_, VEC_, MAXC_>, p.grid, p.block_threads, 0, \
-                     s, x, g, y, rstd, M, N, p.chunks, eps, offset)               \
+                     s, x, g, y, rstd, M, N, p.chunks, eps, offset, ld.x, ld.y)   \
             : launch(fwd_block_kernel<DT_, VEC_, MAXC_>, p.grid, p.block_threads, 0, \
-                     s, x, g, y, rstd, M, N, p.chunks, eps, offset)
+                     s, x, g, y, rstd, M, N, p.chunks, eps, offset, ld.x, ld.y)
   switch (maxc) { RMSNORM_MAXC_CASES(FWD_LAUNCH, DT, VEC) default: break; }
 #undef FWD_LAUNCH
   return err;
@@ -447,7 +453,8 @@ hipError_t fwd_dispatch(const rmsnorm_plan_t& p, const void* x, const void* g,
 template <int DT, int VEC>
 hipError_t bwd_rows_dispatch(const rmsnorm_plan_t& p, const void* dy, const void* x,
                              const void* g, const float* rstd, void* dx, float* part,
-                             int64_t M, int N, int offset, hipStream_t s) {
+                             int64_t M, int N, int offset, const RowStrides& ld,
+                             hipStream_t s) {
   hipError_t err = hipErrorInvalidValue;
   const int maxc = pow2_at_least(p.chunks);
   const int64_t P = p.partials;
@@ -455,15 +462,15 @@ hipError_t bwd_rows_dispatch(const rmsnorm_plan_t& p, const void* dy, const void
   if (p.kernel == RMSNORM_KERNEL_BWD_WAVE)                                             \
     err = launch(bwd_wave_kernel<DT_, VEC_, MAXC_>, p.grid, p.block_threads,           \
                  static_cast<size_t>(p.lds_bytes), s, dy, x, g, rstd, dx, part, M, N,  \
-                 p.chunks, offset, P);                                                 \
+                 p.chunks, offset, P, ld.dy, ld.x, ld.dx);                             \
   else if (p.x_in_lds)                                                                 \
     err = launch(bwd_block_kernel<DT_, VEC_, MAXC_, true>, p.grid, p.block_threads,    \
                  static_cast<size_t>(p.lds_bytes), s, dy, x, g, rstd, dx, part, M, N,  \
-                 p.chunks, offset, P);                                                 \
+                 p.chunks, offset, P, ld.dy, ld.x, ld.dx);                             \
   else                                                                                 \
     err = launch(bwd_block_kernel<DT_, VEC_, MAXC_, false>, p.grid, p.block_threads,   \
                  static_cast<size_t>(p.lds_bytes), s, dy, x, g, rstd, dx, part, M, N,  \
-                 p.chunks, offset, P)
+                 p.chunks, offset, P, ld.dy, ld.x, ld.dx)
   switch (maxc) { RMSNORM_MAXC_CASES(BWD_LAUNCH, DT, VEC) default: break; }
 #undef BWD_LAUNCH
   return err;
@@ -472,24 +479,22 @@ hipError_t bwd_rows_dispatch(const rmsnorm_plan_t& p, const void* dy, const void
 template <int DT>
 hipError_t fwd_by_vec(const rmsnorm_plan_t& p, const void* x, const void* g, void* y,
                       float* rstd, int64_t M, int N, float eps, int offset,
-                      hipStream_t s) {
+                      const RowStrides& ld, hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
-  if (p.kernel == RMSNORM_KERNEL_FWD_ROWS) {
-    const FastFwdArgs a{x, g, y, rstd, M, N, eps, offset};
-    return fast_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
-                               p.weight_in_regs, p.grid, a, s);
-  }
-  if (p.kernel == RMSNORM_KERNEL_FWD_PIPE) {
-    const FastFwdArgs a{x, g, y, rstd, M, N, eps, offset};
+  if (p.kernel == RMSNORM_KERNEL_FWD_ROWS || p.kernel == RMSNORM_KERNEL_FWD_PIPE) {
+    const FastFwdArgs a{x, g, y, rstd, M, N, eps, offset, ld.x * es, ld.y * es};
+    if (p.kernel == RMSNORM_KERNEL_FWD_ROWS)
+      return fast_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
+                                 p.weight_in_regs, p.grid, a, s);
     return pipe_fwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads, p.x_in_lds,
                                p.grid, p.lds_bytes, a, s);
   }
   switch (p.vec * es) {
-    case 16: return fwd_dispatch<DT, 16 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
-    case 8: return fwd_dispatch<DT, 8 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
-    case 4: return fwd_dispatch<DT, 4 / es>(p, x, g, y, rstd, M, N, eps, offset, s);
+    case 16: return fwd_dispatch<DT, 16 / es>(p, x, g, y, rstd, M, N, eps, offset, ld, s);
+    case 8: return fwd_dispatch<DT, 8 / es>(p, x, g, y, rstd, M, N, eps, offset, ld, s);
+    case 4: return fwd_dispatch<DT, 4 / es>(p, x, g, y, rstd, M, N, eps, offset, ld, s);
     case 2:
-      if constexpr (es == 2) return fwd_dispatch<DT, 1>(p, x, g, y, rstd, M, N, eps, offset, s);
+      if constexpr (es == 2) return fwd_dispatch<DT, 1>(p, x, g, y, rstd, M, N, eps, offset, ld, s);
       break;
     default: break;
   }
@@ -499,29 +504,28 @@ hipError_t fwd_by_vec(const rmsnorm_plan_t& p, const void* x, const void* g, voi
 template <int DT>
 hipError_t bwd_rows_by_vec(const rmsnorm_plan_t& p, const void* dy, const void* x,
                            const void* g, const float* rstd, void* dx, float* part,
-                           int64_t M, int N, int offset, hipStream_t s) {
+                           int64_t M, int N, int offset, const RowStrides& ld, hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
-  if (p.kernel == RMSNORM_KERNEL_BWD_ROWS) {
-    const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
-    return fast_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
-                               p.weight_in_regs, p.x_in_lds, p.lds_bytes, a, s);
-  }
-  if (p.kernel == RMSNORM_KERNEL_BWD_LONG) {
-    const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
-    return long_bwd_launch<DT>(p.chunks, p.lds_bytes, a, s);
-  }
-  if (p.kernel == RMSNORM_KERNEL_BWD_PIPE) {
-    const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials};
-    return pipe_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads, p.dy_in_lds,
-                               p.lds_bytes, a, s);
+  const FastBwdArgs a{dy, x, g, rstd, dx, part, M, N, offset, p.partials,
+                      ld.dy * es, ld.x * es, ld.dx * es};
+  switch (p.kernel) {
+    case RMSNORM_KERNEL_BWD_ROWS:
+      return fast_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
+                                 p.weight_in_regs, p.x_in_lds, p.lds_bytes, a, s);
+    case RMSNORM_KERNEL_BWD_LONG:
+      return long_bwd_launch<DT>(p.chunks, p.lds_bytes, a, s);
+    case RMSNORM_KERNEL_BWD_PIPE:
+      return pipe_bwd_launch<DT>(p.threads_per_row / 64, p.chunks, p.block_threads,
+                                 p.dy_in_lds, p.lds_bytes, a, s);
+    default: break;
   }
   switch (p.vec * es) {
-    case 16: return bwd_rows_dispatch<DT, 16 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
-    case 8: return bwd_rows_dispatch<DT, 8 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
-    case 4: return bwd_rows_dispatch<DT, 4 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
+    case 16: return bwd_rows_dispatch<DT, 16 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, ld, s);
+    case 8: return bwd_rows_dispatch<DT, 8 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, ld, s);
+    case 4: return bwd_rows_dispatch<DT, 4 / es>(p, dy, x, g, rstd, dx, part, M, N, offset, ld, s);
     case 2:
       if constexpr (es == 2)
-        return bwd_rows_dispatch<DT, 1>(p, dy, x, g, rstd, dx, part, M, N, offset, s);
+        return bwd_rows_dispatch<DT, 1>(p, dy, x, g, rstd, dx, part, M, N, offset, ld, s);
       break;
     default: break;
   }
@@ -533,34 +537,70 @@ hipError_t bwd_rows_by_vec(const rmsnorm_plan_t& p, const void* dy, const void* 
 int check_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
   if (dtype != RMSNORM_F32 && dtype != RMSNORM_F16 && dtype != RMSNORM_BF16)
     return RMSNORM_ERR_DTYPE;
-  if (flags & ~RMSNORM_FLAG_OFFSET) return RMSNORM_ERR_FLAGS;
+  if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
   if (N < 1 || N > RMSNORM_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
   return RMSNORM_OK;
+}
+
+// Bytes per dgamma element: float32, or the input dtype with
+// RMSNORM_FLAG_DGAMMA_IN_DTYPE.
+int dgamma_elem_bytes(int dtype, uint32_t flags) {
+  return (flags & RMSNORM_FLAG_DGAMMA_IN_DTYPE) ? elem_bytes(dtype) : 4;
 }
 
 bool misaligned(const void* p, int bytes) {
   return p && (reinterpret_cast<uintptr_t>(p) % bytes) != 0;
 }
 
-struct Span {
-  uintptr_t lo, hi;  // [lo, hi)
+// Largest power of two <= 16 dividing v (v > 0).
+int alignment_of(int64_t v) {
+  int a = 16;
+  while (a > 1 && v % a) a >>= 1;
+  return a;
+}
+
+// Memory touched by a matrix of `rows` rows of `width` bytes whose starts are
+// `pitch` bytes apart (a vector is one row).
+struct Region {
+  int64_t base, pitch, rows, width;
 };
 
-Span span(const void* p, int64_t bytes) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  return {a, a + static_cast<uintptr_t>(bytes)};
+Region matrix(const void* p, int64_t rows, int64_t pitch, int64_t width) {
+  return {static_cast<int64_t>(reinterpret_cast<uintptr_t>(p)), pitch, rows, width};
 }
 
-bool overlaps(Span a, Span b) {
-  if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
-  return a.lo < b.hi && b.lo < a.hi;
+Region vec(const void* p, int64_t bytes) { return matrix(p, bytes > 0 ? 1 : 0, bytes, bytes); }
+
+// Whether two regions share a byte.  Extents are compared first; two matrices
+// with one common pitch are then compared row against row, so interleaved
+// layouts (say x in the first N columns of a buffer, y in the next N) are
+// recognised as disjoint.  Other layouts with overlapping extents count as
+// overlapping.
+bool overlaps(const Region& a, const Region& b) {
+  if (a.base == 0 || b.base == 0 || a.rows == 0 || b.rows == 0 || a.width == 0 || b.width == 0)
+    return false;
+  const int64_t a_end = a.base + (a.rows - 1) * a.pitch + a.width;
+  const int64_t b_end = b.base + (b.rows - 1) * b.pitch + b.width;
+  if (a_end <= b.base || b_end <= a.base) return false;
+  if (a.pitch != b.pitch || a.rows == 1 || b.rows == 1) return true;
+  // Row i of a meets row j of b iff -b.width < d + k*pitch < a.width with
+  // d = a.base - b.base and k = i - j in [-(b.rows-1), a.rows-1]; the middle
+  // term grows with k, so only the first k past -b.width needs a look.
+  const int64_t d = a.base - b.base, p = a.pitch;
+  const int64_t k_lo = -(b.rows - 1), k_hi = a.rows - 1;
+  const int64_t num = -b.width - d;  // need k*p > num
+  int64_t k = num >= 0 ? num / p + 1 : -((-num) / p);
+  if (k * p <= num) ++k;
+  if (k < k_lo) k = k_lo;
+  if (k > k_hi) return false;
+  return d + k * p < a.width;
 }
 
-// Every output span must be disjoint from every input span and from every
-// other output span.
-bool any_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+// Every output region must be disjoint from every input region and from every
+// other output region.
+bool any_overlap(std::initializer_list<Region> outs, std::initializer_list<Region> ins) {
   for (auto o = outs.begin(); o != outs.end(); ++o) {
-    for (const Span& i : ins)
+    for (const Region& i : ins)
       if (overlaps(*o, i)) return true;
     for (auto o2 = o + 1; o2 != outs.end(); ++o2)
       if (overlaps(*o, *o2)) return true;
@@ -568,12 +608,33 @@ bool any_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> i
   return false;
 }
 
-int check_bwd_rows_args(const void* dy, const void* x, const void* gamma,
-                        const float* rstd, int64_t M, int64_t N, int dtype,
-                        uint32_t flags, const void* dx, const void* workspace,
+bool bad_stride(int64_t ld, int64_t N) { return ld < N || ld > (int64_t(1) << 40); }
+
+int check_fwd_args(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M,
+                   int64_t N, int dtype, uint32_t flags, const void* y, int64_t ldy,
+                   const float* rstd) {
+  int st = check_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_ERR_EPS;
+  if (bad_stride(ldx, N) || bad_stride(ldy, N)) return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!x || !gamma || !y || !rstd) return RMSNORM_ERR_NULL_POINTER;
+  const int es = elem_bytes(dtype);
+  if (misaligned(x, es) || misaligned(gamma, es) || misaligned(y, es) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(y, M, ldy * es, N * es), vec(rstd, M * 4)},
+                  {matrix(x, M, ldx * es, N * es), vec(gamma, N * es)}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int check_bwd_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                        const void* gamma, const float* rstd, int64_t M, int64_t N, int dtype,
+                        uint32_t flags, const void* dx, int64_t lddx, const void* workspace,
                         size_t workspace_bytes) {
   int st = check_common(M, N, dtype, flags);
   if (st != RMSNORM_OK) return st;
+  if (bad_stride(lddy, N) || bad_stride(ldx, N) || bad_stride(lddx, N)) return RMSNORM_ERR_STRIDE;
   if (M == 0) return RMSNORM_OK;
   if (!dy || !x || !gamma || !rstd || !dx) return RMSNORM_ERR_NULL_POINTER;
   const int es = elem_bytes(dtype);
@@ -583,14 +644,117 @@ int check_bwd_rows_args(const void* dy, const void* x, const void* gamma,
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, static_cast<rmsnorm_dtype_t>(dtype), flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  const int64_t mat = M * N * es;
-  if (any_overlap({span(dx, mat), span(workspace, static_cast<int64_t>(need))},
-                  {span(dy, mat), span(x, mat), span(gamma, N * es), span(rstd, M * 4)}))
+  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
+                   vec(gamma, N * es), vec(rstd, M * 4)}))
     return RMSNORM_ERR_OVERLAP;
   return RMSNORM_OK;
 }
 
+int check_dgamma_args(const void* dgamma, int64_t N, int dtype, uint32_t flags) {
+  if (!dgamma) return RMSNORM_ERR_NULL_POINTER;
+  if (misaligned(dgamma, dgamma_elem_bytes(dtype, flags))) return RMSNORM_ERR_ALIGNMENT;
+  return RMSNORM_OK;
+}
+
 int status_of(hipError_t e) { return e == hipSuccess ? RMSNORM_OK : RMSNORM_ERR_LAUNCH; }
+
+// Alignment the plan may assume: every pointer and every row pitch.
+int layout_alignment(std::initializer_list<const void*> ptrs,
+                     std::initializer_list<int64_t> pitches) {
+  int a = pointer_alignment(ptrs);
+  for (int64_t p : pitches) a = std::min(a, alignment_of(p));
+  return a;
+}
+
+int fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M, int64_t N,
+             rmsnorm_dtype_t dtype, uint32_t flags, void* y, int64_t ldy, float* rstd,
+             hipStream_t stream) {
+  int st = check_fwd_args(x, ldx, gamma, eps, M, N, dtype, flags, y, ldy, rstd);
+  if (st != RMSNORM_OK || M == 0) return st;
+  const int es = elem_bytes(dtype);
+  rmsnorm_plan_t p;
+  fill_plan(M, N, dtype, RMSNORM_PASS_FWD,
+            layout_alignment({x, gamma, y}, {ldx * es, ldy * es}), &p);
+  const int off = (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0;
+  const int n = static_cast<int>(N);
+  const RowStrides ld{ldx, ldy, 0, 0};
+  hipError_t e;
+  switch (dtype) {
+    case RMSNORM_F32: e = fwd_by_vec<kF32>(p, x, gamma, y, rstd, M, n, eps, off, ld, stream); break;
+    case RMSNORM_F16: e = fwd_by_vec<kF16>(p, x, gamma, y, rstd, M, n, eps, off, ld, stream); break;
+    default: e = fwd_by_vec<kBF16>(p, x, gamma, y, rstd, M, n, eps, off, ld, stream); break;
+  }
+  return status_of(e);
+}
+
+// Stage 1 after its arguments were checked.
+int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+                    const float* rstd, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                    uint32_t flags, void* dx, int64_t lddx, void* workspace,
+                    hipStream_t stream) {
+  if (M == 0) return RMSNORM_OK;
+  const int es = elem_bytes(dtype);
+  rmsnorm_plan_t p;
+  fill_plan(M, N, dtype, RMSNORM_PASS_BWD_ROWS,
+            layout_alignment({dy, x, gamma, dx}, {lddy * es, ldx * es, lddx * es}), &p);
+  const int off = (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0;
+  const int n = static_cast<int>(N);
+  float* part = static_cast<float*>(workspace);
+  const RowStrides ld{ldx, 0, lddy, lddx};
+  hipError_t e;
+  switch (dtype) {
+    case RMSNORM_F32: e = bwd_rows_by_vec<kF32>(p, dy, x, gamma, rstd, dx, part, M, n, off, ld, stream); break;
+    case RMSNORM_F16: e = bwd_rows_by_vec<kF16>(p, dy, x, gamma, rstd, dx, part, M, n, off, ld, stream); break;
+    default: e = bwd_rows_by_vec<kBF16>(p, dy, x, gamma, rstd, dx, part, M, n, off, ld, stream); break;
+  }
+  return status_of(e);
+}
+
+// Stage 2 after its arguments were checked.
+int bwd_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                      uint32_t flags, void* dgamma, hipStream_t stream) {
+  rmsnorm_plan_t p;
+  fill_plan(M, N, dtype, RMSNORM_PASS_BWD_REDUCE, 16, &p);
+  const float* part = static_cast<const float*>(workspace);
+  const int n = static_cast<int>(N);
+  const bool r16 = p.kernel == RMSNORM_KERNEL_BWD_REDUCE16;
+  const int out = (flags & RMSNORM_FLAG_DGAMMA_IN_DTYPE) ? static_cast<int>(dtype) : kOutF32;
+#define RMSNORM_REDUCE(OUT)                                                                 \
+  return status_of(r16 ? launch(bwd_reduce16_kernel<OUT>, p.grid, p.block_threads, 0, stream, \
+                                part, dgamma, p.partials, n)                                \
+                       : launch(bwd_reduce_kernel<OUT>, p.grid, p.block_threads, 0, stream,   \
+                                part, dgamma, p.partials, n))
+  switch (out) {
+    case kF32: RMSNORM_REDUCE(kF32);
+    case kF16: RMSNORM_REDUCE(kF16);
+    case kBF16: RMSNORM_REDUCE(kBF16);
+    default: RMSNORM_REDUCE(kOutF32);
+  }
+#undef RMSNORM_REDUCE
+}
+
+int bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+             const float* rstd, int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
+             void* dx, int64_t lddx, void* dgamma, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+  int st = check_bwd_rows_args(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, flags, dx, lddx,
+                               workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  st = check_dgamma_args(dgamma, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  const int es = elem_bytes(dtype);
+  const size_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype, flags);
+  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
+                   matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
+                   vec(gamma, N * es), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  st = bwd_rows_launch(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, flags, dx, lddx, workspace,
+                       stream);
+  if (st != RMSNORM_OK) return st;
+  return bwd_reduce_launch(workspace, M, N, dtype, flags, dgamma, stream);
+}
 
 }  // namespace
 
@@ -609,6 +773,7 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
     case RMSNORM_ERR_LAUNCH: return "kernel launch failed";
     case RMSNORM_ERR_ARGUMENT: return "invalid argument";
+    case RMSNORM_ERR_STRIDE: return "a row stride is smaller than N (or above 2^40)";
     default: return "unknown status";
   }
 }
@@ -634,91 +799,54 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
 int rmsnorm_fwd(const void* x, const void* gamma, float eps, int64_t M, int64_t N,
                 rmsnorm_dtype_t dtype, uint32_t flags, void* y, float* rstd,
                 hipStream_t stream) {
-  int st = check_common(M, N, dtype, flags);
-  if (st != RMSNORM_OK) return st;
-  if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_ERR_EPS;
-  if (M == 0) return RMSNORM_OK;
-  if (!x || !gamma || !y || !rstd) return RMSNORM_ERR_NULL_POINTER;
-  const int es = elem_bytes(dtype);
-  if (misaligned(x, es) || misaligned(gamma, es) || misaligned(y, es) || misaligned(rstd, 4))
-    return RMSNORM_ERR_ALIGNMENT;
-  const int64_t mat = M * N * es;
-  if (any_overlap({span(y, mat), span(rstd, M * 4)}, {span(x, mat), span(gamma, N * es)}))
-    return RMSNORM_ERR_OVERLAP;
-  rmsnorm_plan_t p;
-  fill_plan(M, N, dtype, RMSNORM_PASS_FWD, pointer_alignment({x, gamma, y}), &p);
-  const int off = (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0;
-  const int n = static_cast<int>(N);
-  hipError_t e;
-  switch (dtype) {
-    case RMSNORM_F32: e = fwd_by_vec<kF32>(p, x, gamma, y, rstd, M, n, eps, off, stream); break;
-    case RMSNORM_F16: e = fwd_by_vec<kF16>(p, x, gamma, y, rstd, M, n, eps, off, stream); break;
-    default: e = fwd_by_vec<kBF16>(p, x, gamma, y, rstd, M, n, eps, off, stream); break;
-  }
-  return status_of(e);
+  return fwd_impl(x, N, gamma, eps, M, N, dtype, flags, y, N, rstd, stream);
+}
+
+int rmsnorm_fwd_strided(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M,
+                        int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y, int64_t ldy,
+                        float* rstd, hipStream_t stream) {
+  return fwd_impl(x, ldx, gamma, eps, M, N, dtype, flags, y, ldy, rstd, stream);
 }
 
 int rmsnorm_bwd_rows(const void* dy, const void* x, const void* gamma, const float* rstd,
                      int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_bwd_rows_args(dy, x, gamma, rstd, M, N, dtype, flags, dx, workspace,
+  int st = check_bwd_rows_args(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, workspace,
                                workspace_bytes);
-  if (st != RMSNORM_OK || M == 0) return st;
-  rmsnorm_plan_t p;
-  fill_plan(M, N, dtype, RMSNORM_PASS_BWD_ROWS, pointer_alignment({dy, x, gamma, dx}), &p);
-  const int off = (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0;
-  const int n = static_cast<int>(N);
-  float* part = static_cast<float*>(workspace);
-  hipError_t e;
-  switch (dtype) {
-    case RMSNORM_F32: e = bwd_rows_by_vec<kF32>(p, dy, x, gamma, rstd, dx, part, M, n, off, stream); break;
-    case RMSNORM_F16: e = bwd_rows_by_vec<kF16>(p, dy, x, gamma, rstd, dx, part, M, n, off, stream); break;
-    default: e = bwd_rows_by_vec<kBF16>(p, dy, x, gamma, rstd, dx, part, M, n, off, stream); break;
-  }
-  return status_of(e);
+  if (st != RMSNORM_OK) return st;
+  return bwd_rows_launch(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, workspace, stream);
 }
 
 int rmsnorm_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
-                       rmsnorm_dtype_t dtype, uint32_t flags, float* dgamma,
+                       rmsnorm_dtype_t dtype, uint32_t flags, void* dgamma,
                        hipStream_t stream) {
   int st = check_common(M, N, dtype, flags);
   if (st != RMSNORM_OK) return st;
-  if (!dgamma) return RMSNORM_ERR_NULL_POINTER;
-  if (misaligned(dgamma, 4)) return RMSNORM_ERR_ALIGNMENT;
+  st = check_dgamma_args(dgamma, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({span(dgamma, N * 4)}, {span(workspace, static_cast<int64_t>(need))}))
+  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
+                  {vec(workspace, static_cast<int64_t>(need))}))
     return RMSNORM_ERR_OVERLAP;
-  rmsnorm_plan_t p;
-  fill_plan(M, N, dtype, RMSNORM_PASS_BWD_REDUCE, 16, &p);
-  const float* part = static_cast<const float*>(workspace);
-  const int n = static_cast<int>(N);
-  if (p.kernel == RMSNORM_KERNEL_BWD_REDUCE16)
-    return status_of(launch(bwd_reduce16_kernel, p.grid, p.block_threads, 0, stream, part,
-                            dgamma, p.partials, n));
-  return status_of(launch(bwd_reduce_kernel, p.grid, p.block_threads, 0, stream, part,
-                          dgamma, p.partials, n));
+  return bwd_reduce_launch(workspace, M, N, dtype, flags, dgamma, stream);
 }
 
 int rmsnorm_bwd(const void* dy, const void* x, const void* gamma, const float* rstd,
                 int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
-                float* dgamma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_bwd_rows_args(dy, x, gamma, rstd, M, N, dtype, flags, dx, workspace,
-                               workspace_bytes);
-  if (st != RMSNORM_OK) return st;
-  if (!dgamma) return RMSNORM_ERR_NULL_POINTER;
-  if (misaligned(dgamma, 4)) return RMSNORM_ERR_ALIGNMENT;
-  const int es = elem_bytes(dtype);
-  const int64_t mat = M * N * es;
-  const size_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype, flags);
-  if (any_overlap({span(dgamma, N * 4), span(dx, mat), span(workspace, static_cast<int64_t>(need))},
-                  {span(dy, mat), span(x, mat), span(gamma, N * es), span(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
-  st = rmsnorm_bwd_rows(dy, x, gamma, rstd, M, N, dtype, flags, dx, workspace,
-                        workspace_bytes, stream);
-  if (st != RMSNORM_OK) return st;
-  return rmsnorm_bwd_reduce(workspace, workspace_bytes, M, N, dtype, flags, dgamma, stream);
+                void* dgamma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, dgamma, workspace,
+                  workspace_bytes, stream);
+}
+
+int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                        const void* gamma, const float* rstd, int64_t M, int64_t N,
+                        rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx,
+                        void* dgamma, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return bwd_impl(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, flags, dx, lddx, dgamma,
+                  workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

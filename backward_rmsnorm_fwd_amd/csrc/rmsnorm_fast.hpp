@@ -13,14 +13,13 @@
 //        partial, so only it carries a bounds test
 //   G    = BLOCK/TPR rows processed side by side by one workgroup
 //
-// Rows are addressed through buffer resources (one descriptor per row, a
-// per-thread byte offset t*16 in a VGPR and the chunk offset c*TPR*16 as a
-// scalar offset), so the chunks of a row cost no per-chunk 64-bit addresses
-// in VGPRs.  Streaming accesses carry the cache-policy bit "nt" (no temporal
-// reuse expected).
+// Row i of a matrix starts at byte i*pitch (pitch = the row stride times the
+// element size; pitch = N*sizeof(T) for dense matrices).  Each lane adds its
+// own byte offset t*16 and the chunk offset c*TPR*16.  Streaming accesses
+// carry the cache-policy bit "nt" (no temporal reuse expected).
 //
-// The kernels are picked by the host plan when N*sizeof(T) and every pointer
-// are 16-byte aligned; rmsnorm_kernels.hpp covers all other cases.
+// The kernels are picked by the host plan when N*sizeof(T), every pitch and
+// every pointer are 16-byte aligned; rmsnorm_kernels.hpp covers the others.
 #pragma once
 
 #include "rmsnorm_kernels.hpp"
@@ -29,64 +28,17 @@ namespace rmsnorm_hip {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kPolicyNT = 2;            // cache policy: nt (non-temporal)
-
-// Buffer resource over `bytes` bytes at `base` (base must be uniform).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
-}
-
-template <bool NT>
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? kPolicyNT : 0);
-}
-
-template <bool NT>
-__device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                         uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, NT ? kPolicyNT : 0);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane i of the wavefront
-// lands at lds_wave_base + 16*i (checked on the device).
-__device__ __forceinline__ void bload16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
-                                            uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, soff, 0, 0);
-}
-
 template <typename T>
 __device__ __forceinline__ T uniform(T v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Access to one row (or one vector) of 16-byte elements at byte offsets
-// voff (per thread) + soff (uniform).  BUF selects buffer-resource addressing
-// (no per-chunk 64-bit addresses in VGPRs); otherwise plain global addresses.
-template <bool BUF>
-struct RowAccess;
-
-template <>
-struct RowAccess<true> {
-  __amdgpu_buffer_rsrc_t r;
-  __device__ __forceinline__ RowAccess(const void* base, uint32_t bytes) : r(buffer_of(base, bytes)) {}
-  template <bool NT>
-  __device__ __forceinline__ u32x4 load(uint32_t voff, uint32_t soff) const {
-    return bload16<NT>(r, voff, soff);
-  }
-  template <bool NT>
-  __device__ __forceinline__ void store(u32x4 v, uint32_t voff, uint32_t soff) const {
-    bstore16<NT>(v, r, voff, soff);
-  }
-  __device__ __forceinline__ void to_lds(void* lds_wave_base, uint32_t voff, uint32_t soff) const {
-    bload16_lds(r, lds_wave_base, voff, soff);
-  }
-};
-
-template <>
-struct RowAccess<false> {
+// voff (per thread) + soff (uniform), with plain global addresses.
+struct GRow {
   char* p;
-  __device__ __forceinline__ RowAccess(const void* base, uint32_t) : p(static_cast<char*>(const_cast<void*>(base))) {}
+  __device__ __forceinline__ explicit GRow(const void* base)
+      : p(static_cast<char*>(const_cast<void*>(base))) {}
   template <bool NT>
   __device__ __forceinline__ u32x4 load(uint32_t voff, uint32_t soff) const {
     const u32x4* a = reinterpret_cast<const u32x4*>(p + soff + voff);
@@ -178,10 +130,11 @@ __device__ __forceinline__ float group_sum(float v, float* slots, int& parity, i
 // GREG keeps the weight in registers across rows (else it is re-read from
 // cache each row); NT marks x loads and y stores as streaming.
 // ---------------------------------------------------------------------------
-template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool NT, int MINW = 1, bool BUF = false>
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool NT, int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
-    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
+    float* __restrict__ rstd, int64_t M, int N, float eps, int offset, int64_t x_pitch,
+    int64_t y_pitch) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G;
   constexpr uint32_t kChunk = TPR * 16;  // bytes per chunk sweep
@@ -195,7 +148,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
   const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
   int parity = 0;
   const float n_f = static_cast<float>(N);
-  const RowAccess<BUF> gbuf(gamma, row_bytes);
+  const GRow gbuf(gamma);
 
   PK g[GREG ? CH : 1];
   if constexpr (GREG) {
@@ -216,7 +169,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
     }
     PK xv[CH];
     if (active) {
-      const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+      const GRow xb(static_cast<const char*>(x) + row * x_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) xv[c].raw = xb.template load<NT>(voff, c * kChunk);
@@ -240,7 +193,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
     const float r = 1.0f / sqrtf(ss / n_f + eps);
     if (active) {
       if (t == 0) rstd[row] = r;
-      const RowAccess<BUF> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
+      const GRow yb(static_cast<char*>(y) + row * y_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) {
@@ -262,73 +215,6 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Forward for long rows with the row of x staged in LDS by DMA
-// (buffer_load ... lds) and read back for the sum of squares and for the
-// scale pass; one 1024-thread workgroup per row.  The register-staged
-// fwd_fast_kernel<.., WPR=16, ..> is the alternative it is measured against.
-// ---------------------------------------------------------------------------
-template <int DT, int CH, bool NT, bool BUF = false>
-__global__ __launch_bounds__(1024) void fwd_xlds_kernel(
-    const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
-    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
-  using Geo = Geometry<DT, CH, 16, 1024>;
-  constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
-  constexpr uint32_t kChunk = TPR * 16;
-  using PK = Pack<DT, VEC>;
-  extern __shared__ __align__(16) char xrow[];
-  __shared__ float slots[2 * 16];
-  const int t = threadIdx.x;
-  const int wave = uniform(t / kWave);
-  const int lane = t % kWave;
-  const uint32_t voff = t * 16;
-  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
-  int parity = 0;
-  const float n_f = static_cast<float>(N);
-  const RowAccess<BUF> gbuf(gamma, row_bytes);
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (c < CH - 1 || voff + c * kChunk < row_bytes)
-        xb.to_lds(xrow + c * kChunk + wave * kWave * 16, voff, c * kChunk);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
-        PK xc;
-        xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          const float f = xc.get(k);
-          ss = fmaf(f, f, ss);
-        }
-      }
-    }
-    ss = group_sum<16, 1>(ss, slots, parity, 0, wave, lane);
-    const float r = 1.0f / sqrtf(ss / n_f + eps);
-    if (t == 0) rstd[row] = r;
-    const RowAccess<BUF> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (c < CH - 1 || voff + c * kChunk < row_bytes) {
-        PK xc, gv;
-        xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
-        gv.raw = gbuf.template load<false>(voff, c * kChunk);
-        float o[VEC];
-#pragma unroll
-        for (int k = 0; k < VEC; ++k)
-          o[k] = (xc.get(k) * r) * weight_of(gv.get(k), offset);
-        PK out;
-        out.set(o);
-        yb.template store<NT>(out.raw, voff, c * kChunk);
-      }
-      chunk_fence();
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Backward stage 1.  Workgroup w owns rows [w*M/P, (w+1)*M/P); its G row
 // groups take them in turn (row = r0 + it*G + g), all groups running the same
 // number of iterations.  Per row: dot = sum(dy*g*x) over the row, then one
@@ -340,20 +226,18 @@ __global__ __launch_bounds__(1024) void fwd_xlds_kernel(
 // in flight) and is read back for both sweeps.
 // GREG: the weight lives in registers; otherwise it is re-read from cache.
 // ---------------------------------------------------------------------------
-template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool XLDS, bool NT, int MINW = 1,
-          bool BUF = false, bool DLDS = false>
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool XLDS, bool NT, int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
-    int64_t P) {
+    int64_t P, int64_t dy_pitch, int64_t x_pitch, int64_t dx_pitch) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G, SWEEP = Geo::SWEEP;
   constexpr uint32_t kChunk = TPR * 16;
   using PK = Pack<DT, VEC>;
-  static_assert(XLDS || !DLDS, "dy staging sits behind the staged rows of x");
-  // XLDS: [G][N] elements of x (then, with DLDS, [G][N] elements of dy); after
-  // the row loop: [G][SWEEP] float32 for the combine (G > 1).
+  // XLDS: [G][N] elements of x; after the row loop: [G][SWEEP] float32 for
+  // the combine (G > 1).
   extern __shared__ __align__(16) char dyn[];
   __shared__ float slots[WPR > 1 ? 2 * G * WPR : 1];
   const int t = threadIdx.x % TPR;
@@ -369,8 +253,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
   const int64_t iters = (r1 - r0 + G - 1) / G;
   const float n_f = static_cast<float>(N);
   char* xrow = dyn + static_cast<int64_t>(group) * row_bytes;
-  char* dyrow = dyn + static_cast<int64_t>(G + group) * row_bytes;  // DLDS only
-  const RowAccess<BUF> gbuf(gamma, row_bytes);
+  const GRow gbuf(gamma);
 
   PK g[GREG ? CH : 1];
   if constexpr (GREG) {
@@ -397,13 +280,12 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
     float r = 0.f;
     if (active) {
       r = rstd[row];
-      const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
-      const RowAccess<BUF> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
+      const GRow xb(static_cast<const char*>(x) + row * x_pitch);
+      const GRow db(static_cast<const char*>(dy) + row * dy_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) {
-          if constexpr (DLDS) db.to_lds(dyrow + c * kChunk + wave_in_row * kWave * 16, voff, c * kChunk);
-          else dv[c].raw = db.template load<NT>(voff, c * kChunk);
+          dv[c].raw = db.template load<NT>(voff, c * kChunk);
           if constexpr (XLDS) xb.to_lds(xrow + c * kChunk + wave_in_row * kWave * 16, voff, c * kChunk);
           else xv[c].raw = xb.template load<NT>(voff, c * kChunk);
         } else {
@@ -411,14 +293,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
           if constexpr (!XLDS) xv[c].zero();
         }
       }
-      if constexpr (XLDS || DLDS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if constexpr (DLDS) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          if (c < CH - 1 || voff + c * kChunk < row_bytes)
-            dv[c].raw = *reinterpret_cast<const u32x4*>(dyrow + c * kChunk + voff);
-        }
-      }
+      if constexpr (XLDS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -452,7 +327,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
     }
     const float r3c = ((r * r) * r) * (dot / n_f);
     if (active) {
-      const RowAccess<BUF> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
+      const GRow ob(static_cast<char*>(dx) + row * dx_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) {
@@ -618,7 +493,8 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) {
 template <int DT, int CH, int WPR, int BLOCK, bool NT, bool XL, bool CYC, int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
-    float* __restrict__ rstd, int64_t M, int N, float eps, int offset) {
+    float* __restrict__ rstd, int64_t M, int N, float eps, int offset, int64_t x_pitch,
+    int64_t y_pitch) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G;
   constexpr uint32_t kChunk = TPR * 16;
@@ -638,7 +514,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
   char* const xstage = dyn + static_cast<int64_t>(group) * row_bytes;
   const int64_t stage_stride = static_cast<int64_t>(G) * row_bytes;
   const uint32_t dma_off = wave_in_row * kWave * 16;
-  const RowAccess<false> gbuf(gamma, row_bytes);
+  const GRow gbuf(gamma);
 
   PK g[CH];
 #pragma unroll
@@ -648,7 +524,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
   }
 
   auto issue = [&](int64_t row, int64_t it, PK(&xv)[CH]) __attribute__((always_inline)) {
-    const RowAccess<false> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
+    const GRow xb(static_cast<const char*>(x) + row * x_pitch);
     char* xs = xstage + (it & 1) * stage_stride;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -710,7 +586,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
     const float r = 1.0f / sqrtf(ss / n_f + eps);
     if (active) {
       if (t == 0) rstd[row] = r;
-      const RowAccess<false> yb(static_cast<char*>(y) + row * row_bytes, row_bytes);
+      const GRow yb(static_cast<char*>(y) + row * y_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) {
@@ -766,7 +642,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
-    int64_t P) {
+    int64_t P, int64_t dy_pitch, int64_t x_pitch, int64_t dx_pitch) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G, SWEEP = Geo::SWEEP;
   constexpr uint32_t kChunk = TPR * 16;
@@ -791,7 +667,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
   const int64_t stage_stride = static_cast<int64_t>(kSets) * G * row_bytes;
   const int64_t dy_off = static_cast<int64_t>(G) * row_bytes;
   const uint32_t dma_off = wave_in_row * kWave * 16;
-  const RowAccess<false> gbuf(gamma, row_bytes);
+  const GRow gbuf(gamma);
 
   PK g[CH];
 #pragma unroll
@@ -807,8 +683,8 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
 
   auto issue = [&](int64_t row, int64_t it, PK(&dv)[CH]) __attribute__((always_inline)) {
     char* xs = xstage + (it & 1) * stage_stride;
-    const RowAccess<false> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
-    const RowAccess<false> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
+    const GRow xb(static_cast<const char*>(x) + row * x_pitch);
+    const GRow db(static_cast<const char*>(dy) + row * dy_pitch);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (c < CH - 1 || voff + c * kChunk < row_bytes) {
@@ -880,7 +756,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
     }
     const float r3c = ((r * r) * r) * (dot / n_f);
     if (active) {
-      const RowAccess<false> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
+      const GRow ob(static_cast<char*>(dx) + row * dx_pitch);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) {
@@ -996,7 +872,7 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
-    int64_t P) {
+    int64_t P, int64_t dy_pitch, int64_t x_pitch, int64_t dx_pitch) {
   constexpr int WPR = 8, BLOCK = 512;
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
@@ -1028,8 +904,8 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
   };
   auto issue_chunk = [&](int64_t row, int c) __attribute__((always_inline)) {
     if (in_row(c)) {
-      const URow xb(static_cast<const char*>(x) + row * row_bytes);
-      const URow db(static_cast<const char*>(dy) + row * row_bytes);
+      const URow xb(static_cast<const char*>(x) + row * x_pitch);
+      const URow db(static_cast<const char*>(dy) + row * dy_pitch);
       xb.to_lds(dyn + c * kChunk + dma_off, voff, c * kChunk);  // DMA first,
       dv[c].raw = db.template load<NT>(voff, c * kChunk);        // then dy
     } else {
@@ -1075,7 +951,7 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
     const float r3c = ((r * r) * r) * (dot / n_f);
 
     // pass B
-    const URow ob(static_cast<char*>(dx) + row * row_bytes);
+    const URow ob(static_cast<char*>(dx) + row * dx_pitch);
     gc = load_g(0);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -1115,186 +991,11 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Backward stage 1 for long rows: one workgroup (64*WPR threads) per row.  At
-// N = 65536 a row of x and dy plus the dgamma accumulators would need more
-// than the CU's register file, so only the accumulators persist across the
-// row reduction:
-//   pass A  streams the row once: dot += dy*g*x and acc += (dy*x)*r
-//           (r comes from the forward, so the dgamma term needs no reduction)
-//   pass B  re-reads x, dy and g and writes dx = r*u - x*(r^3*dot/N).
-// Both passes are software-pipelined over batches of D chunks: the loads of
-// batch b+1 are in flight while batch b is computed, and scheduling fences
-// keep the compiler from hoisting more than that.
-// XS: x reaches LDS by DMA in pass A and pass B reads it there (else pass B
-//     re-reads x through the cache hierarchy).
-// GS: gamma is copied to LDS once per workgroup (else read through cache).
-// XS and GS together need 2*N*sizeof(T) bytes of LDS.
-// ---------------------------------------------------------------------------
-template <int DT, int CH, bool XS, bool GS, bool NT, int D = 2, int WPR = 16, bool BUF = false>
-__global__ __launch_bounds__(64 * WPR) void bwd_long_kernel(
-    const void* __restrict__ dy, const void* __restrict__ x,
-    const void* __restrict__ gamma, const float* __restrict__ rstd,
-    void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
-    int64_t P) {
-  using Geo = Geometry<DT, CH, WPR, 64 * WPR>;
-  constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
-  constexpr uint32_t kChunk = TPR * 16;
-  constexpr int NB = (CH + D - 1) / D;  // batches per pass
-  using PK = Pack<DT, VEC>;
-  extern __shared__ __align__(16) char dyn[];
-  __shared__ float slots[2 * WPR];
-  const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
-  char* xrow = dyn;                                // [N] when XS
-  char* grow = dyn + (XS ? row_bytes : 0);         // [N] when GS
-  const int t = threadIdx.x;
-  const int wave = uniform(t / kWave);
-  const int lane = t % kWave;
-  const uint32_t voff = t * 16;
-  int parity = 0;
-  const int64_t w = blockIdx.x;
-  const int64_t r0 = block_row_begin(w, M, P);
-  const int64_t r1 = block_row_begin(w + 1, M, P);
-  const float n_f = static_cast<float>(N);
-  const RowAccess<BUF> gbuf(gamma, row_bytes);
-
-  if constexpr (GS) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (c < CH - 1 || voff + c * kChunk < row_bytes)
-        *reinterpret_cast<u32x4*>(grow + c * kChunk + voff) = gbuf.template load<false>(voff, c * kChunk);
-    // each thread later reads back only the bytes it wrote: no barrier
-  }
-
-  float acc[CH][VEC];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
-
-  PK bx[2][D], bd[2][D], bg[2][D];  // register buffers of two batches
-
-  for (int64_t row = r0; row < r1; ++row) {
-    const float r = rstd[row];
-    const RowAccess<BUF> xb(static_cast<const char*>(x) + row * row_bytes, row_bytes);
-    const RowAccess<BUF> db(static_cast<const char*>(dy) + row * row_bytes, row_bytes);
-    const RowAccess<BUF> ob(static_cast<char*>(dx) + row * row_bytes, row_bytes);
-
-    // Loads of batch b into buffer b&1: cached in pass A (read again in
-    // pass B), streaming in pass B (last use).  `vo` is the thread's byte
-    // offset routed through `after`, a value the previous batch computed, so
-    // the loads cannot be hoisted ahead of that work (which would make every
-    // batch's registers live at once).
-    uint32_t vo = voff;
-    auto load_batch = [&](int b, bool last_use, float after) {
-      asm volatile("" : "+v"(vo) : "v"(after));
-#pragma unroll
-      for (int i = 0; i < D; ++i) {
-        const int c = b * D + i;
-        if (c < CH) {
-          if (c < CH - 1 || voff + c * kChunk < row_bytes) {
-            if constexpr (!XS) {
-              bx[b & 1][i].raw = last_use ? xb.template load<NT>(vo, c * kChunk)
-                                          : xb.template load<false>(vo, c * kChunk);
-            }
-            bd[b & 1][i].raw = last_use ? db.template load<NT>(vo, c * kChunk)
-                                        : db.template load<false>(vo, c * kChunk);
-            if constexpr (!GS) bg[b & 1][i].raw = gbuf.template load<false>(vo, c * kChunk);
-          } else {
-            if constexpr (!XS) bx[b & 1][i].zero();
-            bd[b & 1][i].zero();
-            if constexpr (!GS) bg[b & 1][i].zero();
-          }
-        }
-      }
-    };
-
-    // ---- pass A ----
-    if constexpr (XS) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (c < CH - 1 || voff + c * kChunk < row_bytes)
-          xb.to_lds(xrow + c * kChunk + wave * kWave * 16, voff, c * kChunk);
-    }
-    float dot = 0.f;
-    load_batch(0, false, r);
-    if constexpr (XS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b + 1 < NB) load_batch(b + 1, false, dot);
-#pragma unroll
-      for (int i = 0; i < D; ++i) {
-        const int c = b * D + i;
-        if (c < CH && (c < CH - 1 || voff + c * kChunk < row_bytes)) {
-          PK xc, gv;
-          if constexpr (XS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
-          else xc = bx[b & 1][i];
-          if constexpr (GS) gv.raw = *reinterpret_cast<const u32x4*>(grow + c * kChunk + voff);
-          else gv = bg[b & 1][i];
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) {
-            const float xf = xc.get(k);
-            const float dyf = bd[b & 1][i].get(k);
-            dot = fmaf(dyf * weight_of(gv.get(k), offset), xf, dot);
-            acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
-          }
-        }
-      }
-      chunk_fence();
-    }
-    dot = group_sum<WPR, 1>(dot, slots, parity, 0, wave, lane);
-    const float r3c = ((r * r) * r) * (dot / n_f);
-
-    // ---- pass B ----
-    float last = r3c;
-    load_batch(0, true, last);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b + 1 < NB) load_batch(b + 1, true, last);
-#pragma unroll
-      for (int i = 0; i < D; ++i) {
-        const int c = b * D + i;
-        if (c < CH && (c < CH - 1 || voff + c * kChunk < row_bytes)) {
-          PK xc, gv;
-          if constexpr (XS) xc.raw = *reinterpret_cast<const u32x4*>(xrow + c * kChunk + voff);
-          else xc = bx[b & 1][i];
-          if constexpr (GS) gv.raw = *reinterpret_cast<const u32x4*>(grow + c * kChunk + voff);
-          else gv = bg[b & 1][i];
-          float o[VEC];
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) {
-            const float u = bd[b & 1][i].get(k) * weight_of(gv.get(k), offset);
-            o[k] = fmaf(-xc.get(k), r3c, r * u);
-          }
-          PK out;
-          out.set(o);
-          ob.template store<NT>(out.raw, voff, c * kChunk);
-          last = o[0];
-        }
-      }
-      chunk_fence();
-    }
-  }
-
-  float* dst = part + w * static_cast<int64_t>(N);
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int e = (c * TPR + t) * VEC;
-    if (c < CH - 1 || e < N) store_f32<VEC>(dst + e, acc[c]);
-  }
-}
-
-template <int DT, bool XS, bool GS>
-constexpr int64_t bwd_long_lds_bytes(int N) {
-  return static_cast<int64_t>((XS ? 1 : 0) + (GS ? 1 : 0)) * N * ElemBytes<DT>::value;
-}
-
 // LDS bytes the backward kernel needs for a given N.
-template <int DT, int CH, int WPR, int BLOCK, bool XLDS, bool DLDS = false>
+template <int DT, int CH, int WPR, int BLOCK, bool XLDS>
 constexpr int64_t bwd_fast_lds_bytes(int N) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
-  const int64_t stage = static_cast<int64_t>((XLDS ? 1 : 0) + (DLDS ? 1 : 0)) * Geo::G * N *
-                        ElemBytes<DT>::value;
+  const int64_t stage = static_cast<int64_t>(XLDS ? 1 : 0) * Geo::G * N * ElemBytes<DT>::value;
   const int64_t comb = Geo::G > 1 ? static_cast<int64_t>(Geo::G) * Geo::SWEEP * 4 : 0;
   return stage > comb ? stage : comb;
 }
@@ -1305,8 +1006,9 @@ constexpr int64_t bwd_fast_lds_bytes(int N) {
 // float64, then 16 threads add the 64 slice sums in slice order.  Needs
 // N % 4 == 0 (16-byte partial rows).
 // ---------------------------------------------------------------------------
+template <int OUT>
 static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce16_kernel(
-    const float* __restrict__ part, float* __restrict__ dgamma, int64_t P, int N) {
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
   constexpr int kQuads = 4, kSlices = 64;
   __shared__ double sums[kSlices][kQuads * 4 + 1];
   const int q = threadIdx.x % kQuads;
@@ -1332,7 +1034,7 @@ static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce
     if (c < N) {
       double tot = 0.0;
       for (int i = 0; i < kSlices; ++i) tot += sums[i][threadIdx.x];
-      dgamma[c] = static_cast<float>(tot);
+      store_dgamma<OUT>(dgamma, c, tot);
     }
   }
 }

@@ -12,7 +12,7 @@ hipError_t fast_fwd_launch<kF32>(int wpr, int ch, int block, int greg, int64_t g
 #define RMSNORM_X(W, C, B, GR)                                                              \
   if (wpr == W && ch == C && block == B && greg == GR)                                      \
     return launch(fwd_fast_kernel<kF32, C, W, B, GR != 0, true>, grid, B, 0, s, a.x, a.gamma, \
-                  a.y, a.rstd, a.M, a.N, a.eps, a.offset);
+                  a.y, a.rstd, a.M, a.N, a.eps, a.offset, a.x_pitch, a.y_pitch);
   RMSNORM_FWD_FAST_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
@@ -25,7 +25,7 @@ hipError_t fast_bwd_launch<kF32>(int wpr, int ch, int block, int greg, int xlds,
   if (wpr == W && ch == C && block == B && greg == GR && xlds == XL)                        \
     return launch(bwd_fast_kernel<kF32, C, W, B, GR != 0, XL != 0, true>, a.P, B,             \
                   static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
-                  a.M, a.N, a.offset, a.P);
+                  a.M, a.N, a.offset, a.P, a.dy_pitch, a.x_pitch, a.dx_pitch);
   RMSNORM_BWD_FAST_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
@@ -38,7 +38,7 @@ hipError_t pipe_fwd_launch<kF32>(int wpr, int ch, int block, int xl, int64_t gri
   if (wpr == W && ch == C && block == B && xl == XL)                                        \
     return launch(fwd_pipe_kernel<kF32, C, W, B, true, XL != 0, true>, grid, B,              \
                   static_cast<size_t>(lds), s, a.x, a.gamma, a.y, a.rstd, a.M, a.N, a.eps,  \
-                  a.offset);
+                  a.offset, a.x_pitch, a.y_pitch);
   RMSNORM_FWD_PIPE_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
@@ -51,7 +51,7 @@ hipError_t pipe_bwd_launch<kF32>(int wpr, int ch, int block, int dlds, int64_t l
   if (wpr == W && ch == C && block == B && dlds == DL)                                      \
     return launch(bwd_pipe_kernel<kF32, C, W, B, true, DL != 0, true>, a.P, B,               \
                   static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
-                  a.M, a.N, a.offset, a.P);
+                  a.M, a.N, a.offset, a.P, a.dy_pitch, a.x_pitch, a.dx_pitch);
   RMSNORM_BWD_PIPE_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
@@ -62,7 +62,8 @@ hipError_t long_bwd_launch<kF32>(int ch, int64_t lds, const FastBwdArgs& a, hipS
 #define RMSNORM_X(C)                                                                        \
   if (ch == C)                                                                              \
     return launch(bwd_longrow_kernel<kF32, C, true>, a.P, 512, static_cast<size_t>(lds), s,   \
-                  a.dy, a.x, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, a.P);
+                  a.dy, a.x, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, a.P,        \
+                  a.dy_pitch, a.x_pitch, a.dx_pitch);
   RMSNORM_BWD_LONG_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;

@@ -205,7 +205,7 @@ template <int DT, int VEC, int MAXC>
 __global__ __launch_bounds__(256) void fwd_wave_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma,
     void* __restrict__ y, float* __restrict__ rstd, int64_t M, int N,
-    int chunks, float eps, int offset) {
+    int chunks, float eps, int offset, int64_t ldx, int64_t ldy) {
   using P = Pack<DT, VEC>;
   const int lane = threadIdx.x & (kWave - 1);
   const int group = threadIdx.x / kWave;
@@ -222,14 +222,13 @@ __global__ __launch_bounds__(256) void fwd_wave_kernel(
 
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * groups + group; row < M;
        row += static_cast<int64_t>(gridDim.x) * groups) {
-    const int64_t base = row * N;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) g[c].opaque();
     P xv[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int e = (c * kWave + lane) * VEC;
-      if (c < chunks && e < N) xv[c].load(x, base + e);
+      if (c < chunks && e < N) xv[c].load(x, row * ldx + e);
       else xv[c].zero();
     }
     float ss = 0.f;
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(256) void fwd_wave_kernel(
           o[k] = (xv[c].get(k) * r) * weight_of(g[c].get(k), offset);
         P out;
         out.set(o);
-        out.store(y, base + e);
+        out.store(y, row * ldy + e);
       }
     }
   }
@@ -272,7 +271,7 @@ template <int DT, int VEC, int MAXC>
 __global__ __launch_bounds__(1024) void fwd_block_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma,
     void* __restrict__ y, float* __restrict__ rstd, int64_t M, int N,
-    int chunks, float eps, int offset) {
+    int chunks, float eps, int offset, int64_t ldx, int64_t ldy) {
   using P = Pack<DT, VEC>;
   __shared__ float slots[2 * kMaxWavesPerBlock];
   const int tpr = blockDim.x;
@@ -284,12 +283,11 @@ __global__ __launch_bounds__(1024) void fwd_block_kernel(
   const float n_f = static_cast<float>(N);
 
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const int64_t base = row * N;
     P xv[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int e = (c * tpr + t) * VEC;
-      if (c < chunks && e < N) xv[c].load(x, base + e);
+      if (c < chunks && e < N) xv[c].load(x, row * ldx + e);
       else xv[c].zero();
     }
     float ss = 0.f;
@@ -320,7 +318,7 @@ __global__ __launch_bounds__(1024) void fwd_block_kernel(
           o[k] = (xv[c].get(k) * r) * weight_of(gv.get(k), offset);
         P out;
         out.set(o);
-        out.store(y, base + e);
+        out.store(y, row * ldy + e);
       }
     }
   }
@@ -376,7 +374,7 @@ __global__ __launch_bounds__(512) void bwd_wave_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N,
-    int chunks, int offset, int64_t P) {
+    int chunks, int offset, int64_t P, int64_t lddy, int64_t ldx, int64_t lddx) {
   using PK = Pack<DT, VEC>;
   extern __shared__ float comb[];  // [N] running sum of the groups' partials
   const int lane = threadIdx.x & (kWave - 1);
@@ -401,7 +399,6 @@ __global__ __launch_bounds__(512) void bwd_wave_kernel(
     for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
 
   for (int64_t row = r0 + group; row < r1; row += groups) {
-    const int64_t base = row * N;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) g[c].opaque();
     PK xv[MAXC], dv[MAXC];
@@ -409,8 +406,8 @@ __global__ __launch_bounds__(512) void bwd_wave_kernel(
     for (int c = 0; c < MAXC; ++c) {
       const int e = (c * kWave + lane) * VEC;
       if (c < chunks && e < N) {
-        xv[c].load(x, base + e);
-        dv[c].load(dy, base + e);
+        xv[c].load(x, row * ldx + e);
+        dv[c].load(dy, row * lddy + e);
       } else {
         xv[c].zero();
         dv[c].zero();
@@ -451,7 +448,7 @@ __global__ __launch_bounds__(512) void bwd_wave_kernel(
         }
         PK out;
         out.set(o);
-        out.store(dx, base + e);
+        out.store(dx, row * lddx + e);
       }
     }
   }
@@ -494,7 +491,7 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N,
-    int chunks, int offset, int64_t P) {
+    int chunks, int offset, int64_t P, int64_t lddy, int64_t ldx, int64_t lddx) {
   using PK = Pack<DT, VEC>;
   extern __shared__ __align__(16) char xrow[];  // [N] elements of x when XLDS
   __shared__ float slots[2 * kMaxWavesPerBlock];
@@ -516,7 +513,6 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
     for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
 
   for (int64_t row = r0; row < r1; ++row) {
-    const int64_t base = row * N;
     PK dv[MAXC];
     PK xv[XLDS ? 1 : MAXC];
     const float r = rstd[row];
@@ -525,8 +521,8 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
       const int e = (c * tpr + t) * VEC;
       PK& xc = xv[XLDS ? 0 : c];
       if (c < chunks && e < N) {
-        xc.load(x, base + e);
-        dv[c].load(dy, base + e);
+        xc.load(x, row * ldx + e);
+        dv[c].load(dy, row * lddy + e);
         if constexpr (XLDS) xc.store(xrow, e);
       } else {
         xc.zero();
@@ -578,7 +574,7 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
         }
         PK out;
         out.set(o);
-        out.store(dx, base + e);
+        out.store(dx, row * lddx + e);
       }
     }
   }
@@ -596,8 +592,30 @@ __global__ __launch_bounds__(1024) void bwd_block_kernel(
 // A workgroup covers 64 columns; its S = blockDim.x/64 slices take partial
 // rows p = s, s+S, ...; the slices are then added in slice order.
 // ---------------------------------------------------------------------------
+// dgamma output type of stage 2: float32, or the input dtype (kF16/kBF16/kF32)
+// rounded to nearest even from the float32 value.
+constexpr int kOutF32 = -1;
+
+template <int OUT>
+__device__ __forceinline__ void store_dgamma(void* dgamma, int64_t j, double tot) {
+  // The float32 value is materialised first: the compiler may not fold the
+  // two conversions into one rounding from float64 (which differs when the
+  // float32 value falls exactly halfway between two values of T).
+  float f32 = static_cast<float>(tot);
+  asm volatile("" : "+v"(f32));
+  const float f[1] = {f32};
+  if constexpr (OUT == kOutF32) {
+    static_cast<float*>(dgamma)[j] = f[0];
+  } else {
+    Pack<OUT, 1> v;
+    v.set(f);
+    v.store(dgamma, j);
+  }
+}
+
+template <int OUT>
 static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduce_kernel(
-    const float* __restrict__ part, float* __restrict__ dgamma, int64_t P, int N) {
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
   __shared__ double sums[kMaxWavesPerBlock][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int s = threadIdx.x / kWave;
@@ -613,7 +631,7 @@ static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduc
   if (s == 0 && col < N) {
     double tot = 0.0;
     for (int i = 0; i < S; ++i) tot += sums[i][lane];
-    dgamma[col] = static_cast<float>(tot);
+    store_dgamma<OUT>(dgamma, col, tot);
   }
 }
 

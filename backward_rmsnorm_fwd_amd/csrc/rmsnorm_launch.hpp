@@ -40,6 +40,8 @@ struct FastFwdArgs {
   int N;
   float eps;
   int offset;
+  int64_t x_pitch;  // bytes between row starts
+  int64_t y_pitch;
 };
 
 struct FastBwdArgs {
@@ -53,6 +55,9 @@ struct FastBwdArgs {
   int N;
   int offset;
   int64_t P;
+  int64_t dy_pitch;  // bytes between row starts
+  int64_t x_pitch;
+  int64_t dx_pitch;
 };
 
 // Launch a listed full-width configuration (rmsnorm_fast_table.hpp) for

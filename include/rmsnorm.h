@@ -27,10 +27,11 @@
  *
  * Conventions shared by every entry point:
  *  - x, gamma, dy, y and dx hold elements of one dtype T (rmsnorm_dtype_t);
- *    rstd and dgamma are float32.
- *  - Matrices are row-major and dense: row i starts at element i*N (the row
- *    stride equals N).  Any leading dimensions are flattened into M by the
- *    caller.
+ *    rstd is float32, dgamma float32 unless RMSNORM_FLAG_DGAMMA_IN_DTYPE
+ *    asks for T (the page's reduce_gamma_gradient returns gamma's dtype).
+ *  - Matrices are row-major: row i starts at element i*N (dense), or at
+ *    element i*ld for the *_strided entry points, ld >= N given per matrix.
+ *    Any leading dimensions are flattened into M by the caller.
  *  - All pointers are device pointers on the calling thread's current HIP
  *    device; the stream belongs to that device (0 = the null stream).
  *  - The caller owns and allocates every buffer.  The library allocates
@@ -69,6 +70,9 @@ typedef enum {
 
 /* flags */
 #define RMSNORM_FLAG_OFFSET 1u /* apply the weight as (1 + w) */
+/* Write dgamma in the input dtype T (rounded to nearest even from the
+ * float32 value of the sum), as the weight's own dtype, instead of float32. */
+#define RMSNORM_FLAG_DGAMMA_IN_DTYPE 2u
 
 #define RMSNORM_MAX_N 65536
 #define RMSNORM_MAX_M (((int64_t)1) << 40)
@@ -85,6 +89,7 @@ typedef enum {
 #define RMSNORM_ERR_OVERLAP (-8)
 #define RMSNORM_ERR_LAUNCH (-9)
 #define RMSNORM_ERR_ARGUMENT (-10)
+#define RMSNORM_ERR_STRIDE (-11) /* a row stride below N (or above 2^40) */
 
 /*
  * Forward: y = x * r * g per row, and rstd[i] = r_i (float32) kept for the
@@ -119,7 +124,8 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
  *   gamma  [N] T, read (gamma, or w in offset mode)
  *   rstd   [M] float32, read (as written by rmsnorm_fwd for this x and eps)
  *   dx     [M, N] T, written
- *   dgamma [N] float32, written (sum over the M rows; zeros when M = 0)
+ *   dgamma [N] float32, written (sum over the M rows; zeros when M = 0); with
+ *          RMSNORM_FLAG_DGAMMA_IN_DTYPE [N] T instead
  *   workspace, workspace_bytes: device scratch of at least
  *          rmsnorm_bwd_workspace_bytes(M, N, dtype, flags) bytes, 16-byte
  *          aligned, owned by the caller; its contents on entry do not matter
@@ -130,7 +136,7 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
  */
 int rmsnorm_bwd(const void* dy, const void* x, const void* gamma,
                 const float* rstd, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
-                uint32_t flags, void* dx, float* dgamma, void* workspace,
+                uint32_t flags, void* dx, void* dgamma, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -149,13 +155,38 @@ int rmsnorm_bwd_rows(const void* dy, const void* x, const void* gamma,
 
 /*
  * Backward stage 2 alone: dgamma[j] = sum over p = 0..P-1 of partial[p, j],
- * added in float64 in a fixed order and rounded once to float32.  The
+ * added in float64 in a fixed order and rounded once to float32 (then to T
+ * with RMSNORM_FLAG_DGAMMA_IN_DTYPE).  The
  * workspace must hold what rmsnorm_bwd_rows wrote for the same
  * (M, N, dtype, flags).
  */
 int rmsnorm_bwd_reduce(const void* workspace, size_t workspace_bytes,
                        int64_t M, int64_t N, rmsnorm_dtype_t dtype,
-                       uint32_t flags, float* dgamma, hipStream_t stream);
+                       uint32_t flags, void* dgamma, hipStream_t stream);
+
+/*
+ * Strided variants (the page's section "Adapting the kernel and moving to
+ * production": other layouts need addressing through strides, and tests).
+ * Identical to rmsnorm_fwd / rmsnorm_bwd except that row i of x, y, dy and dx
+ * starts at element i*ldx, i*ldy, i*lddy, i*lddx of its matrix (each ld >= N;
+ * elements between the end of one row and the start of the next are neither
+ * read nor written).  The contiguous entry points are these with ld = N.
+ * An output may share a buffer with an input when their rows interleave
+ * without a common byte (same ld, column ranges disjoint); matrices with
+ * different strides must have disjoint extents.
+ * Errors: as rmsnorm_fwd / rmsnorm_bwd, plus STRIDE.
+ */
+int rmsnorm_fwd_strided(const void* x, int64_t ldx, const void* gamma, float eps,
+                        int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                        uint32_t flags, void* y, int64_t ldy, float* rstd,
+                        hipStream_t stream);
+
+int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x,
+                        int64_t ldx, const void* gamma, const float* rstd,
+                        int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                        uint32_t flags, void* dx, int64_t lddx, void* dgamma,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* rmsnorm_status_string(int status);

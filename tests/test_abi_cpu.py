@@ -22,6 +22,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(rn.library_path()),
                                 reason="librmsnorm.so not built")
 
 OK, ENULL, EDTYPE, ESHAPE, EEPS, EFLAGS, EWS, EALIGN, EOVL = 0, -1, -2, -3, -4, -5, -6, -7, -8
+ESTRIDE = -11
 A = 0x10000000  # fake, 16-byte aligned "device" addresses; never dereferenced
 
 
@@ -59,7 +60,7 @@ def fwd_call(x=A, g=A + (1 << 24), eps=1e-6, M=4, N=256, dtype=2, flags=0,
 
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": 3}, EDTYPE), ({"dtype": -1}, EDTYPE),
-    ({"flags": 2}, EFLAGS),
+    ({"flags": 4}, EFLAGS), ({"flags": 6}, EFLAGS),
     ({"N": 0}, ESHAPE), ({"N": 65537}, ESHAPE), ({"M": -1}, ESHAPE),
     ({"eps": 0.0}, EEPS), ({"eps": -1e-6}, EEPS), ({"eps": float("nan")}, EEPS),
     ({"eps": float("inf")}, EEPS),
@@ -116,6 +117,65 @@ def test_bwd_stage_entry_points_reject():
     assert L.rmsnorm_bwd_reduce(None, ws, 4, 256, 2, 0, A + (5 << 24), None) == EWS
     assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 0, A + 8, None) == EOVL
     assert L.rmsnorm_bwd_reduce(A, ws, 4, 0, 2, 0, A + (5 << 24), None) == ESHAPE
+
+
+def test_dgamma_in_dtype_flag():
+    """Flag 2 asks for dgamma in the input dtype: accepted by every entry
+    point's argument check, same workspace, element-size alignment and span
+    for dgamma; unknown bits stay rejected."""
+    L = lib()
+    ws = L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 0)
+    assert L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 2) == ws
+    assert L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 3) == ws
+    assert L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 4) == 0
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 4, A + (5 << 24), None) == EFLAGS
+    # a 2-byte-aligned dgamma is fine for bf16 output, not for float32 output
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 0, A + (5 << 24) + 2, None) == EALIGN
+    assert L.rmsnorm_bwd_reduce(A, ws, 4, 256, 2, 2, A + (5 << 24) + 1, None) == EALIGN
+    # the bf16 dgamma span is N*2 = 512 bytes: starting 2 bytes in, it
+    # reaches 2 bytes into a workspace placed 512 bytes after its base
+    assert L.rmsnorm_bwd_reduce(A + 512, ws, 4, 256, 2, 2, A + 2, None) == EOVL
+
+
+def fwd_strided_call(x=A, ldx=256, g=A + (1 << 24), eps=1e-6, M=4, N=256, dtype=2, flags=0,
+                     y=A + (2 << 24), ldy=256, r=A + (3 << 24)):
+    return lib().rmsnorm_fwd_strided(x, ldx, g, eps, M, N, dtype, flags, y, ldy, r, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"ldx": 255}, ESTRIDE), ({"ldy": 0}, ESTRIDE), ({"ldx": -256}, ESTRIDE),
+    ({"ldx": (1 << 40) + 1}, ESTRIDE), ({"flags": 4}, EFLAGS), ({"y": None}, ENULL),
+    # y starts half a row into x's rows at the same stride: they share bytes
+    ({"ldx": 512, "ldy": 512, "y": A + 256}, EOVL),
+    # y one element before the end of x's first row, at x's stride
+    ({"ldx": 512, "ldy": 512, "y": A + 510}, EOVL),
+    # different strides with overlapping extents count as overlapping
+    ({"ldx": 512, "ldy": 768, "y": A + 512}, EOVL),
+    # the weight inside the gaps of strided x is still an input: y may not hit it
+    ({"ldx": 512, "ldy": 256, "g": A + 512, "y": A + 512 + 128}, EOVL),
+])
+def test_fwd_strided_rejects(kw, code):
+    assert fwd_strided_call(**kw) == code
+
+
+def test_bwd_strided_rejects():
+    L = lib()
+    ws = L.rmsnorm_bwd_workspace_bytes(4, 256, 2, 0)
+    args = dict(dy=A, lddy=256, x=A + (1 << 24), ldx=256, g=A + (2 << 24), r=A + (3 << 24),
+                dx=A + (4 << 24), lddx=256, dg=A + (5 << 24), ws=A + (6 << 24))
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.rmsnorm_bwd_strided(a["dy"], a["lddy"], a["x"], a["ldx"], a["g"], a["r"], 4,
+                                     256, 2, 0, a["dx"], a["lddx"], a["dg"], a["ws"], ws, None)
+    assert call(lddy=100) == ESTRIDE and call(ldx=255) == ESTRIDE and call(lddx=1) == ESTRIDE
+    # dx interleaved half a row into dy's rows (same stride 512): overlap
+    assert call(lddy=512, lddx=512, dx=A + 256) == EOVL
+    assert call(dg=None) == ENULL
+
+
+def test_stride_status_string():
+    assert "stride" in rn.rmsnorm_status_string(ESTRIDE)
 
 
 def test_workspace_bytes():

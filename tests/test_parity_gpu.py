@@ -134,6 +134,87 @@ def test_stage_entry_points_match_combined(cuda):
     assert torch.equal(dx, dx2) and torch.equal(dg, dg2)
 
 
+@pytest.mark.parametrize("name,M,N", [("c2", 1500, 4096), ("c3", 3001, 1000), ("c5", 301, 5120),
+                                    ("c4", 9, 65528)])
+def test_dgamma_in_input_dtype(cuda, name, M, N):
+    """With RMSNORM_FLAG_DGAMMA_IN_DTYPE dgamma is the float32 result rounded
+    to nearest even to the input dtype (combined call and stage 2 alone)."""
+    inp = workloads.make_inputs(name, M=M, N=N)
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    off = inp["offset"]
+    _, r = rn.fwd(x, w, inp["eps"], off)
+    dx, dg32 = rn.bwd(dy, x, w, r, off)
+    dx2, dgT = rn.bwd(dy, x, w, r, off, poison=True, dgamma_dtype=x.dtype)
+    ws = torch.empty(rn.rmsnorm_bwd_workspace_bytes(M, N, x.dtype, off) // 4, device=cuda)
+    rn.rmsnorm_bwd_rows(dy, x, w, r, torch.empty_like(x), ws, off)
+    dgT2 = torch.full((N,), float("nan"), device=cuda, dtype=x.dtype)
+    rn.rmsnorm_bwd_reduce(ws, M, N, x.dtype, dgT2, off)
+    torch.cuda.synchronize()
+    assert dgT.dtype == x.dtype
+    assert torch.equal(dx, dx2)
+    assert torch.equal(dgT, dg32.to(x.dtype)) and torch.equal(dgT2, dgT)
+
+
+# (recipe, M, N, row stride of x/dy, row stride of y/dx): full-width kernels
+# (16-byte aligned strides), the long-row kernel, and odd strides that force
+# narrower vectors.
+STRIDED = [("c2", 1500, 4096, 4104, 4160), ("c3", 3001, 1000, 1003, 1024),
+           ("c5", 301, 5120, 5200, 5128), ("c4", 9, 65528, 65536, 65600),
+           ("c1a", 65, 128, 130, 129)]
+
+
+@pytest.mark.parametrize("name,M,N,ldi,ldo", STRIDED)
+def test_strided_rows(cuda, name, M, N, ldi, ldo):
+    """x and dy are column slices of wider buffers, y and dx are written into
+    wider buffers; the gaps between rows are never touched."""
+    inp = workloads.make_inputs(name, M=M, N=N)
+    off, eps = inp["offset"], inp["eps"]
+    T = inp["x"].dtype
+    sentinel = -12345.0
+
+    def sliced(t, ld):
+        buf = torch.full((M, ld), sentinel, dtype=T, device=cuda)
+        buf[:, :N] = t.to(cuda)
+        return buf, buf[:, :N]
+
+    xbuf, x = sliced(inp["x"], ldi)
+    dybuf, dy = sliced(inp["dy"], ldi)
+    ybuf = torch.full((M, ldo), float("nan"), dtype=T, device=cuda)
+    dxbuf = torch.full((M, ldo), float("nan"), dtype=T, device=cuda)
+    ybuf[:, N:] = sentinel
+    dxbuf[:, N:] = sentinel
+    y, dx = ybuf[:, :N], dxbuf[:, :N]
+    w = inp["w"].to(cuda)
+    rstd = torch.full((M,), float("nan"), device=cuda)
+    dg = torch.full((N,), float("nan"), device=cuda)
+    ws = torch.empty(max(4, rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)) // 4, device=cuda)
+    log(f"case strided {name} M={M} N={N} ld {ldi}/{ldo}")
+    rn.rmsnorm_fwd_strided(x, w, eps, y, rstd, off)
+    rn.rmsnorm_bwd_strided(dy, x, w, rstd, dx, dg, ws, off)
+    torch.cuda.synchronize()
+    for buf in (ybuf, dxbuf):
+        assert bool((buf[:, N:] == sentinel).all()), "a gap between rows was written"
+    for buf in (xbuf, dybuf):
+        assert bool((buf[:, N:] == sentinel).all()), "an input gap was written"
+    out = {"y": y.contiguous(), "rstd": rstd, "dx": dx.contiguous(), "dgamma": dg}
+    assert_pass(gate_full(inp, out), f"strided {name}")
+
+
+def test_output_interleaved_with_input(cuda):
+    """x in the first N columns of a buffer, y in the next N (same row stride):
+    accepted as disjoint and computed correctly."""
+    inp = workloads.make_inputs("c2", M=777, N=4096)
+    buf = torch.empty((777, 2 * 4096), dtype=torch.bfloat16, device=cuda)
+    buf[:, :4096] = inp["x"].to(cuda)
+    x, y = buf[:, :4096], buf[:, 4096:]
+    rstd = torch.empty(777, device=cuda)
+    rn.rmsnorm_fwd_strided(x, inp["w"].to(cuda), inp["eps"], y, rstd)
+    y0, r0 = rn.fwd(inp["x"].to(cuda), inp["w"].to(cuda), inp["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(rstd, r0)
+    assert torch.equal(x, inp["x"].to(cuda))
+
+
 def test_side_stream(cuda):
     inp = workloads.make_inputs("c3", M=5000, N=1024)
     x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
