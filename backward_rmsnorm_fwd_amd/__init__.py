@@ -34,7 +34,9 @@ RMSNORM_FLAG_DGAMMA_IN_DTYPE = 2
 PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
 KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
-                9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long"}
+                9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
+                13: "bwd_split", 14: "bwd_reduce_wide"}
+MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
@@ -61,7 +63,8 @@ class Plan(ctypes.Structure):
                 ("chunks", ctypes.c_int32), ("x_in_lds", ctypes.c_int32),
                 ("weight_in_regs", ctypes.c_int32), ("dy_in_lds", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("partials", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int64)]
+                ("lds_bytes", ctypes.c_int64), ("segments", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}

@@ -6,8 +6,9 @@
 // rather than rerouted (section "Adapting the kernel and moving to
 // production": no silent fallback).  The accepted domain is widened from the
 // page's (fp32/fp16, N <= 4096, a 64 MiB scratch cap on an M x N partial
-// array) to fp32/fp16/bf16 and N <= 65536, because the M x N partial array is
-// replaced by a [P, N] one (P = number of backward workgroups).
+// array) to fp32/fp16/bf16 and N <= 2^24, because the M x N partial array is
+// replaced by a [P, N] one (P = number of backward workgroups) and rows longer
+// than 65536 elements take the split-row plan (rmsnorm_split.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,6 +32,7 @@ using namespace rmsnorm_hip;
 constexpr int kCUs = 256;
 constexpr int kMaxChunksPreferred = 16;  // register-resident chunks per thread
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int64_t kMaxRowN = 65536;  // longest row handled by one workgroup
 
 int elem_bytes(int dtype) { return dtype == RMSNORM_F32 ? 4 : 2; }
 
@@ -271,12 +273,54 @@ int64_t generic_bwd_partials(int64_t M, int64_t N, int vec) {
   return std::min<int64_t>(M, static_cast<int64_t>(kCUs) * per_cu);
 }
 
+// ---- split rows (N > kMaxRowN): rmsnorm_split.hip ----------------------------
+//
+// Segments of 16 KiB; P row blocks.  The forward aims at 2048 workgroups.
+// The backward keeps at least 16 rows per block where M allows (each block
+// writes one float32 partial row, so fewer rows per block cost more partial
+// traffic) and otherwise aims at 1024 workgroups.  The grid stays below 2^24
+// workgroups of 256 threads.
+constexpr int64_t kSplitFwdWorkgroups = 2048;
+constexpr int64_t kSplitBwdWorkgroups = 1024;
+constexpr int64_t kSplitBwdRowsPerBlock = 16;
+constexpr int64_t kMaxSplitGrid = (int64_t(1) << 24) - 1;
+
+bool split_rows(int64_t N) { return N > kMaxRowN; }
+
+int64_t split_nseg(int64_t N, int es) { return ceil_div(N, split_segment_elems(es)); }
+
+int64_t split_partials(int64_t M, int64_t N, int es, bool backward) {
+  const int64_t nseg = split_nseg(N, es);
+  int64_t P = backward ? std::max(ceil_div(M, kSplitBwdRowsPerBlock),
+                                  ceil_div(kSplitBwdWorkgroups, nseg))
+                       : ceil_div(kSplitFwdWorkgroups, nseg);
+  P = std::min(P, kMaxSplitGrid / nseg);
+  return std::max<int64_t>(1, std::min(P, M));
+}
+
+// Backward workspace of the split plan: part[P, N], then the per-(row,
+// segment) dot partials [M, nseg], then the per-row coefficients [M], each
+// starting on a 16-byte boundary.
+struct SplitWorkspace {
+  int64_t part_floats, dotp_offset, coef_offset, total_floats;
+};
+
+SplitWorkspace split_workspace(int64_t M, int64_t N, int es) {
+  SplitWorkspace w;
+  w.part_floats = split_partials(M, N, es, true) * N;
+  w.dotp_offset = ceil_div(w.part_floats, 4) * 4;
+  w.coef_offset = w.dotp_offset + ceil_div(M * split_nseg(N, es), 4) * 4;
+  w.total_floats = w.coef_offset + ceil_div(M, 4) * 4;
+  return w;
+}
+
 // Backward workgroup count P: a function of (M, N, dtype) only, computed
 // with the vector width that N alone allows (pointer alignment can only
 // change which kernel runs, never P).
 int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
   if (M <= 0) return 0;
   const int es = elem_bytes(dtype);
+  if (split_rows(N)) return split_partials(M, N, es, true);
   const int vec = pick_vec(N, es, 16);
   if (vec * es == 16) {
     const PipeCfg pc = plan_pipe_bwd(N / vec);
@@ -299,6 +343,11 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
       p->kernel = RMSNORM_KERNEL_BWD_REDUCE16;
       p->block_threads = 256;
       p->grid = ceil_div(N, 16);
+    } else if (N % 4 == 0) {
+      // One wavefront slice per 4 partial rows, at most 16.
+      p->kernel = RMSNORM_KERNEL_BWD_REDUCE_WIDE;
+      p->block_threads = kWave * std::min(16, pow2_at_least(ceil_div(p->partials, 4)));
+      p->grid = ceil_div(N, 256);
     } else {
       p->kernel = RMSNORM_KERNEL_BWD_REDUCE;
       p->block_threads = 1024;
@@ -308,6 +357,20 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
     return;
   }
   p->vec = vec;
+  if (split_rows(N)) {
+    const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+    const int64_t nseg = split_nseg(N, es);
+    p->kernel = bwd ? RMSNORM_KERNEL_BWD_SPLIT : RMSNORM_KERNEL_FWD_SPLIT;
+    p->segments = static_cast<int32_t>(nseg);
+    p->threads_per_row = static_cast<int32_t>(256 * nseg);
+    p->chunks = split_chunks(vec, es);
+    p->block_threads = 256;
+    p->weight_in_regs = 1;
+    const int64_t P = split_partials(M, N, es, bwd);
+    p->partials = bwd ? P : 0;
+    p->grid = P * nseg;
+    return;
+  }
   if (pass == RMSNORM_PASS_FWD && full) {
     const PipeCfg pc = plan_pipe_fwd(N / vec);
     if (pc.ok) {
@@ -539,6 +602,8 @@ int check_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
     return RMSNORM_ERR_DTYPE;
   if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
   if (N < 1 || N > RMSNORM_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  // Keeps every row-block boundary p*M (p < 2^24 workgroups) inside int64.
+  if (M > RMSNORM_MAX_ELEMENTS / N) return RMSNORM_ERR_SHAPE;
   return RMSNORM_OK;
 }
 
@@ -680,6 +745,11 @@ int fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M
   const int n = static_cast<int>(N);
   const RowStrides ld{ldx, ldy, 0, 0};
   hipError_t e;
+  if (p.kernel == RMSNORM_KERNEL_FWD_SPLIT) {
+    const FastFwdArgs a{x, gamma, y, rstd, M, n, eps, off, ldx * es, ldy * es};
+    const SplitPlan sp{p.vec, p.segments, p.grid / p.segments};
+    return status_of(split_fwd_launch(dtype, sp, a, stream));
+  }
   switch (dtype) {
     case RMSNORM_F32: e = fwd_by_vec<kF32>(p, x, gamma, y, rstd, M, n, eps, off, ld, stream); break;
     case RMSNORM_F16: e = fwd_by_vec<kF16>(p, x, gamma, y, rstd, M, n, eps, off, ld, stream); break;
@@ -703,6 +773,14 @@ int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, co
   float* part = static_cast<float*>(workspace);
   const RowStrides ld{ldx, 0, lddy, lddx};
   hipError_t e;
+  if (p.kernel == RMSNORM_KERNEL_BWD_SPLIT) {
+    const FastBwdArgs a{dy, x, gamma, rstd, dx, part, M, n, off, p.partials,
+                        lddy * es, ldx * es, lddx * es};
+    const SplitPlan sp{p.vec, p.segments, p.partials};
+    const SplitWorkspace w = split_workspace(M, N, es);
+    return status_of(split_bwd_launch(dtype, sp, a, part + w.dotp_offset, part + w.coef_offset,
+                                      stream));
+  }
   switch (dtype) {
     case RMSNORM_F32: e = bwd_rows_by_vec<kF32>(p, dy, x, gamma, rstd, dx, part, M, n, off, ld, stream); break;
     case RMSNORM_F16: e = bwd_rows_by_vec<kF16>(p, dy, x, gamma, rstd, dx, part, M, n, off, ld, stream); break;
@@ -718,13 +796,19 @@ int bwd_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype
   fill_plan(M, N, dtype, RMSNORM_PASS_BWD_REDUCE, 16, &p);
   const float* part = static_cast<const float*>(workspace);
   const int n = static_cast<int>(N);
-  const bool r16 = p.kernel == RMSNORM_KERNEL_BWD_REDUCE16;
   const int out = (flags & RMSNORM_FLAG_DGAMMA_IN_DTYPE) ? static_cast<int>(dtype) : kOutF32;
-#define RMSNORM_REDUCE(OUT)                                                                 \
-  return status_of(r16 ? launch(bwd_reduce16_kernel<OUT>, p.grid, p.block_threads, 0, stream, \
-                                part, dgamma, p.partials, n)                                \
-                       : launch(bwd_reduce_kernel<OUT>, p.grid, p.block_threads, 0, stream,   \
-                                part, dgamma, p.partials, n))
+#define RMSNORM_REDUCE(OUT)                                                                   \
+  switch (p.kernel) {                                                                         \
+    case RMSNORM_KERNEL_BWD_REDUCE16:                                                         \
+      return status_of(launch(bwd_reduce16_kernel<OUT>, p.grid, p.block_threads, 0, stream,   \
+                              part, dgamma, p.partials, n));                                  \
+    case RMSNORM_KERNEL_BWD_REDUCE_WIDE:                                                      \
+      return status_of(launch(bwd_reduce_wide_kernel<OUT>, p.grid, p.block_threads, 0, stream, \
+                              part, dgamma, p.partials, n));                                  \
+    default:                                                                                  \
+      return status_of(launch(bwd_reduce_kernel<OUT>, p.grid, p.block_threads, 0, stream,     \
+                              part, dgamma, p.partials, n));                                  \
+  }
   switch (out) {
     case kF32: RMSNORM_REDUCE(kF32);
     case kF16: RMSNORM_REDUCE(kF16);
@@ -765,7 +849,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_OK: return "ok";
     case RMSNORM_ERR_NULL_POINTER: return "a required pointer is NULL";
     case RMSNORM_ERR_DTYPE: return "unsupported dtype (fp32, fp16 and bf16 are supported)";
-    case RMSNORM_ERR_SHAPE: return "unsupported shape (need 1 <= N <= 65536 and 0 <= M <= 2^40)";
+    case RMSNORM_ERR_SHAPE:
+      return "unsupported shape (need 1 <= N <= 2^24, 0 <= M <= 2^40 and M*N <= 2^46)";
     case RMSNORM_ERR_EPS: return "eps must be finite and positive";
     case RMSNORM_ERR_FLAGS: return "unknown flag bits";
     case RMSNORM_ERR_WORKSPACE: return "workspace missing or smaller than rmsnorm_bwd_workspace_bytes()";
@@ -792,7 +877,8 @@ int rmsnorm_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t fla
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                    uint32_t flags) {
-  if (check_common(M, N, dtype, flags) != RMSNORM_OK) return 0;
+  if (check_common(M, N, dtype, flags) != RMSNORM_OK || M == 0) return 0;
+  if (split_rows(N)) return static_cast<size_t>(split_workspace(M, N, elem_bytes(dtype)).total_floats * 4);
   return static_cast<size_t>(bwd_partials(M, N, dtype) * N * 4);
 }
 

@@ -1039,4 +1039,50 @@ static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward stage 2 for long rows: each lane adds 4 adjacent columns with
+// 16-byte loads, so one wavefront reads 1 KiB of a partial row; the S
+// wavefronts of a workgroup (S = blockDim.x / 64, a power of two <= 16) take
+// the partial rows s, s+S, ... of the same 256 columns in float64, and the
+// S slice sums are then added in slice order.  Needs N % 4 == 0.
+// ---------------------------------------------------------------------------
+template <int OUT>
+static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduce_wide_kernel(
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
+  constexpr int kCols = 256;
+  __shared__ double sums[kMaxWavesPerBlock][kCols];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = threadIdx.x / kWave;
+  const int S = blockDim.x / kWave;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * kCols + lane * 4;
+  double a[4] = {0.0, 0.0, 0.0, 0.0};
+  if (col < N) {
+#pragma unroll 4
+    for (int64_t p = s; p < P; p += S) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + p * N + col);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] += static_cast<double>(v[k]);
+    }
+  }
+  if (S == 1) {
+    if (col < N) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) store_dgamma<OUT>(dgamma, col + k, a[k]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sums[s][lane * 4 + k] = a[k];
+  __syncthreads();
+  // blockDim.x is 128 .. 1024: each thread finishes every blockDim.x-th column.
+  for (int j = threadIdx.x; j < kCols; j += blockDim.x) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kCols + j;
+    if (c < N) {
+      double tot = 0.0;
+      for (int i = 0; i < S; ++i) tot += sums[i][j];
+      store_dgamma<OUT>(dgamma, c, tot);
+    }
+  }
+}
+
 }  // namespace rmsnorm_hip

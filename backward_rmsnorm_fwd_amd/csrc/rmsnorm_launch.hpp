@@ -77,4 +77,24 @@ hipError_t pipe_bwd_launch(int wpr, int ch, int block, int dlds, int64_t lds,
 template <int DT>
 hipError_t long_bwd_launch(int ch, int64_t lds, const FastBwdArgs& a, hipStream_t s);
 
+// Split-row plan (rows longer than 65536 elements): segments of
+// split_segment_elems(elem_bytes) elements, P row blocks, workgroup
+// p*nseg + s on segment s of block p.  `vec` is the access width in
+// elements.
+struct SplitPlan {
+  int vec;
+  int nseg;
+  int64_t P;
+};
+int split_segment_elems(int elem_bytes);
+int split_chunks(int vec, int elem_bytes);
+// Forward: stats, finish and apply kernels (y rows hold the segment sums
+// between the first two).
+hipError_t split_fwd_launch(int dtype, const SplitPlan& sp, const FastFwdArgs& a,
+                            hipStream_t s);
+// Backward stage 1: stats (dot partials [M, nseg] and part[P, N]), finish
+// (coef[M]) and apply (dx).
+hipError_t split_bwd_launch(int dtype, const SplitPlan& sp, const FastBwdArgs& a, float* dotp,
+                            float* coef, hipStream_t s);
+
 }  // namespace rmsnorm_hip

@@ -48,8 +48,10 @@
  *  - Bitwise reproducibility: the same inputs and (M, N, dtype, flags, and
  *    pointer alignment modulo 16 bytes) give bitwise-identical outputs; no
  *    atomics are used and every reduction has a fixed order.
- *  - Limits: 1 <= N <= RMSNORM_MAX_N, 0 <= M <= RMSNORM_MAX_M.  M = 0 is a
- *    no-op for the row outputs; the backward then writes dgamma = 0.
+ *  - Limits: 1 <= N <= RMSNORM_MAX_N (2^24), 0 <= M <= RMSNORM_MAX_M and
+ *    M * N <= RMSNORM_MAX_ELEMENTS.  M = 0 is a no-op for the row outputs;
+ *    the backward then writes dgamma = 0.  Rows of more than 65536 elements
+ *    take the split-row plan (RMSNORM_KERNEL_FWD_SPLIT / BWD_SPLIT).
  */
 #ifndef RMSNORM_H
 #define RMSNORM_H
@@ -74,8 +76,9 @@ typedef enum {
  * float32 value of the sum), as the weight's own dtype, instead of float32. */
 #define RMSNORM_FLAG_DGAMMA_IN_DTYPE 2u
 
-#define RMSNORM_MAX_N 65536
+#define RMSNORM_MAX_N (((int64_t)1) << 24)
 #define RMSNORM_MAX_M (((int64_t)1) << 40)
+#define RMSNORM_MAX_ELEMENTS (((int64_t)1) << 46) /* M * N */
 
 /* status codes */
 #define RMSNORM_OK 0
@@ -97,7 +100,9 @@ typedef enum {
  *   x     [M, N] T, read
  *   gamma [N] T (gamma, or w in offset mode), read
  *   eps   added to the mean square inside the square root; finite and > 0
- *   y     [M, N] T, written (every element)
+ *   y     [M, N] T, written (every element).  For N > 65536 the first
+ *         bytes of each row of y hold the per-segment partial sums between
+ *         the forward's kernels; on return y holds only the result.
  *   rstd  [M] float32, written
  * Errors: NULL_POINTER (a needed pointer is NULL; pointers may be NULL only
  * when M = 0), DTYPE, SHAPE, EPS, FLAGS, ALIGNMENT, OVERLAP, LAUNCH (the
@@ -110,8 +115,10 @@ int rmsnorm_fwd(const void* x, const void* gamma, float eps, int64_t M,
 /*
  * Bytes of device workspace the backward needs for (M, N, dtype, flags): the
  * per-workgroup float32 partial sums of dgamma, [P, N] with P a fixed
- * function of (M, N, dtype).  Returns 0 for M = 0 and for invalid arguments
- * (which the backward then rejects).
+ * function of (M, N, dtype).  For N > 65536 it also holds, each from a
+ * 16-byte boundary, the [M, segments] float32 partial row sums of dy*g*x and
+ * the [M] per-row coefficients r^3*c.  Returns 0 for M = 0 and for invalid
+ * arguments (which the backward then rejects).
  */
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                    uint32_t flags);
@@ -204,6 +211,8 @@ typedef struct {
   int64_t grid;            /* workgroups launched */
   int64_t partials;        /* P: rows of the dgamma partial-sum workspace */
   int64_t lds_bytes;       /* dynamic LDS per workgroup */
+  int32_t segments;        /* split-row plan: workgroups sharing one row */
+  int32_t reserved;
 } rmsnorm_plan_t;
 
 /* Kernels.  The *_ROWS kernels use 16-byte accesses with the row geometry
@@ -226,6 +235,17 @@ typedef struct {
  * row, x staged in LDS and dy in registers for the whole row, the next
  * row's chunks loaded behind the current row's dx stores. */
 #define RMSNORM_KERNEL_BWD_LONG 11
+/* Split-row plan for N > 65536: each row is cut into `segments` segments of
+ * 16 KiB, one 256-thread workgroup per (row block, segment).  A stats kernel
+ * writes each segment's partial row sum, a finish kernel adds them per row
+ * (float64, segment order) and an apply kernel writes the row outputs.  The
+ * forward keeps the segment sums in the first bytes of each row of y
+ * between its kernels; the backward keeps them in the workspace. */
+#define RMSNORM_KERNEL_FWD_SPLIT 12 /* forward, three kernels */
+#define RMSNORM_KERNEL_BWD_SPLIT 13 /* backward stage 1, three kernels */
+/* Backward stage 2 for rows of more than 8192 elements (N % 4 == 0): 256
+ * columns per workgroup with 16-byte loads, up to 16 slices of partial rows. */
+#define RMSNORM_KERNEL_BWD_REDUCE_WIDE 14
 
 #define RMSNORM_PASS_FWD 0
 #define RMSNORM_PASS_BWD_ROWS 1

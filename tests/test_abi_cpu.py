@@ -61,7 +61,8 @@ def fwd_call(x=A, g=A + (1 << 24), eps=1e-6, M=4, N=256, dtype=2, flags=0,
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": 3}, EDTYPE), ({"dtype": -1}, EDTYPE),
     ({"flags": 4}, EFLAGS), ({"flags": 6}, EFLAGS),
-    ({"N": 0}, ESHAPE), ({"N": 65537}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"N": 0}, ESHAPE), ({"N": (1 << 24) + 1}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"M": 1 << 40, "N": 65537}, ESHAPE),  # M*N above 2^46
     ({"eps": 0.0}, EEPS), ({"eps": -1e-6}, EEPS), ({"eps": float("nan")}, EEPS),
     ({"eps": float("inf")}, EEPS),
     ({"x": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL), ({"r": None}, ENULL),
@@ -93,7 +94,7 @@ def bwd_call(dy=A, x=A + (1 << 24), g=A + (2 << 24), r=A + (3 << 24), M=4, N=256
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": 5}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": 70000}, ESHAPE),
+    ({"dtype": 5}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": (1 << 24) + 1}, ESHAPE),
     ({"dy": None}, ENULL), ({"x": None}, ENULL), ({"g": None}, ENULL), ({"r": None}, ENULL),
     ({"dx": None}, ENULL), ({"dg": None}, ENULL),
     ({"ws": None}, EWS), ({"ws_bytes": 16}, EWS),
@@ -225,7 +226,8 @@ def test_plans_for_the_workloads():
     red = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_REDUCE)
     assert red["kernel_name"] == "bwd_reduce16" and red["grid"] == 4096 // 16
     red4 = rn.rmsnorm_query_plan(2048, 65536, 2, which=rn.PASS_BWD_REDUCE)
-    assert red4["kernel_name"] == "bwd_reduce" and red4["grid"] == 65536 // 64
+    assert red4["kernel_name"] == "bwd_reduce_wide" and red4["grid"] == 65536 // 256
+    assert red4["block_threads"] == 1024
 
 
 def test_partials_do_not_depend_on_alignment():
@@ -270,6 +272,69 @@ def test_plan_covers_every_n():
                     assert n % p["vec"] == 0
                     assert p["chunks"] <= 64 and p["block_threads"] <= 1024
                     assert p["lds_bytes"] <= 160 * 1024
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("M,N,dt", [(33, 131072, 2), (5, 65537, 1), (7, 65540, 0),
+                                    (2, 1 << 24, 2), (261, 98304, 2), (100000, 70000, 1),
+                                    (1, 1 << 24, 0), (4096, 65537, 0)])
+def test_split_plan(M, N, dt):
+    """Rows longer than 65536 elements: 16 KiB segments, one 256-thread
+    workgroup per (row block, segment), blocks of at least 16 rows where M
+    allows; the workspace holds the [P, N] column partials, the [M, segments]
+    row partials and the [M] coefficients, each from a 16-byte boundary."""
+    es = 4 if dt == 0 else 2
+    nseg = _ceil(N * es, 16384)
+    f = rn.rmsnorm_query_plan(M, N, dt, which=rn.PASS_FWD)
+    b = rn.rmsnorm_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
+    assert f["kernel_name"] == "fwd_split" and b["kernel_name"] == "bwd_split"
+    for p in (f, b):
+        assert p["segments"] == nseg and p["block_threads"] == 256
+        assert p["threads_per_row"] == 256 * nseg
+        assert p["grid"] % nseg == 0 and p["grid"] < 1 << 24
+        assert p["chunks"] * p["vec"] * es == 64
+        assert 1 <= p["grid"] // nseg <= M
+    P = b["partials"]
+    assert b["grid"] == P * nseg
+    assert P == max(1, min(M, max(_ceil(M, 16), _ceil(1024, nseg)), ((1 << 24) - 1) // nseg))
+    assert f["partials"] == 0
+    assert f["grid"] // nseg == max(1, min(M, _ceil(2048, nseg), ((1 << 24) - 1) // nseg))
+    r4 = lambda v: _ceil(v, 4) * 4  # noqa: E731
+    assert rn.rmsnorm_bwd_workspace_bytes(M, N, dt) == 4 * (r4(P * N) + r4(M * nseg) + r4(M))
+    red = rn.rmsnorm_query_plan(M, N, dt, which=rn.PASS_BWD_REDUCE)
+    assert red["partials"] == P
+    if N % 4 == 0:
+        assert red["kernel_name"] == "bwd_reduce_wide" and red["grid"] == _ceil(N, 256)
+        slices = 1
+        while slices < min(16, _ceil(P, 4)):
+            slices *= 2
+        assert red["block_threads"] == 64 * slices
+    else:
+        assert red["kernel_name"] == "bwd_reduce"
+
+
+def test_split_plan_covers_rows_and_scratch():
+    """Every split N: the segments cover the row with no empty segment, and a
+    row of y has room for the forward's per-segment float32 sums (two 16-bit
+    or one 32-bit element each)."""
+    for dt in (0, 1, 2):
+        es = 4 if dt == 0 else 2
+        for n in [65537, 65540, 65544, 73728, 98303, 131072, 131073, 999999, (1 << 24) - 1,
+                  1 << 24]:
+            for align in (16, 8, 4, 2):
+                if es == 4 and align < 4:
+                    continue
+                p = rn.rmsnorm_query_plan(3, n, dt, which=rn.PASS_FWD, align_bytes=align)
+                seg = 256 * p["chunks"] * p["vec"]
+                assert seg * es == 16384 and n % p["vec"] == 0
+                assert p["segments"] * seg >= n > (p["segments"] - 1) * seg
+                assert p["segments"] * (4 // es) <= n
+    assert rn.rmsnorm_query_plan(3, 65536, 2, which=rn.PASS_FWD)["kernel_name"] != "fwd_split"
+    with pytest.raises(rn.RmsnormError):
+        rn.rmsnorm_query_plan(3, (1 << 24) + 1, 2)
 
 
 def test_query_plan_rejects():

@@ -108,7 +108,8 @@ def test_full_size_sampled(cuda, name):
 
 
 def test_backward_is_bitwise_reproducible(cuda):
-    for name, M, N in [("c2", 4096, 4096), ("c5", 999, 5120), ("c4", 21, 65536)]:
+    for name, M, N in [("c2", 4096, 4096), ("c5", 999, 5120), ("c4", 21, 65536),
+                       ("c4", 40, 131072)]:
         inp = workloads.make_inputs(name, M=M, N=N)
         x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
         y0, r0 = rn.fwd(x, w, inp["eps"], inp["offset"])
@@ -119,8 +120,9 @@ def test_backward_is_bitwise_reproducible(cuda):
             assert torch.equal(dx, runs[0][0]) and torch.equal(dg, runs[0][1]), name
 
 
-def test_stage_entry_points_match_combined(cuda):
-    inp = workloads.make_inputs("c2", M=1500, N=4096)
+@pytest.mark.parametrize("M,N", [(1500, 4096), (70, 131072)])
+def test_stage_entry_points_match_combined(cuda, M, N):
+    inp = workloads.make_inputs("c2", M=M, N=N)
     x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
     _, r = rn.fwd(x, w)
     dx, dg = rn.bwd(dy, x, w, r)
@@ -160,7 +162,8 @@ def test_dgamma_in_input_dtype(cuda, name, M, N):
 # narrower vectors.
 STRIDED = [("c2", 1500, 4096, 4104, 4160), ("c3", 3001, 1000, 1003, 1024),
            ("c5", 301, 5120, 5200, 5128), ("c4", 9, 65528, 65536, 65600),
-           ("c1a", 65, 128, 130, 129)]
+           ("c1a", 65, 128, 130, 129), ("c4", 19, 98304, 98305, 98312),
+           ("c3", 9, 70000, 70008, 70001)]
 
 
 @pytest.mark.parametrize("name,M,N,ldi,ldo", STRIDED)
@@ -229,6 +232,38 @@ def test_side_stream(cuda):
     assert torch.equal(y0, y1) and torch.equal(dx0, dx1) and torch.equal(dg0, dg1)
 
 
+# Rows longer than 65536 elements take the split-row plan: 16 KiB segments
+# (4096 fp32 / 8192 16-bit elements) over several workgroups, stats -> finish
+# -> apply.  Cases: a last segment of 1 element with 2-byte accesses (fp16
+# N=65537), 17 segments with a 4-element tail (fp32 N=65540), one row per
+# block (M=3), odd M (the two-row steps' tail), blocks of 16+ rows, the
+# recipes' special rows (c3) and offset weight (c5), and the largest N.
+# Stage 2 then runs with 1, 2, 4, 8 and 16 slices of partial rows.
+SPLIT_TILES = [((5, 65537), torch.float16, 21), ((7, 65540), torch.float32, 22),
+               ((3, 1 << 20), torch.bfloat16, 23), ((2, rn.MAX_N), torch.bfloat16, 24),
+               ((4, 3, 100003), torch.float16, 25), ((11, 200000), torch.float32, 26),
+               ((30, 327680), torch.bfloat16, 27)]
+SPLIT_RECIPES = [("c4", 33, 131072), ("c4", 261, 98304), ("c3", 301, 70000),
+                 ("c5", 129, 81920), ("c2", 600, 73728)]
+
+
+@pytest.mark.parametrize("shape,dtype,seed", SPLIT_TILES)
+def test_split_rows_tiles(cuda, shape, dtype, seed):
+    plan = rn.rmsnorm_query_plan(int(np.prod(shape[:-1])), shape[-1], dtype,
+                                 which=rn.PASS_BWD_ROWS)
+    assert plan["kernel_name"] == "bwd_split"
+    inp = workloads.make_tile_case(shape, dtype, seed)
+    log(f"case split {shape} {dtype} seed {seed} segments {plan['segments']}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"split {shape} {dtype}")
+
+
+@pytest.mark.parametrize("name,M,N", SPLIT_RECIPES)
+def test_split_rows_recipes(cuda, name, M, N):
+    inp = workloads.make_inputs(name, M=M, N=N)
+    log(f"case split {name} recipe at M={M} N={N}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"split {name} @ {M}x{N}")
+
+
 @pytest.mark.parametrize("dtype,N", [(torch.float32, 1), (torch.bfloat16, 1), (torch.float16, 2),
                                      (torch.float32, 65536), (torch.float32, 65535),
                                      (torch.bfloat16, 65535), (torch.float16, 32769),
@@ -284,5 +319,6 @@ def test_binding_rejects_bad_tensors(cuda):
     with pytest.raises(rn.RmsnormError):
         rn.fwd(x, w, eps=0.0)
     with pytest.raises(rn.RmsnormError):
-        rn.fwd(torch.empty(2, 70000, device=cuda, dtype=torch.bfloat16),
-               torch.ones(70000, device=cuda, dtype=torch.bfloat16))
+        n = rn.MAX_N + 1
+        rn.fwd(torch.empty(2, n, device=cuda, dtype=torch.bfloat16),
+               torch.ones(n, device=cuda, dtype=torch.bfloat16))
