@@ -98,6 +98,38 @@ def make_inputs(name, M=None, N=None, seed=None, dtype=None):
     offset weight w when ``offset``), ``dy`` [M, N], plus ``offset``, ``eps``,
     ``dtype`` and, for the scaled-rows recipe, the row index sets.
     """
+    out, arrays, _ = _draw(name, M, N, seed, dtype)
+    x, g, dy = arrays
+    out.update(x=_cast(x, out["dtype"]), w=_cast(g, out["dtype"]), dy=_cast(dy, out["dtype"]))
+    return out
+
+
+def make_layernorm_inputs(name, M=None, N=None, seed=None, dtype=None):
+    """LayerNorm inputs for workload ``name``: the RMSNorm recipe's x, weight
+    and dy (same draws), then, from the same generator, a bias
+    ``b ~ U(-0.5, 0.5)`` [N] and a per-row shift ``s_i ~ N(0, 1)`` added to
+    every element of row i before the cast, so rows have non-zero means (the
+    c3 recipe's all-zero rows become constant rows).  The worked examples
+    (c1b, c1c) keep x = [3, 4] and take b = [0, 0] and [0.5, -0.25].
+    The offset recipe's weight is used as gamma directly (LayerNorm has no
+    offset mode).  Returns the dict of ``make_inputs`` plus ``b``.
+    """
+    out, arrays, rng = _draw(name, M, N, seed, dtype)
+    x, g, dy = arrays
+    M, N = out["M"], out["N"]
+    if rng is None:
+        b = np.array([0.0, 0.0] if name == "c1b" else [0.5, -0.25], dtype=np.float32)
+    else:
+        b = _uniform(rng, (N,), -0.5, 0.5)
+        x = x + _normal(rng, (M, 1))
+    T = out["dtype"]
+    out.update(x=_cast(x, T), w=_cast(g, T), dy=_cast(dy, T), b=_cast(b, T), offset=False)
+    return out
+
+
+def _draw(name, M, N, seed, dtype):
+    """The float32 arrays (x, weight, dy) of a recipe, its metadata, and the
+    generator after the draws (None for the fixed worked examples)."""
     wl = WORKLOADS[name]
     M = wl.M if M is None else int(M)
     N = wl.N if N is None else int(N)
@@ -110,8 +142,7 @@ def make_inputs(name, M=None, N=None, seed=None, dtype=None):
         g = np.array([1.0, 1.0] if wl.recipe == "c1b" else [2.0, 0.5],
                      dtype=np.float32)
         dy = np.array([[1.0, 2.0]], dtype=np.float32)
-        out.update(x=_cast(x, dtype), w=_cast(g, dtype), dy=_cast(dy, dtype))
-        return out
+        return out, (x, g, dy), None
     rng = np.random.Generator(np.random.PCG64(seed))
     if wl.recipe == "c1a":
         x = np.zeros((M, N), dtype=np.float32)
@@ -143,8 +174,7 @@ def make_inputs(name, M=None, N=None, seed=None, dtype=None):
                    zero_rows=np.sort(zero))
     else:  # pragma: no cover
         raise KeyError(wl.recipe)
-    out.update(x=_cast(x, dtype), w=_cast(g, dtype), dy=_cast(dy, dtype))
-    return out
+    return out, (x, g, dy), rng
 
 
 def make_tile_case(shape, dtype, seed, scale=1.0):
@@ -161,3 +191,20 @@ def make_tile_case(shape, dtype, seed, scale=1.0):
     dy = _normal(rng, shape)
     return {"x": _cast(x, dtype), "w": _cast(g, dtype), "dy": _cast(dy, dtype),
             "offset": False, "eps": 1e-6, "dtype": dtype}
+
+
+def make_layernorm_tile_case(shape, dtype, seed, scale=1.0, shift_std=1.0):
+    """LayerNorm version of ``make_tile_case``: the same draws, then a bias
+    b ~ U(-0.5, 0.5) and a per-row shift ~ N(0, shift_std) added before the
+    cast.  A small ``scale`` with a large ``shift_std`` gives rows whose
+    spread is tiny against their mean (the variance then comes from a
+    cancelling difference)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = shape[-1]
+    x = _normal(rng, shape) * np.float32(scale)
+    g = _uniform(rng, (n,), 0.5, 1.5)
+    dy = _normal(rng, shape)
+    b = _uniform(rng, (n,), -0.5, 0.5)
+    x = x + _normal(rng, shape[:-1] + (1,), shift_std)
+    return {"x": _cast(x, dtype), "w": _cast(g, dtype), "dy": _cast(dy, dtype),
+            "b": _cast(b, dtype), "offset": False, "eps": 1e-6, "dtype": dtype}

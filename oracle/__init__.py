@@ -15,11 +15,14 @@ page, section "核心方法" (core method): golden / reference / target):
 * ``reference`` -- an eager PyTorch-CPU implementation in the kernel's dtype
                    with float32 intermediates; it measures how close a correct
                    same-precision implementation gets to the golden.
+* ``layernorm`` -- the same two roles (float64 golden, float32 same-dtype
+                   reference) for LayerNorm, the sibling operation.
 * ``gate``      -- the correctness gate of that page (section "正确性判据",
                    the correctness criterion) with its conditioning check,
                    plus the constants it uses, fixed before any kernel ran.
 
-Parity status: every public function of ``golden`` is pinned by the
+Parity status: every public function of ``golden`` and ``layernorm`` is
+pinned (``tests/test_layernorm_oracle.py`` for the latter) by the
 ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py`` (printed worked
 examples, closed forms, invariants, central differences, and PyTorch's own
 ``rms_norm`` with autograd in float64).  ``reference`` is pinned against the
