@@ -26,6 +26,8 @@ __all__ = [
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_query_plan", "rmsnorm_fwd_strided",
     "rmsnorm_bwd_strided", "row_layout", "fwd", "bwd", "EXPORTED_SYMBOLS",
+    "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
+    "layernorm_bwd_rows", "layernorm_bwd_reduce", "ln_fwd", "ln_bwd", "LAYERNORM_MAX_N",
 ]
 
 RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
@@ -35,13 +37,17 @@ PASS_FWD, PASS_BWD_ROWS, PASS_BWD_REDUCE = 0, 1, 2
 KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
                 9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
-                13: "bwd_split", 14: "bwd_reduce_wide"}
+                13: "bwd_split", 14: "bwd_reduce_wide", 15: "ln_fwd",
+                16: "ln_bwd"}
+LAYERNORM_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_status_string", "rmsnorm_query_plan",
     "rmsnorm_fwd_strided", "rmsnorm_bwd_strided",
+    "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
+    "layernorm_bwd_rows", "layernorm_bwd_reduce",
 )
 
 _DTYPES = {torch.float32: RMSNORM_F32, torch.float16: RMSNORM_F16,
@@ -107,6 +113,20 @@ def load_library():
     lib.rmsnorm_bwd_strided.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, u32, vp, i64,
                                         vp, vp, sz, vp]
     lib.rmsnorm_bwd_strided.restype = i32
+    lib.layernorm_fwd.argtypes = [vp, i64, vp, vp, f32, i64, i64, i32, u32, vp, i64, vp, vp, vp]
+    lib.layernorm_fwd.restype = i32
+    lib.layernorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i32, u32, vp, i64,
+                                  vp, vp, vp, sz, vp]
+    lib.layernorm_bwd.restype = i32
+    lib.layernorm_bwd_workspace_bytes.argtypes = [i64, i64, i32, u32]
+    lib.layernorm_bwd_workspace_bytes.restype = sz
+    lib.layernorm_query_plan.argtypes = [i64, i64, i32, u32, i32, i32, ctypes.POINTER(Plan)]
+    lib.layernorm_query_plan.restype = i32
+    lib.layernorm_bwd_rows.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i32, u32, vp, i64,
+                                       vp, sz, vp]
+    lib.layernorm_bwd_rows.restype = i32
+    lib.layernorm_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp, vp]
+    lib.layernorm_bwd_reduce.restype = i32
     _LIB = lib
     return lib
 
@@ -316,3 +336,104 @@ def bwd(dy, x, gamma, rstd, offset=False, stream=None, poison=False, workspace=N
         workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
     rmsnorm_bwd_strided(dy, x, gamma, rstd, dx, dgamma, workspace, offset, stream)
     return dx, dgamma
+
+
+# ---- LayerNorm (include/layernorm.h) --------------------------------------------
+
+def _code(dtype):
+    return _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+
+
+def layernorm_query_plan(M, N, dtype, which=PASS_FWD, align_bytes=16, dgamma_in_dtype=False):
+    p = Plan()
+    _check("layernorm_query_plan", load_library().layernorm_query_plan(
+        int(M), int(N), _code(dtype), _flags(False, dgamma_in_dtype), int(which),
+        int(align_bytes), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def layernorm_bwd_workspace_bytes(M, N, dtype):
+    return int(load_library().layernorm_bwd_workspace_bytes(int(M), int(N), _code(dtype), 0))
+
+
+def layernorm_fwd(x, gamma, beta, eps, y, mean, rstd, stream=None):
+    """y, mean, rstd <- LayerNorm forward of x; beta may be None (no bias).
+    Row strides of x and y are taken from the tensors."""
+    m, n, ldx = _layout(x, "x")
+    _, _, ldy = _layout(y, "y")
+    _check("layernorm_fwd", load_library().layernorm_fwd(
+        _ptr(x), ldx, _ptr(gamma), _ptr(beta), float(eps), m, n, _dtype_code(x), 0,
+        _ptr(y), ldy, _ptr(mean), _ptr(rstd), _stream(x.device, stream)))
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream=None):
+    """dx, dgamma, dbeta <- LayerNorm backward; dbeta may be None.  dgamma and
+    dbeta are float32, or both of x's dtype."""
+    m, n, ldx = _layout(x, "x")
+    _, _, lddy = _layout(dy, "dy")
+    _, _, lddx = _layout(dx, "dx")
+    in_dtype = dgamma.dtype != torch.float32
+    _require(dbeta is None or dbeta.dtype == dgamma.dtype, "dgamma and dbeta must share a dtype")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("layernorm_bwd", load_library().layernorm_bwd(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(mean), _ptr(rstd), m, n,
+        _dtype_code(x), _flags(False, in_dtype), _ptr(dx), lddx, _ptr(dgamma), _ptr(dbeta),
+        _ptr(workspace), ws_bytes, _stream(x.device, stream)))
+
+
+def layernorm_bwd_rows(dy, x, gamma, mean, rstd, dx, workspace, stream=None):
+    m, n, ldx = _layout(x, "x")
+    _, _, lddy = _layout(dy, "dy")
+    _, _, lddx = _layout(dx, "dx")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("layernorm_bwd_rows", load_library().layernorm_bwd_rows(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(mean), _ptr(rstd), m, n,
+        _dtype_code(x), 0, _ptr(dx), lddx, _ptr(workspace), ws_bytes, _stream(x.device, stream)))
+
+
+def layernorm_bwd_reduce(workspace, M, N, dtype, dgamma, dbeta=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    in_dtype = dgamma.dtype != torch.float32
+    _check("layernorm_bwd_reduce", load_library().layernorm_bwd_reduce(
+        _ptr(workspace), ws_bytes, int(M), int(N), _code(dtype), _flags(False, in_dtype),
+        _ptr(dgamma), _ptr(dbeta), _stream(dgamma.device, stream)))
+
+
+def ln_fwd(x, gamma, beta=None, eps=1e-5, stream=None, poison=False):
+    """Returns ``(y, mean, rstd)``: y like x (dense rows), mean and rstd
+    float32 with one value per row."""
+    _check_inputs(x, gamma)
+    if beta is not None:
+        _require(beta.shape == gamma.shape and beta.dtype == x.dtype and beta.is_contiguous()
+                 and beta.device == x.device, "beta must be like gamma")
+    m, _, _ = row_layout(x)
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    y = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)
+    mean = fill((m,), float("nan"), device=x.device, dtype=torch.float32)
+    rstd = fill((m,), float("nan"), device=x.device, dtype=torch.float32)
+    layernorm_fwd(x, gamma, beta, eps, y, mean, rstd, stream)
+    return y, mean, rstd
+
+
+def ln_bwd(dy, x, gamma, mean, rstd, stream=None, poison=False, workspace=None,
+           dgamma_dtype=torch.float32, bias=True):
+    """Returns ``(dx, dgamma, dbeta)`` (dbeta None when ``bias`` is False)."""
+    _check_inputs(x, gamma)
+    _require(dy.shape == x.shape and dy.dtype == x.dtype and dy.device == x.device,
+             "dy must match x in shape, dtype and device")
+    if row_layout(dy) is None:
+        dy = dy.contiguous()
+    m, n, _ = row_layout(x)
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        _require(t.dtype == torch.float32 and t.numel() == m and t.is_contiguous(),
+                 f"{name} must be a contiguous float32 tensor with one value per row")
+    _require(dgamma_dtype in (torch.float32, x.dtype), "dgamma_dtype must be float32 or x's dtype")
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    dx = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)
+    dgamma = fill((n,), float("nan"), device=x.device, dtype=dgamma_dtype)
+    dbeta = fill((n,), float("nan"), device=x.device, dtype=dgamma_dtype) if bias else None
+    if workspace is None:
+        nbytes = layernorm_bwd_workspace_bytes(m, n, x.dtype)
+        workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
+    layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream)
+    return dx, dgamma, dbeta

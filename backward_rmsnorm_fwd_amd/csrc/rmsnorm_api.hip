@@ -17,6 +17,7 @@
 #include <cstring>
 #include <initializer_list>
 
+#include "../../include/layernorm.h"
 #include "../../include/rmsnorm.h"
 #include "rmsnorm_fast.hpp"
 #include "rmsnorm_fast_table.hpp"
@@ -332,28 +333,34 @@ int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
   return generic_bwd_partials(M, N, vec);
 }
 
+// Stage 2 over a [P, N] block of partial column sums.
+void fill_reduce_plan(int64_t P, int64_t N, rmsnorm_plan_t* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->partials = P;
+  p->vec = 1;
+  if (N % 4 == 0 && N <= 8192) {
+    p->kernel = RMSNORM_KERNEL_BWD_REDUCE16;
+    p->block_threads = 256;
+    p->grid = ceil_div(N, 16);
+  } else if (N % 4 == 0) {
+    // One wavefront slice per 4 partial rows, at most 16.
+    p->kernel = RMSNORM_KERNEL_BWD_REDUCE_WIDE;
+    p->block_threads = kWave * std::min(16, pow2_at_least(ceil_div(P, 4)));
+    p->grid = ceil_div(N, 256);
+  } else {
+    p->kernel = RMSNORM_KERNEL_BWD_REDUCE;
+    p->block_threads = 1024;
+    p->grid = ceil_div(N, kWave);
+  }
+}
+
 void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   const int es = elem_bytes(dtype);
   const int vec = pick_vec(N, es, align);
   const bool full = vec * es == 16;
   if (pass == RMSNORM_PASS_BWD_REDUCE) {
-    p->partials = bwd_partials(M, N, dtype);
-    if (N % 4 == 0 && N <= 8192) {
-      p->kernel = RMSNORM_KERNEL_BWD_REDUCE16;
-      p->block_threads = 256;
-      p->grid = ceil_div(N, 16);
-    } else if (N % 4 == 0) {
-      // One wavefront slice per 4 partial rows, at most 16.
-      p->kernel = RMSNORM_KERNEL_BWD_REDUCE_WIDE;
-      p->block_threads = kWave * std::min(16, pow2_at_least(ceil_div(p->partials, 4)));
-      p->grid = ceil_div(N, 256);
-    } else {
-      p->kernel = RMSNORM_KERNEL_BWD_REDUCE;
-      p->block_threads = 1024;
-      p->grid = ceil_div(N, kWave);
-    }
-    p->vec = 1;
+    fill_reduce_plan(bwd_partials(M, N, dtype), N, p);
     return;
   }
   p->vec = vec;
@@ -789,12 +796,23 @@ int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, co
   return status_of(e);
 }
 
+// Column sums of a [P, N] float32 partial block into dst (float32, or the
+// input dtype with RMSNORM_FLAG_DGAMMA_IN_DTYPE), with the stage-2 kernel
+// fill_plan picks for (P, N).
+int reduce_columns(const float* part, int64_t P, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
+                   void* dst, hipStream_t stream);
+
 // Stage 2 after its arguments were checked.
 int bwd_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                       uint32_t flags, void* dgamma, hipStream_t stream) {
+  return reduce_columns(static_cast<const float*>(workspace), bwd_partials(M, N, dtype), N, dtype,
+                        flags, dgamma, stream);
+}
+
+int reduce_columns(const float* part, int64_t P, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
+                   void* dgamma, hipStream_t stream) {
   rmsnorm_plan_t p;
-  fill_plan(M, N, dtype, RMSNORM_PASS_BWD_REDUCE, 16, &p);
-  const float* part = static_cast<const float*>(workspace);
+  fill_reduce_plan(P, N, &p);
   const int n = static_cast<int>(N);
   const int out = (flags & RMSNORM_FLAG_DGAMMA_IN_DTYPE) ? static_cast<int>(dtype) : kOutF32;
 #define RMSNORM_REDUCE(OUT)                                                                   \
@@ -838,6 +856,184 @@ int bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const voi
                        stream);
   if (st != RMSNORM_OK) return st;
   return bwd_reduce_launch(workspace, M, N, dtype, flags, dgamma, stream);
+}
+
+// ---- LayerNorm (layernorm.hip) ----------------------------------------------
+//
+// Row-resident plan: the row over `wpr` wavefronts of a 1024-thread
+// workgroup with at most 4 vectors (32 elements) per lane in the forward and
+// 16 elements (8 vectors) in the backward, whose two float32 column
+// accumulators per element are the register cost; rows of 16384 elements
+// with 2-byte accesses (odd N or misaligned 16-bit data) need 16 vectors per
+// lane over 16 wavefronts.  The backward's P (rows of each partial block) is a
+// function of (M, N, dtype): it is computed with the vector width N alone
+// allows, so pointer alignment changes only the kernel variant.
+constexpr int64_t kLnFwdWorkgroups = 512;
+constexpr int64_t kLnBwdWorkgroups = 256;
+
+LnPlan ln_plan(int64_t M, int64_t N, int es, bool backward, int align) {
+  LnPlan p{};
+  p.vec = pick_vec(N, es, align);
+  const int64_t nvec = N / p.vec;
+  const int target = backward ? std::max(1, std::min(8, 16 / p.vec))
+                              : std::max(1, std::min(4, 32 / p.vec));
+  p.wpr = std::min(16, pow2_at_least(ceil_div(nvec, int64_t(kWave) * target)));
+  p.chunks = static_cast<int>(ceil_div(nvec, int64_t(kWave) * p.wpr));
+  const int64_t G = ln_block_threads() / (kWave * p.wpr);
+  if (backward) {
+    p.lds = G > 1 ? int64_t(ln_block_threads()) * p.vec * 4 : 0;
+    const LnPlan base = p.vec == pick_vec(N, es, 16) ? p : ln_plan(M, N, es, true, 16);
+    const int64_t Gb = ln_block_threads() / (kWave * base.wpr);
+    p.grid = std::min(ceil_div(M, Gb), kLnBwdWorkgroups);
+  } else {
+    p.grid = std::min(ceil_div(M, G), kLnFwdWorkgroups);
+  }
+  return p;
+}
+
+int64_t ln_partials(int64_t M, int64_t N, int es) {
+  return M > 0 ? ln_plan(M, N, es, true, 16).grid : 0;
+}
+
+int check_ln_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
+  if (dtype != RMSNORM_F32 && dtype != RMSNORM_F16 && dtype != RMSNORM_BF16)
+    return RMSNORM_ERR_DTYPE;
+  if (flags & ~RMSNORM_FLAG_DGAMMA_IN_DTYPE) return RMSNORM_ERR_FLAGS;
+  if (N < 1 || N > LAYERNORM_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  return RMSNORM_OK;
+}
+
+int ln_fwd_impl(const void* x, int64_t ldx, const void* gamma, const void* beta, float eps,
+                int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y, int64_t ldy,
+                float* mean, float* rstd, hipStream_t stream) {
+  int st = check_ln_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_ERR_EPS;
+  if (bad_stride(ldx, N) || bad_stride(ldy, N)) return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!x || !gamma || !y || !mean || !rstd) return RMSNORM_ERR_NULL_POINTER;
+  const int es = elem_bytes(dtype);
+  if (misaligned(x, es) || misaligned(gamma, es) || misaligned(beta, es) ||
+      misaligned(y, es) || misaligned(mean, 4) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(y, M, ldy * es, N * es), vec(mean, M * 4), vec(rstd, M * 4)},
+                  {matrix(x, M, ldx * es, N * es), vec(gamma, N * es),
+                   vec(beta, beta ? N * es : 0)}))
+    return RMSNORM_ERR_OVERLAP;
+  const LnPlan p = ln_plan(M, N, es, false,
+                           layout_alignment({x, gamma, beta, y}, {ldx * es, ldy * es}));
+  const LnFwdArgs a{x, gamma, beta, y, mean, rstd, M, static_cast<int>(N), eps, ldx * es,
+                    ldy * es};
+  return status_of(ln_fwd_launch(dtype, p, a, stream));
+}
+
+size_t ln_workspace_bytes(int64_t M, int64_t N, int dtype) {
+  return static_cast<size_t>(2 * ln_partials(M, N, elem_bytes(dtype)) * N * 4);
+}
+
+// Stage-1 argument checks (dy, x, gamma, mean, rstd, dx, workspace).
+int check_ln_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                       const void* gamma, const float* mean, const float* rstd, int64_t M,
+                       int64_t N, int dtype, uint32_t flags, const void* dx, int64_t lddx,
+                       const void* workspace, size_t workspace_bytes) {
+  int st = check_ln_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (bad_stride(lddy, N) || bad_stride(ldx, N) || bad_stride(lddx, N)) return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!dy || !x || !gamma || !mean || !rstd || !dx) return RMSNORM_ERR_NULL_POINTER;
+  const int es = elem_bytes(dtype);
+  if (misaligned(dy, es) || misaligned(x, es) || misaligned(gamma, es) || misaligned(dx, es) ||
+      misaligned(mean, 4) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  const size_t need = ln_workspace_bytes(M, N, dtype);
+  if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
+                   vec(gamma, N * es), vec(mean, M * 4), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int ln_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+                   const float* mean, const float* rstd, int64_t M, int64_t N,
+                   rmsnorm_dtype_t dtype, void* dx, int64_t lddx, void* workspace,
+                   hipStream_t stream) {
+  if (M == 0) return RMSNORM_OK;
+  const int es = elem_bytes(dtype);
+  const LnPlan p = ln_plan(M, N, es, true,
+                           layout_alignment({dy, x, gamma, dx}, {lddy * es, ldx * es, lddx * es}));
+  const LnBwdArgs a{dy, x, gamma, mean, rstd, dx, static_cast<float*>(workspace), M,
+                    static_cast<int>(N), lddy * es, ldx * es, lddx * es};
+  return status_of(ln_bwd_launch(dtype, p, a, stream));
+}
+
+int ln_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                     uint32_t flags, void* dgamma, void* dbeta, hipStream_t stream) {
+  const int64_t P = ln_partials(M, N, elem_bytes(dtype));
+  const float* part = static_cast<const float*>(workspace);
+  int st = reduce_columns(part, P, N, dtype, flags, dgamma, stream);
+  if (st != RMSNORM_OK || !dbeta) return st;
+  return reduce_columns(M > 0 ? part + P * N : part, P, N, dtype, flags, dbeta, stream);
+}
+
+int check_ln_reduce_args(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                         int dtype, uint32_t flags, const void* dgamma, const void* dbeta) {
+  int st = check_ln_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!dgamma) return RMSNORM_ERR_NULL_POINTER;
+  const int gb = dgamma_elem_bytes(dtype, flags);
+  if (misaligned(dgamma, gb) || misaligned(dbeta, gb)) return RMSNORM_ERR_ALIGNMENT;
+  const size_t need = ln_workspace_bytes(M, N, dtype);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0)},
+                  {vec(workspace, static_cast<int64_t>(need))}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+                const float* mean, const float* rstd, int64_t M, int64_t N,
+                rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx, void* dgamma,
+                void* dbeta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_ln_rows_args(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, flags, dx, lddx,
+                              workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  st = check_ln_reduce_args(workspace, workspace_bytes, M, N, dtype, flags, dgamma, dbeta);
+  if (st != RMSNORM_OK) return st;
+  const int es = elem_bytes(dtype);
+  const int gb = dgamma_elem_bytes(dtype, flags);
+  const size_t need = ln_workspace_bytes(M, N, dtype);
+  if (any_overlap({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0),
+                   matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
+                   vec(gamma, N * es), vec(mean, M * 4), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  st = ln_rows_launch(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, dx, lddx, workspace,
+                      stream);
+  if (st != RMSNORM_OK) return st;
+  return ln_reduce_launch(workspace, M, N, dtype, flags, dgamma, dbeta, stream);
+}
+
+void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* out) {
+  std::memset(out, 0, sizeof(*out));
+  const int es = elem_bytes(dtype);
+  if (pass == RMSNORM_PASS_BWD_REDUCE) {
+    fill_reduce_plan(ln_partials(M, N, es), N, out);
+    return;
+  }
+  const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+  const LnPlan p = ln_plan(M, N, es, bwd, align);
+  out->kernel = bwd ? LAYERNORM_KERNEL_BWD : LAYERNORM_KERNEL_FWD;
+  out->vec = p.vec;
+  out->threads_per_row = kWave * p.wpr;
+  out->block_threads = ln_block_threads();
+  out->chunks = p.chunks;
+  out->weight_in_regs = 1;
+  out->grid = p.grid;
+  out->partials = bwd ? p.grid : 0;
+  out->lds_bytes = bwd ? p.lds : 0;
 }
 
 }  // namespace
@@ -933,6 +1129,58 @@ int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x, int64_t ldx
                         hipStream_t stream) {
   return bwd_impl(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, flags, dx, lddx, dgamma,
                   workspace, workspace_bytes, stream);
+}
+
+int layernorm_fwd(const void* x, int64_t ldx, const void* gamma, const void* beta, float eps,
+                  int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y,
+                  int64_t ldy, float* mean, float* rstd, hipStream_t stream) {
+  return ln_fwd_impl(x, ldx, gamma, beta, eps, M, N, dtype, flags, y, ldy, mean, rstd, stream);
+}
+
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                                     uint32_t flags) {
+  if (check_ln_common(M, N, dtype, flags) != RMSNORM_OK || M == 0) return 0;
+  return ln_workspace_bytes(M, N, dtype);
+}
+
+int layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+                  const float* mean, const float* rstd, int64_t M, int64_t N,
+                  rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx, void* dgamma,
+                  void* dbeta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ln_bwd_impl(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, flags, dx, lddx, dgamma,
+                     dbeta, workspace, workspace_bytes, stream);
+}
+
+int layernorm_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                       const void* gamma, const float* mean, const float* rstd, int64_t M,
+                       int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_ln_rows_args(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, flags, dx,
+                                    lddx, workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  return ln_rows_launch(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, dx, lddx, workspace,
+                        stream);
+}
+
+int layernorm_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                         rmsnorm_dtype_t dtype, uint32_t flags, void* dgamma, void* dbeta,
+                         hipStream_t stream) {
+  const int st = check_ln_reduce_args(workspace, workspace_bytes, M, N, dtype, flags, dgamma,
+                                      dbeta);
+  if (st != RMSNORM_OK) return st;
+  return ln_reduce_launch(workspace, M, N, dtype, flags, dgamma, dbeta, stream);
+}
+
+int layernorm_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, int pass,
+                         int align_bytes, rmsnorm_plan_t* plan) {
+  const int st = check_ln_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!plan) return RMSNORM_ERR_NULL_POINTER;
+  if (pass < RMSNORM_PASS_FWD || pass > RMSNORM_PASS_BWD_REDUCE) return RMSNORM_ERR_ARGUMENT;
+  if (align_bytes < 1 || align_bytes > 4096 || (align_bytes & (align_bytes - 1)))
+    return RMSNORM_ERR_ARGUMENT;
+  fill_ln_plan(M, N, dtype, pass, std::min(align_bytes, 16), plan);
+  return RMSNORM_OK;
 }
 
 }  // extern "C"

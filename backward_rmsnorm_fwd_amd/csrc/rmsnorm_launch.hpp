@@ -97,4 +97,48 @@ hipError_t split_fwd_launch(int dtype, const SplitPlan& sp, const FastFwdArgs& a
 hipError_t split_bwd_launch(int dtype, const SplitPlan& sp, const FastBwdArgs& a, float* dotp,
                             float* coef, hipStream_t s);
 
+// LayerNorm (layernorm.hip): row-resident kernels, `wpr` wavefronts per row,
+// `chunks` vector accesses of `vec` elements per lane, 1024-thread
+// workgroups.  Backward: grid = P row blocks, `lds` bytes for the combine.
+struct LnPlan {
+  int vec;
+  int wpr;
+  int chunks;
+  int64_t grid;
+  int64_t lds;
+};
+
+struct LnFwdArgs {
+  const void* x;
+  const void* gamma;
+  const void* beta;  // may be null: no bias
+  void* y;
+  float* mean;
+  float* rstd;
+  int64_t M;
+  int N;
+  float eps;
+  int64_t x_pitch;  // bytes between row starts
+  int64_t y_pitch;
+};
+
+struct LnBwdArgs {
+  const void* dy;
+  const void* x;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  float* part;  // [2, P, N]: dgamma partials, then dbeta partials
+  int64_t M;
+  int N;
+  int64_t dy_pitch;
+  int64_t x_pitch;
+  int64_t dx_pitch;
+};
+
+int ln_block_threads();
+hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
+hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
+
 }  // namespace rmsnorm_hip

@@ -16,6 +16,13 @@ timed steps.  A cold-cache figure (each call preceded by a 1 GiB read that
 evicts L2 and the 256 MB Infinity Cache) is reported beside it, a 1 GiB
 device copy as an achievable-bandwidth reference, and the CPU oracle's
 throughput on the same workload as ``cpu_baseline``.
+
+``--op layernorm`` measures the LayerNorm path of the same library instead
+(layernorm_fwd, layernorm_bwd_rows, layernorm_bwd_reduce) on the LayerNorm
+inputs of the workload (the same x, gamma and dy draws plus a bias and
+per-row mean shifts).  Algorithmic bytes: forward 2*M*N*s + 2*N*s + 8*M
+(x, gamma, beta read; y, mean, rstd written), backward stage 1
+3*M*N*s + N*s + 8*M, stage 2 8*N (dgamma and dbeta).
 """
 import argparse
 import hashlib
@@ -64,7 +71,9 @@ def measured_traffic(workload):
         return None
 
 
-def alg_bytes(M, N, s):
+def alg_bytes(M, N, s, op="rmsnorm"):
+    if op == "layernorm":
+        return 2 * M * N * s + 2 * N * s + 8 * M, 3 * M * N * s + N * s + 8 * M, 8 * N
     fwd = 2 * M * N * s + N * s + 4 * M
     bwd_rows = 3 * M * N * s + N * s + 4 * M
     bwd_reduce = 4 * N
@@ -79,6 +88,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
+    ap.add_argument("--op", choices=("rmsnorm", "layernorm"), default="rmsnorm")
     ap.add_argument("--cold-samples", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1 << 62,
@@ -103,7 +113,8 @@ def main():
     rn.load_library()
     wl = workloads.WORKLOADS[args.workload]
     t0 = time.time()
-    inp = workloads.make_inputs(args.workload)
+    ln = args.op == "layernorm"
+    inp = (workloads.make_layernorm_inputs if ln else workloads.make_inputs)(args.workload)
     M, N, T, off, eps = inp["M"], inp["N"], inp["dtype"], inp["offset"], inp["eps"]
     s = torch.tensor([], dtype=T).element_size()
     x, w, dy = (inp[k].to(dev) for k in ("x", "w", "dy"))
@@ -111,19 +122,35 @@ def main():
     rstd = torch.empty(M, device=dev, dtype=torch.float32)
     dx = torch.empty_like(x)
     dgamma = torch.empty(N, device=dev, dtype=torch.float32)
-    ws = torch.empty(max(4, rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)) // 4,
-                     device=dev, dtype=torch.float32)
+    if ln:
+        bias = inp["b"].to(dev)
+        mean = torch.empty(M, device=dev, dtype=torch.float32)
+        dbeta = torch.empty(N, device=dev, dtype=torch.float32)
+        nbytes = rn.layernorm_bwd_workspace_bytes(M, N, T)
+    else:
+        nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)
+    ws = torch.empty(max(4, nbytes) // 4, device=dev, dtype=torch.float32)
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    def fwd():
-        rn.rmsnorm_fwd(x, w, eps, y, rstd, off)
+    if ln:
+        def fwd():
+            rn.layernorm_fwd(x, w, bias, eps, y, mean, rstd)
 
-    def bwd_rows():
-        rn.rmsnorm_bwd_rows(dy, x, w, rstd, dx, ws, off)
+        def bwd_rows():
+            rn.layernorm_bwd_rows(dy, x, w, mean, rstd, dx, ws)
 
-    def bwd_reduce():
-        rn.rmsnorm_bwd_reduce(ws, M, N, T, dgamma, off)
+        def bwd_reduce():
+            rn.layernorm_bwd_reduce(ws, M, N, T, dgamma, dbeta)
+    else:
+        def fwd():
+            rn.rmsnorm_fwd(x, w, eps, y, rstd, off)
+
+        def bwd_rows():
+            rn.rmsnorm_bwd_rows(dy, x, w, rstd, dx, ws, off)
+
+        def bwd_reduce():
+            rn.rmsnorm_bwd_reduce(ws, M, N, T, dgamma, off)
 
     stages = [("fwd", fwd), ("bwd_rows", bwd_rows), ("bwd_reduce", bwd_reduce)]
     for _ in range(args.warmup):
@@ -173,7 +200,7 @@ def main():
         torch.cuda.synchronize()
         per_kernel_us[k] = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
 
-    fb, rb, db = alg_bytes(M, N, s)
+    fb, rb, db = alg_bytes(M, N, s, args.op)
     step_bytes = fb + rb + db
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = rb / (dominant_us * 1e-6) / 1e9
@@ -226,6 +253,7 @@ def main():
     cpu_baseline = None
     if not args.no_cpu_baseline:
         from oracle import golden
+        from oracle import layernorm as ln_oracle
         R = min(args.cpu_rows, M)
         xs, dys = inp["x"][:R], inp["dy"][:R]
         nthreads = torch.get_num_threads()
@@ -233,13 +261,18 @@ def main():
         times = []
         for _ in range(3):
             t = time.perf_counter()
-            golden.golden_forward(xs, inp["w"], eps, off)
-            golden.golden_dx(dys, xs, inp["w"], eps, off)
-            golden.golden_dgamma(dys, xs, eps)
+            if ln:
+                ln_oracle.golden_ln_forward(xs, inp["w"], inp["b"], eps)
+                ln_oracle.golden_ln_dx(dys, xs, inp["w"], eps)
+                ln_oracle.golden_ln_param_grads(dys, xs, eps)
+            else:
+                golden.golden_forward(xs, inp["w"], eps, off)
+                golden.golden_dx(dys, xs, inp["w"], eps, off)
+                golden.golden_dgamma(dys, xs, eps)
             times.append(time.perf_counter() - t)
         torch.set_num_threads(nthreads)
         cpu_s = statistics.median(times)
-        sb = sum(alg_bytes(R, N, s))
+        sb = sum(alg_bytes(R, N, s, args.op))
         cpu_baseline = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
                         "kind": "oracle",
                         "sample": f"float64 NumPy golden forward+backward over {R} of {M} rows "
@@ -248,7 +281,8 @@ def main():
                         "host_cores_available": len(os.sched_getaffinity(0))}
 
     result = {
-        "metric": "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
+        "metric": ("LayerNorm" if ln else "RMSNorm")
+        + " fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -260,7 +294,8 @@ def main():
         "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[T],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {wl.description}", "M": M, "N": N,
+        "config": {"workload": f"{args.workload}: {wl.description}"
+                   + (" (LayerNorm inputs)" if ln else ""), "op": args.op, "M": M, "N": N,
                    "eps": eps, "offset_weight": off, "seed": inp["seed"],
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 1),
@@ -273,10 +308,11 @@ def main():
                                             + per_kernel_us["bwd_reduce"]) * 1e-6) / 1e9, 1)},
         "cold_cache": cold,
         "device_copy_GBps": round(copy_gbs, 1),
-        "roofline": {"kernel": "bwd_rows", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "ln_bwd_rows" if ln else "bwd_rows", "bound": "hbm",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": None if ln else measured_traffic(args.workload),
                      "alg_bytes_per_launch": rb},
         "cpu_baseline": cpu_baseline,
     }

@@ -234,6 +234,40 @@ def gate_rstd(target_rstd, golden_r, reference_rstd=None,
     return row
 
 
+# LayerNorm row statistics.  A row's mean and inverse standard deviation are
+# each one sum over the row, so comparing two float32 evaluations of them
+# compares rounding luck, not correctness: they are checked against the
+# float64 golden with fixed bounds instead.  The mean: one float32 unit in the
+# last place of the exact mean plus 2^-36 of the row's largest |x| (room for
+# the rounding of a float64 accumulation over up to 2^14 terms).  rstd: the
+# RMSNorm bound, RSTD_MAX_REL_ERROR relative.
+MEAN_ROW_ABS_SLACK = 2.0 ** -36
+
+
+def gate_mean(target_mean, golden_mean, row_absmax):
+    """|mean_i - mu_i| <= 2^-23 |mu_i| + 2^-36 max_j |x_ij| for every row."""
+    g = np.asarray(golden_mean, dtype=np.float64).ravel()
+    a = np.asarray(row_absmax, dtype=np.float64).ravel()
+    row = GateRow(tensor="mean", dtype="float32", shape=tuple(g.shape))
+    why = structure_mismatch(np.asarray(_to_f64(target_mean)).ravel(), g)
+    if why is None and _dtype_name(target_mean) != "float32":
+        why = f"dtype {_dtype_name(target_mean)} != expected float32"
+    if why is not None:
+        row.verdict, row.note = "FAIL", "structure: " + why
+        return row
+    t = _to_f64(target_mean).ravel()
+    bound = 2.0 ** -23 * np.abs(g) + MEAN_ROW_ABS_SLACK * a
+    err = np.abs(t - g)
+    row.target_error = float(np.max(err)) if g.size else 0.0
+    row.threshold = float(np.max(err / np.where(bound > 0, bound, 1.0))) if g.size else 0.0
+    row.absolute_floor = 0.0
+    row.golden_scale = float(np.max(np.abs(g))) if g.size else 0.0
+    row.gate_valid = True
+    row.verdict = "PASS" if bool(np.all(err <= bound)) else "FAIL"
+    row.note = "per-row bound 2^-23|mu| + 2^-36 max|x| (threshold column: worst error/bound)"
+    return row
+
+
 def overall_verdict(rows):
     verdicts = [r.verdict for r in rows]
     if any(v == "FAIL" for v in verdicts):

@@ -9,6 +9,7 @@ import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from oracle import gate, golden, reference
+from oracle import layernorm as lnref
 
 
 def log(msg):
@@ -95,3 +96,65 @@ def assert_pass(rows, title):
     text = gate.report(rows, title)
     log(text)
     assert gate.overall_verdict(rows) == "PASS", text
+
+
+# ---- LayerNorm ------------------------------------------------------------------
+
+def run_ln_target(inp, device, poison=True, bias=True):
+    """LayerNorm forward + backward on the GPU (outputs pre-poisoned with NaN)."""
+    x = inp["x"].to(device)
+    w = inp["w"].to(device)
+    b = inp["b"].to(device) if bias else None
+    dy = inp["dy"].to(device)
+    y, mean, rstd = rn.ln_fwd(x, w, b, inp["eps"], poison=poison)
+    dx, dg, db = rn.ln_bwd(dy, x, w, mean, rstd, poison=poison, bias=bias)
+    torch.cuda.synchronize()
+    return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
+
+
+def gate_ln_full(inp, out, bias=True):
+    """Gate every element of y, mean, rstd, dx, dgamma and dbeta."""
+    x, w, dy, eps, T = inp["x"], inp["w"], inp["dy"], inp["eps"], inp["x"].dtype
+    b = inp["b"] if bias else None
+    n = x.shape[-1]
+    y_r, mu_r, r_r = lnref.reference_ln_forward(x, w, b, eps)
+    dx_r, dg_r, db_r = lnref.reference_ln_backward(dy, x, w, eps)
+    y_g, mu_g, r_g = lnref.golden_ln_forward(x, w, b, eps)
+    dx_g, dg_g, db_g = lnref.golden_ln_backward(dy, x, w, eps)
+    worst = int(np.argmax(np.abs(out["dgamma"].double().cpu().numpy() - dg_g))) if n else 0
+    cg, cb = lnref.ln_param_condition(dy, x, eps, worst) if x.numel() else (None, None)
+    rows = [
+        gate.gate_tensor("y", out["y"].cpu().reshape(-1, n), y_r, y_g, T),
+        gate.gate_mean(out["mean"].cpu(), mu_g, x.reshape(-1, n).abs().amax(1).double()
+                       if x.numel() else np.zeros(0)),
+        gate.gate_rstd(out["rstd"].cpu(), r_g, r_r),
+        gate.gate_tensor("dx", out["dx"].cpu().reshape(-1, n), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32, condition=cg),
+    ]
+    if out.get("dbeta") is not None:
+        rows.append(gate.gate_tensor("dbeta", out["dbeta"].cpu(), db_r, db_g, torch.float32))
+    return rows
+
+
+def gate_ln_sampled(inp, out, rows, cols):
+    """Sampled rows of y, mean, rstd, dx; sampled columns of dgamma and dbeta
+    (still sums over all M rows)."""
+    x, w, b, dy, eps, T = inp["x"], inp["w"], inp["b"], inp["dy"], inp["eps"], inp["x"].dtype
+    rt = torch.as_tensor(rows, dtype=torch.long)
+    xs, dys = x[rt], dy[rt]
+    y_r, mu_r, r_r = lnref.reference_ln_forward(xs, w, b, eps)
+    dx_r, _, _ = lnref.reference_ln_backward(dys, xs, w, eps)
+    y_g, mu_g, r_g = lnref.golden_ln_forward(xs, w, b, eps)
+    dx_g = lnref.golden_ln_dx(dys, xs, w, eps)
+    dg_g, db_g = lnref.golden_ln_param_grads(dy, x, eps, cols=cols)
+    dg_r, db_r = lnref.reference_ln_param_grads(dy, x, eps, cols=cols)
+    dr = rt.to(out["y"].device)
+    dc = torch.as_tensor(cols, dtype=torch.long, device=out["y"].device)
+    return [
+        gate.gate_tensor("y[rows]", out["y"][dr].cpu(), y_r, y_g, T),
+        gate.gate_mean(out["mean"][dr].cpu(), mu_g, xs.abs().amax(1).double()),
+        gate.gate_rstd(out["rstd"][dr].cpu(), r_g, r_r),
+        gate.gate_tensor("dx[rows]", out["dx"][dr].cpu(), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma[cols]", out["dgamma"][dc].cpu(), dg_r, dg_g, torch.float32),
+        gate.gate_tensor("dbeta[cols]", out["dbeta"][dc].cpu(), db_r, db_g, torch.float32),
+    ]

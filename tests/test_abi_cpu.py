@@ -8,6 +8,7 @@ calculation before accelerating it", section "The memory contract is part of
 the computation" (reject before writing), with the domain of include/rmsnorm.h.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -16,7 +17,7 @@ import pytest
 import backward_rmsnorm_fwd_amd as rn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rmsnorm.h", "layernorm.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(rn.library_path()),
                                 reason="librmsnorm.so not built")
@@ -31,9 +32,13 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(rmsnorm_\w+)\(",
+    text = "".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+((?:rmsnorm|layernorm)_\w+)\(",
                                  text, re.M)))
+
+
+def test_every_header_is_scanned():
+    assert sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) == sorted(HEADERS)
 
 
 def test_header_declares_what_the_binding_knows():

@@ -190,3 +190,22 @@ def test_report_layout():
     text = gate.report(rows, "c1b")
     assert "| Tensor | Ref/golden | Condition | Target error | Threshold | Gate valid | Verdict |" in text
     assert "Overall: **PASS**" in text
+
+
+def test_gate_mean_bounds():
+    """The LayerNorm mean check: a correctly rounded float32 mean passes, one
+    four float32 ulps away fails; a zero mean is held to the 2^-36 max|x|
+    slack only."""
+    g = np.array([1.0 / 3.0, -12.5 + 1e-9, 0.0])
+    absmax = np.array([2.0, 20.0, 1.0])
+    t = torch.tensor(g, dtype=torch.float32)
+    assert gate.gate_mean(t, g, absmax).verdict == "PASS"
+    bad = t.clone()
+    bad[0] = float(np.float32(g[0]) + 4 * np.spacing(np.float32(g[0])))
+    assert gate.gate_mean(bad, g, absmax).verdict == "FAIL"
+    bad = t.clone()
+    bad[2] = 2.0 ** -30
+    assert gate.gate_mean(bad, g, absmax).verdict == "FAIL"
+    bad[2] = 2.0 ** -38
+    assert gate.gate_mean(bad, g, absmax).verdict == "PASS"
+    assert gate.gate_mean(t.double(), g, absmax).verdict == "FAIL"  # must be float32

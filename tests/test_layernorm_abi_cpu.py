@@ -1,0 +1,131 @@
+"""LayerNorm entry points (include/layernorm.h) on the host: argument checks
+and launch plans, no device work.  Every call below is invalid in exactly
+one way, so nothing is ever launched on the fake addresses."""
+import ctypes
+
+import pytest
+
+import backward_rmsnorm_fwd_amd as rn
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(rn.library_path()),
+                                reason="librmsnorm.so not built")
+
+OK, ENULL, EDTYPE, ESHAPE, EEPS, EFLAGS, EWS, EALIGN, EOVL = 0, -1, -2, -3, -4, -5, -6, -7, -8
+EARG, ESTRIDE = -10, -11
+A = 0x10000000  # fake, 16-byte aligned "device" addresses; never dereferenced
+S = 1 << 24     # spacing between the fake buffers
+
+
+def lib():
+    return rn.load_library()
+
+
+def fwd_call(x=A, ldx=None, g=A + S, b=A + 2 * S, eps=1e-5, M=4, N=256, dtype=2, flags=0,
+             y=A + 3 * S, ldy=None, mean=A + 4 * S, rstd=A + 5 * S):
+    ldx = N if ldx is None else ldx
+    ldy = N if ldy is None else ldy
+    return lib().layernorm_fwd(x, ldx, g, b, eps, M, N, dtype, flags, y, ldy, mean, rstd, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 3}, EDTYPE), ({"flags": 1}, EFLAGS), ({"flags": 4}, EFLAGS),
+    ({"N": 0}, ESHAPE), ({"N": 16385}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"eps": 0.0}, EEPS), ({"eps": float("nan")}, EEPS),
+    ({"ldx": 255}, ESTRIDE), ({"ldy": 100}, ESTRIDE),
+    ({"x": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL),
+    ({"mean": None}, ENULL), ({"rstd": None}, ENULL),
+    ({"x": A + 1}, EALIGN), ({"b": A + 2 * S + 1}, EALIGN), ({"mean": A + 4 * S + 2}, EALIGN),
+    ({"y": A + 64}, EOVL),                  # y overlaps x
+    ({"mean": A + S + 8}, EOVL),            # mean overlaps gamma
+    ({"rstd": A + 2 * S + 4}, EOVL),        # rstd overlaps beta
+    ({"rstd": A + 4 * S + 8}, EOVL),        # rstd overlaps mean
+])
+def test_fwd_rejects(kw, code):
+    assert fwd_call(**kw) == code
+
+
+def test_fwd_m0_is_a_noop():
+    assert fwd_call(M=0, x=None, g=None, b=None, y=None, mean=None, rstd=None) == OK
+
+
+def bwd_call(dy=A, x=A + S, g=A + 2 * S, mean=A + 3 * S, rstd=A + 4 * S, M=4, N=256,
+             dtype=2, flags=0, dx=A + 5 * S, dg=A + 6 * S, db=A + 7 * S, ws=A + 8 * S,
+             ws_bytes=None, lddy=None, ldx=None, lddx=None):
+    if ws_bytes is None:
+        ws_bytes = lib().layernorm_bwd_workspace_bytes(M, N, dtype, flags)
+    lddy = N if lddy is None else lddy
+    ldx = N if ldx is None else ldx
+    lddx = N if lddx is None else lddx
+    return lib().layernorm_bwd(dy, lddy, x, ldx, g, mean, rstd, M, N, dtype, flags, dx, lddx,
+                               dg, db, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 5}, EDTYPE), ({"flags": 1}, EFLAGS), ({"N": 20000}, ESHAPE),
+    ({"lddx": 3}, ESTRIDE),
+    ({"dy": None}, ENULL), ({"x": None}, ENULL), ({"g": None}, ENULL), ({"mean": None}, ENULL),
+    ({"rstd": None}, ENULL), ({"dx": None}, ENULL), ({"dg": None}, ENULL),
+    ({"ws": None}, EWS), ({"ws_bytes": 16}, EWS),
+    ({"ws": A + 8 * S + 4}, EALIGN), ({"dy": A + 1}, EALIGN), ({"db": A + 7 * S + 2}, EALIGN),
+    ({"dx": A + 16}, EOVL),                 # dx overlaps dy
+    ({"dg": A + 3 * S + 4}, EOVL),          # dgamma overlaps mean
+    ({"db": A + 6 * S + 8}, EOVL),          # dbeta overlaps dgamma
+    ({"ws": A + 5 * S + 256}, EOVL),        # workspace overlaps dx
+])
+def test_bwd_rejects(kw, code):
+    assert bwd_call(**kw) == code
+
+
+def test_bwd_m0_still_needs_dgamma():
+    assert bwd_call(M=0, dg=None, dy=None, x=None, g=None, mean=None, rstd=None, dx=None,
+                    ws=None) == ENULL
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_plans_cover_rows(dt):
+    """Every N gets a plan whose lanes cover the row with no empty chunk,
+    within the register-slot caps, in 1024-thread workgroups; P does not
+    depend on alignment; the workspace holds two [P, N] blocks."""
+    es = 4 if dt == 0 else 2
+    for n in list(range(1, 130)) + [255, 256, 257, 1000, 1024, 4095, 4096, 4097, 5120, 8191,
+                                    8192, 8193, 12288, 16383, 16384]:
+        for m in (1, 7, 1000, 262144):
+            P = None
+            for align in (16, 8, 4, 2):
+                if es == 4 and align < 4:
+                    continue
+                for which, target in ((rn.PASS_FWD, lambda v: min(4, 32 // v)),
+                                      (rn.PASS_BWD_ROWS, lambda v: min(8, 16 // v))):
+                    p = rn.layernorm_query_plan(m, n, dt, which=which, align_bytes=align)
+                    assert p["kernel_name"] == ("ln_fwd" if which == rn.PASS_FWD else "ln_bwd")
+                    vec, tpr, ch = p["vec"], p["threads_per_row"], p["chunks"]
+                    assert n % vec == 0 and vec * es <= align
+                    assert tpr * ch * vec >= n > tpr * (ch - 1) * vec
+                    assert p["block_threads"] == 1024 and 64 <= tpr <= 1024
+                    cap = max(target(vec), 16 // vec)
+                    assert ch <= cap
+                    if which == rn.PASS_BWD_ROWS:
+                        if P is None:
+                            P = p["partials"]
+                        assert p["partials"] == P == p["grid"]
+                        assert p["lds_bytes"] == (0 if tpr == 1024 else 1024 * vec * 4)
+            assert P == min(256, _ceil(m, 1024 // rn.layernorm_query_plan(
+                m, n, dt, which=rn.PASS_BWD_ROWS)["threads_per_row"]))
+            assert rn.layernorm_bwd_workspace_bytes(m, n, dt) == 2 * P * n * 4
+            red = rn.layernorm_query_plan(m, n, dt, which=rn.PASS_BWD_REDUCE)
+            assert red["partials"] == P
+
+
+def test_query_plan_rejects():
+    L = lib()
+    p = rn.Plan()
+    assert L.layernorm_query_plan(4, 256, 2, 0, 7, 16, ctypes.byref(p)) == EARG
+    assert L.layernorm_query_plan(4, 256, 2, 1, 0, 16, ctypes.byref(p)) == EFLAGS
+    assert L.layernorm_query_plan(4, 16385, 2, 0, 0, 16, ctypes.byref(p)) == ESHAPE
+    assert L.layernorm_query_plan(4, 256, 2, 0, 0, 16, None) == ENULL
+    assert rn.layernorm_bwd_workspace_bytes(0, 256, 2) == 0
+    assert rn.layernorm_bwd_workspace_bytes(4, 16385, 2) == 0

@@ -1,0 +1,184 @@
+"""LayerNorm on the GPU through the C ABI (include/layernorm.h), gated
+against the LayerNorm oracle (oracle.layernorm): every element of y, mean,
+rstd, dx, dgamma and dbeta at reduced sizes of each recipe, tile-boundary
+and degenerate rows, misaligned and strided layouts, and the c2 and c3
+shapes at full size on sampled rows and columns."""
+import numpy as np
+import pytest
+import torch
+
+import backward_rmsnorm_fwd_amd as rn
+from backward_rmsnorm_fwd_amd import workloads
+from parity import (assert_pass, gate_ln_full, gate_ln_sampled, log, run_ln_target,
+                    sample_cols, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1a", "c1b", "c1c"])
+def test_small_workloads(cuda, name):
+    inp = workloads.make_layernorm_inputs(name)
+    log(f"case ln {name} M={inp['M']} N={inp['N']}")
+    assert_pass(gate_ln_full(inp, run_ln_target(inp, cuda)), f"ln {name}")
+
+
+def test_two_value_closed_form(cuda):
+    """x = [3, 4], gamma = [2, 0.5], beta = [0.5, -0.25]: mean 3.5, variance
+    1/4, so y = [-r + 0.5, r/4 - 0.25] with r = 1/sqrt(1/4 + eps)."""
+    out = run_ln_target(workloads.make_layernorm_inputs("c1c"), cuda)
+    r = 1.0 / np.sqrt(0.25 + 1e-6)
+    assert np.allclose(out["y"].cpu().numpy(), [[-r + 0.5, 0.25 * r - 0.25]], rtol=1e-6)
+    assert out["mean"].item() == 3.5
+    assert np.isclose(out["rstd"].item(), r, rtol=1e-6)
+
+
+SCALED = [("c2", 2051, 4096), ("c2", 517, 4104), ("c3", 3001, 1000), ("c3", 20011, 1024),
+          ("c5", 1031, 5120), ("c5", 301, 5112), ("c4", 37, 16384), ("c4", 9, 16376)]
+
+
+@pytest.mark.parametrize("name,M,N", SCALED)
+def test_scaled_recipes(cuda, name, M, N):
+    inp = workloads.make_layernorm_inputs(name, M=M, N=N)
+    log(f"case ln {name} recipe at M={M} N={N}")
+    assert_pass(gate_ln_full(inp, run_ln_target(inp, cuda)), f"ln {name} @ {M}x{N}")
+
+
+TILES = [((3, 1), torch.float32), ((3, 255), torch.float32),
+         ((3, 256), torch.bfloat16), ((3, 257), torch.float16), ((8, 6, 256), torch.bfloat16),
+         ((8, 4095), torch.bfloat16), ((8, 4097), torch.float16), ((37, 2048), torch.float32),
+         ((7, 8191), torch.float32), ((7, 8193), torch.bfloat16), ((5, 12288), torch.float16),
+         ((4, 16383), torch.float16), ((4, 16384), torch.float32), ((3, 16383), torch.float32)]
+
+
+@pytest.mark.parametrize("shape,dtype", TILES)
+def test_tile_shapes(cuda, shape, dtype):
+    inp = workloads.make_layernorm_tile_case(shape, dtype, 31 + shape[-1] % 97)
+    log(f"case ln tile {shape} {dtype}")
+    assert_pass(gate_ln_full(inp, run_ln_target(inp, cuda)), f"ln tile {shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_two_element_rows(cuda, dtype):
+    """N = 2: xhat = +-1 up to eps, and dx = r*(u - mean(u))*eps/(var + eps)
+    is what is left after terms of size up to T = r*max|u| cancel (golden
+    row 0 of seed 33: 1e-7 against T ~ 1).  Every intermediate of the general
+    formula (u, mean(u), xhat*mean(u*xhat)) is at most T in size, so any
+    float32 evaluation carries about ten float32 roundings of T; the
+    same-precision reference is no yardstick for dx here.  dx is checked
+    against the float64 golden within 16 float32 ulps of T plus the output's
+    rounding.  y, mean, rstd, dgamma and dbeta go through the gate."""
+    inp = workloads.make_layernorm_tile_case((64, 2), dtype, 33)
+    out = run_ln_target(inp, cuda)
+    rows = gate_ln_full(inp, out)
+    assert_pass([r for r in rows if r.tensor != "dx"], f"ln N=2 {dtype} (all but dx)")
+    from oracle import layernorm as lnref
+    dx_g = lnref.golden_ln_dx(inp["dy"], inp["x"], inp["w"], inp["eps"])
+    xg = inp["x"].double().numpy()
+    u = inp["dy"].double().numpy() * inp["w"].double().numpy()
+    r = 1.0 / np.sqrt(((xg - xg.mean(1, keepdims=True)) ** 2).mean(1) + inp["eps"])
+    T = r * np.abs(u).max(1)
+    ulp_out = {torch.bfloat16: 2.0 ** -8, torch.float32: 2.0 ** -24}[dtype]
+    bound = 16 * 2.0 ** -24 * T[:, None] + ulp_out * np.abs(dx_g)
+    err = np.abs(out["dx"].double().cpu().numpy() - dx_g)
+    log(f"N=2 dx: max err {err.max():.3e}, max err/bound {(err / bound).max():.3f}")
+    assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("scale,shift,dtype", [(1e-3, 50.0, torch.float32),
+                                               (1e-2, 8.0, torch.float16),
+                                               (0.0, 3.0, torch.bfloat16),
+                                               (0.0, 0.0, torch.float32)])
+def test_degenerate_rows(cuda, scale, shift, dtype):
+    """Rows whose spread is tiny against their mean (the variance comes from
+    a cancelling difference), and constant rows (zero variance: y = beta)."""
+    inp = workloads.make_layernorm_tile_case((16, 5120), dtype, 41, scale=scale, shift_std=shift)
+    log(f"case ln degenerate scale={scale} shift={shift} {dtype}")
+    out = run_ln_target(inp, cuda)
+    assert_pass(gate_ln_full(inp, out), f"ln degenerate {scale} {shift} {dtype}")
+    if scale == 0.0:
+        assert torch.equal(out["y"].cpu(), inp["b"].expand(16, 5120))
+
+
+def test_no_bias(cuda):
+    inp = workloads.make_layernorm_inputs("c2", M=300, N=4096)
+    out = run_ln_target(inp, cuda, bias=False)
+    assert out["dbeta"] is None
+    assert_pass(gate_ln_full(inp, out, bias=False), "ln without bias")
+
+
+@pytest.mark.parametrize("name,M,N", [("c2", None, None), ("c3", None, None)])
+def test_full_size_sampled(cuda, name, M, N):
+    inp = workloads.make_layernorm_inputs(name, M=M, N=N)
+    log(f"case ln {name} full size M={inp['M']} N={inp['N']} generated")
+    out = run_ln_target(inp, cuda)
+    log(f"case ln {name} device run done")
+    rows = sample_rows(inp, 2048)
+    cols = sample_cols(inp["N"], 64)
+    assert_pass(gate_ln_sampled(inp, out, rows, cols), f"ln {name} full size, sampled")
+    for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
+        assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
+def test_reproducible_and_dgamma_in_dtype(cuda):
+    inp = workloads.make_layernorm_inputs("c5", M=999, N=5120)
+    x, w, b, dy = (inp[k].to(cuda) for k in ("x", "w", "b", "dy"))
+    y0, mu0, r0 = rn.ln_fwd(x, w, b, 1e-6)
+    runs = [rn.ln_bwd(dy, x, w, mu0, r0) for _ in range(3)]
+    y1, mu1, r1 = rn.ln_fwd(x, w, b, 1e-6)
+    assert torch.equal(y0, y1) and torch.equal(mu0, mu1) and torch.equal(r0, r1)
+    for dx, dg, db in runs[1:]:
+        assert torch.equal(dx, runs[0][0]) and torch.equal(dg, runs[0][1])
+        assert torch.equal(db, runs[0][2])
+    dxT, dgT, dbT = rn.ln_bwd(dy, x, w, mu0, r0, dgamma_dtype=x.dtype, poison=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dxT, runs[0][0])
+    assert torch.equal(dgT, runs[0][1].to(x.dtype)) and torch.equal(dbT, runs[0][2].to(x.dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_misaligned_and_strided(cuda, dtype):
+    """Buffers one element past an aligned address, and x/dy as column
+    slices of wider buffers (y/dx dense): same gate."""
+    M, N = 33, 4096
+    inp = workloads.make_layernorm_inputs("c2", M=M, N=N, dtype=dtype)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=cuda)
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to(cuda))
+        return v
+
+    x, w, b, dy = (shifted(inp[k]) for k in ("x", "w", "b", "dy"))
+    y = shifted(torch.full_like(inp["x"], float("nan")))
+    mean = torch.empty(M, device=cuda)
+    rstd = torch.empty(M, device=cuda)
+    rn.layernorm_fwd(x, w, b, inp["eps"], y, mean, rstd)
+    dx, dg, db = rn.ln_bwd(dy, x, w, mean, rstd, poison=True)
+    torch.cuda.synchronize()
+    out = {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
+    assert_pass(gate_ln_full(inp, out), f"ln misaligned {dtype}")
+
+    wide_x = torch.full((M, N + 24), -7.0, dtype=dtype, device=cuda)
+    wide_dy = torch.full((M, N + 24), -7.0, dtype=dtype, device=cuda)
+    wide_x[:, 8:8 + N] = inp["x"].to(cuda)
+    wide_dy[:, 16:16 + N] = inp["dy"].to(cuda)
+    xs, dys = wide_x[:, 8:8 + N], wide_dy[:, 16:16 + N]
+    y2, m2, r2 = rn.ln_fwd(xs, inp["w"].to(cuda), inp["b"].to(cuda), inp["eps"], poison=True)
+    dx2, dg2, db2 = rn.ln_bwd(dys, xs, inp["w"].to(cuda), m2, r2, poison=True)
+    torch.cuda.synchronize()
+    out2 = {"y": y2, "mean": m2, "rstd": r2, "dx": dx2, "dgamma": dg2, "dbeta": db2}
+    assert_pass(gate_ln_full(inp, out2), f"ln strided {dtype}")
+
+
+def test_m_zero_and_rejections(cuda):
+    x = torch.empty((0, 64), device=cuda, dtype=torch.bfloat16)
+    w = torch.ones(64, device=cuda, dtype=torch.bfloat16)
+    y, mu, r = rn.ln_fwd(x, w, None)
+    dx, dg, db = rn.ln_bwd(x, x, w, mu, r, poison=True)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and torch.equal(dg.cpu(), torch.zeros(64))
+    assert torch.equal(db.cpu(), torch.zeros(64))
+    n = rn.LAYERNORM_MAX_N + 1
+    with pytest.raises(rn.RmsnormError):
+        rn.ln_fwd(torch.empty(2, n, device=cuda, dtype=torch.bfloat16),
+                  torch.ones(n, device=cuda, dtype=torch.bfloat16))
