@@ -25,8 +25,8 @@
 //
 // Geometry: a row is spread over `wpr` wavefronts (64*wpr lanes, a power of
 // two up to 16); lane t of a row owns vectors c*64*wpr + t for c < chunks,
-// so each chunk is one coalesced sweep.  A 1024-thread workgroup holds
-// G = 16/wpr rows at a time.  Elements past N are loaded as 0 and left out of
+// so each chunk is one coalesced sweep.  A workgroup of B threads (256, or
+// 64*wpr for longer rows; at most 1024) holds G = B/(64*wpr) rows at a time.  Elements past N are loaded as 0 and left out of
 // the variance and of every store.
 //
 // Backward stage 1: workgroup w owns rows [w*M/P, (w+1)*M/P) (its G row
@@ -44,73 +44,101 @@
 namespace rmsnorm_hip {
 namespace {
 
-constexpr int kLnBlock = 1024;
-constexpr int kLnWaves = kLnBlock / kWave;
+constexpr int kLnMaxBlock = 1024;
+constexpr int kLnWaves = kLnMaxBlock / kWave;
 
-// Sum of v over the wpr wavefronts of this thread's row (wpr uniform across
-// the workgroup, so every thread takes the same path and the barrier is
-// reached by all).  slots: [2][kLnWaves] floats; parity alternates.
-__device__ __forceinline__ float row_sum(float v, float* slots, int& parity, int wpr,
-                                         int first_wave, int wave, int lane) {
-  v = wave_sum(v);
-  if (wpr == 1) return v;
-  float* s = slots + parity * kLnWaves;
-  if (lane == 0) s[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < wpr; ++i) t += s[first_wave + i];
-  parity ^= 1;
-  return t;
+// ---- row reductions ---------------------------------------------------------
+//
+// Every sum below is over the wpr wavefronts of one row: each wavefront sums
+// its 64 lanes (every lane ends with the same bits), then, when wpr > 1, the
+// wavefronts' sums are added in wavefront order through LDS.  `slots` hold
+// [2][kLnWaves][K] values; parity alternates so one barrier per exchange
+// suffices.  wpr is uniform across the workgroup, so every thread takes the
+// same path and reaches the same barriers.
+
+// float64 move between lanes with a DPP control (two 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(b)),
+                                             CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(b >> 32)),
+                                             CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
 }
 
-// float64 sum over the 64 lanes: xor butterfly, every lane ends with the
-// same bits (each pairwise add sees the same two operands).
+__device__ __forceinline__ double lane_value_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), lane));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// float64 sum over the 64 lanes, in the same pattern as wave_sum.
 __device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_move_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move_f64<0x141>(v);  // row_half_mirror: 8-lane sums
+  v += dpp_move_f64<0x140>(v);  // row_mirror: 16-lane sums
+  return (lane_value_f64(v, 0) + lane_value_f64(v, 16)) +
+         (lane_value_f64(v, 32) + lane_value_f64(v, 48));
+}
+
+struct RowGeom {
+  int tpr, G, t, group, first_wave, wave, lane;
+};
+
+__device__ __forceinline__ RowGeom row_geom(int wpr) {
+  RowGeom g;
+  g.tpr = kWave * wpr;
+  g.G = blockDim.x / g.tpr;
+  g.t = threadIdx.x % g.tpr;
+  g.group = threadIdx.x / g.tpr;
+  g.first_wave = g.group * wpr;
+  g.wave = threadIdx.x / kWave;
+  g.lane = threadIdx.x % kWave;
+  return g;
+}
+
+// KD float64 and KF float32 row sums in one exchange.  The slot arrays are
+// [2][kLnWaves][SD] doubles and [2][kLnWaves][SF] floats with the same
+// SD >= KD, SF >= KF in every call of a kernel, so the two parity halves are
+// disjoint whatever KD and KF are: an exchange writes only the half the
+// previous one did not read, and the half it reads is rewritten two
+// exchanges later, after a barrier every reader has passed.
+template <int KD, int KF, int SD, int SF>
+__device__ __forceinline__ void row_sums(double* a, float* b, double* s64, float* s32,
+                                         int& parity, int wpr, const RowGeom& rg) {
+  static_assert(KD <= SD && KF <= SF, "slot layout");
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
-__device__ __forceinline__ double row_sum_f64(double v, double* slots, int& parity, int wpr,
-                                              int first_wave, int wave, int lane) {
-  v = wave_sum_f64(v);
-  if (wpr == 1) return v;
-  double* s = slots + parity * kLnWaves;
-  if (lane == 0) s[wave] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < wpr; ++i) t += s[first_wave + i];
-  parity ^= 1;
-  return t;
-}
-
-// One float64 and two float32 sums in one exchange (one barrier).
-// slots64: [2][kLnWaves]; slots: [2][kLnWaves][2].
-__device__ __forceinline__ void row_sum3(double& a, float& b, float& c, double* slots64,
-                                         float* slots, int& parity, int wpr, int first_wave,
-                                         int wave, int lane) {
-  a = wave_sum_f64(a);
-  b = wave_sum(b);
-  c = wave_sum(c);
+  for (int i = 0; i < KD; ++i) a[i] = wave_sum_f64(a[i]);
+#pragma unroll
+  for (int i = 0; i < KF; ++i) b[i] = wave_sum(b[i]);
   if (wpr == 1) return;
-  double* s64 = slots64 + parity * kLnWaves;
-  float* s = slots + parity * kLnWaves * 2;
-  if (lane == 0) {
-    s64[wave] = a;
-    s[2 * wave] = b;
-    s[2 * wave + 1] = c;
+  double* d = s64 + parity * kLnWaves * SD;
+  float* f = s32 + parity * kLnWaves * SF;
+  if (rg.lane == 0) {
+#pragma unroll
+    for (int i = 0; i < KD; ++i) d[rg.wave * SD + i] = a[i];
+#pragma unroll
+    for (int i = 0; i < KF; ++i) f[rg.wave * SF + i] = b[i];
   }
   __syncthreads();
-  double ta = 0.0;
-  float tb = 0.f, tc = 0.f;
-  for (int i = 0; i < wpr; ++i) {
-    ta += s64[first_wave + i];
-    tb += s[2 * (first_wave + i)];
-    tc += s[2 * (first_wave + i) + 1];
+#pragma unroll
+  for (int i = 0; i < KD; ++i) {
+    double t = 0.0;
+    for (int w = 0; w < wpr; ++w) t += d[(rg.first_wave + w) * SD + i];
+    a[i] = t;
   }
-  a = ta;
-  b = tb;
-  c = tc;
+#pragma unroll
+  for (int i = 0; i < KF; ++i) {
+    float t = 0.f;
+    for (int w = 0; w < wpr; ++w) t += f[(rg.first_wave + w) * SF + i];
+    b[i] = t;
+  }
   parity ^= 1;
 }
 
@@ -139,33 +167,30 @@ __device__ __forceinline__ void st(const Pack<DT, VEC>& v, const char* row, int 
   __builtin_nontemporal_store(v.raw, reinterpret_cast<R*>(const_cast<char*>(row) + off));
 }
 
-struct RowGeom {
-  int tpr, G, t, group, first_wave, wave, lane;
-};
-
-__device__ __forceinline__ RowGeom row_geom(int wpr) {
-  RowGeom g;
-  g.tpr = kWave * wpr;
-  g.G = kLnBlock / g.tpr;
-  g.t = threadIdx.x % g.tpr;
-  g.group = threadIdx.x / g.tpr;
-  g.first_wave = g.group * wpr;
-  g.wave = threadIdx.x / kWave;
-  g.lane = threadIdx.x % kWave;
-  return g;
+// Rows each row group takes per step: two when the rows' data fits in 16
+// VGPRs per row in 256-thread workgroups (8 in larger ones, whose register
+// budget is 128): both rows' loads are then in flight at once and their
+// reductions share one exchange.  Else one.
+template <int DT, int VEC, int MAXC, int MATRICES, int BLK>
+constexpr int rows_per_step() {
+  constexpr int regs = (VEC * ElemBytes<DT>::value + 3) / 4;
+  return MAXC * regs * MATRICES <= (BLK == 256 ? 16 : 8) ? 2 : 1;
 }
 
-template <int DT, int VEC, int MAXC>
-__global__ __launch_bounds__(kLnBlock) void ln_fwd_kernel(
+// BLK: 256 for 256-thread workgroups (at least 3 wavefronts per SIMD, up to
+// 168 VGPRs), else 1024 (512- and 1024-thread workgroups, 128 VGPRs).
+template <int DT, int VEC, int MAXC, int BLK>
+__global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, const void* __restrict__ beta,
     void* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd, int64_t M, int N,
     int chunks, int wpr, float eps, int64_t ldx, int64_t ldy) {
   using PK = Pack<DT, VEC>;
-  __shared__ float slots[2 * kLnWaves];
-  __shared__ double slots64[2 * kLnWaves];
+  constexpr int R = rows_per_step<DT, VEC, MAXC, 1, BLK>();
+  __shared__ float slots[2 * kLnWaves * R];
+  __shared__ double slots64[2 * kLnWaves * R];
   const RowGeom rg = row_geom(wpr);
   const float n_f = static_cast<float>(N);
-  int parity = 0, parity64 = 0;
+  int parity = 0;
   PK g[MAXC], b[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
@@ -177,52 +202,68 @@ __global__ __launch_bounds__(kLnBlock) void ln_fwd_kernel(
       if (beta) ld<DT, VEC, false>(b[c], static_cast<const char*>(beta), e);
     }
   }
-  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * rg.G; row0 < M;
-       row0 += static_cast<int64_t>(gridDim.x) * rg.G) {
-    const int64_t row = row0 + rg.group;
-    const bool active = row < M;
-    const char* xr = row_base<DT>(x, row, ldx);
+  const int64_t step = static_cast<int64_t>(rg.G) * R;
+  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * step; row0 < M;
+       row0 += static_cast<int64_t>(gridDim.x) * step) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       g[c].opaque();
       b[c].opaque();
     }
-    PK xv[MAXC];
+    int64_t row[R];
+    bool active[R];
+    PK xv[R][MAXC];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e = (c * rg.tpr + rg.t) * VEC;
-      xv[c].zero();
-      if (active && c < chunks && e < N) ld<DT, VEC, true>(xv[c], xr, e);
+    for (int j = 0; j < R; ++j) {
+      row[j] = row0 + j * rg.G + rg.group;
+      active[j] = row[j] < M;
+      const char* xr = row_base<DT>(x, row[j], ldx);
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = (c * rg.tpr + rg.t) * VEC;
+        xv[j][c].zero();
+        if (active[j] && c < chunks && e < N) ld<DT, VEC, true>(xv[j][c], xr, e);
+      }
     }
-    double s = 0.0;
+    double s[R];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
+    for (int j = 0; j < R; ++j) {
+      s[j] = 0.0;
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) s += static_cast<double>(xv[c].get(k));
-    s = row_sum_f64(s, slots64, parity64, wpr, rg.first_wave, rg.wave, rg.lane);
-    const double mu64 = s / static_cast<double>(N);
-    const float mu = static_cast<float>(mu64);
-    const float cm = static_cast<float>(mu64 - static_cast<double>(mu));
-    float q = 0.f;
+      for (int c = 0; c < MAXC; ++c)
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e = (c * rg.tpr + rg.t) * VEC;
-      if (c < chunks && e < N) {
+        for (int k = 0; k < VEC; ++k) s[j] += static_cast<double>(xv[j][c].get(k));
+    }
+    row_sums<R, 0, R, R>(s, nullptr, slots64, slots, parity, wpr, rg);
+    float mu[R], cm[R], q[R];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          const float d = xv[c].get(k) - mu;
-          q = fmaf(d, d, q);
+    for (int j = 0; j < R; ++j) {
+      const double mu64 = s[j] / static_cast<double>(N);
+      mu[j] = static_cast<float>(mu64);
+      cm[j] = static_cast<float>(mu64 - static_cast<double>(mu[j]));
+      q[j] = 0.f;
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = (c * rg.tpr + rg.t) * VEC;
+        if (c < chunks && e < N) {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            const float d = xv[j][c].get(k) - mu[j];
+            q[j] = fmaf(d, d, q[j]);
+          }
         }
       }
     }
-    q = row_sum(q, slots, parity, wpr, rg.first_wave, rg.wave, rg.lane);
-    const float r = 1.0f / sqrtf((q / n_f - cm * cm) + eps);
-    if (active) {
+    row_sums<0, R, R, R>(nullptr, q, slots64, slots, parity, wpr, rg);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float r = 1.0f / sqrtf((q[j] / n_f - cm[j] * cm[j]) + eps);
+      if (!active[j]) continue;
       if (rg.t == 0) {
-        mean[row] = mu;
-        rstd[row] = r;
+        mean[row[j]] = mu[j];
+        rstd[row[j]] = r;
       }
-      const char* yr = row_base<DT>(y, row, ldy);
+      const char* yr = row_base<DT>(y, row[j], ldy);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = (c * rg.tpr + rg.t) * VEC;
@@ -230,7 +271,7 @@ __global__ __launch_bounds__(kLnBlock) void ln_fwd_kernel(
           float o[VEC];
 #pragma unroll
           for (int k = 0; k < VEC; ++k)
-            o[k] = fmaf(((xv[c].get(k) - mu) - cm) * r, g[c].get(k), b[c].get(k));
+            o[k] = fmaf(((xv[j][c].get(k) - mu[j]) - cm[j]) * r, g[c].get(k), b[c].get(k));
           PK out;
           out.set(o);
           st<DT, VEC>(out, yr, e);
@@ -240,8 +281,8 @@ __global__ __launch_bounds__(kLnBlock) void ln_fwd_kernel(
   }
 }
 
-template <int DT, int VEC, int MAXC>
-__global__ __launch_bounds__(kLnBlock) void ln_bwd_kernel(
+template <int DT, int VEC, int MAXC, int BLK>
+__global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
     const void* __restrict__ dy, const void* __restrict__ x, const void* __restrict__ gamma,
     const float* __restrict__ mean, const float* __restrict__ rstd, void* __restrict__ dx,
     float* __restrict__ part, int64_t M, int N, int chunks, int wpr, int64_t P, int64_t lddy,
@@ -252,16 +293,18 @@ __global__ __launch_bounds__(kLnBlock) void ln_bwd_kernel(
   // calls below are deliberate.
 #pragma clang fp contract(off)
   using PK = Pack<DT, VEC>;
-  extern __shared__ __align__(16) float comb[];  // [kLnBlock * VEC] when G > 1
-  __shared__ float slots[2 * kLnWaves * 2];
-  __shared__ double slots64[2 * kLnWaves];
+  constexpr int R = rows_per_step<DT, VEC, MAXC, 2, BLK>();
+  extern __shared__ __align__(16) float comb[];  // [blockDim.x * VEC] when G > 1
+  __shared__ float slots[2 * kLnWaves * 2 * R];
+  __shared__ double slots64[2 * kLnWaves * R];
   const RowGeom rg = row_geom(wpr);
   const float n_f = static_cast<float>(N);
   int parity = 0;
   const int64_t w = blockIdx.x;
   const int64_t r0 = block_row_begin(w, M, P);
   const int64_t r1 = block_row_begin(w + 1, M, P);
-  const int64_t iters = (r1 - r0 + rg.G - 1) / rg.G;
+  const int64_t step = static_cast<int64_t>(rg.G) * R;
+  const int64_t iters = (r1 - r0 + step - 1) / step;
   PK g[MAXC];
   float ag[MAXC][VEC], ab[MAXC][VEC];
 #pragma unroll
@@ -273,53 +316,71 @@ __global__ __launch_bounds__(kLnBlock) void ln_bwd_kernel(
     for (int k = 0; k < VEC; ++k) ag[c][k] = ab[c][k] = 0.f;
   }
   for (int64_t it = 0; it < iters; ++it) {
-    const int64_t row = r0 + it * rg.G + rg.group;
-    const bool active = row < r1;
-    const char* dyr = row_base<DT>(dy, row, lddy);
-    const char* xr = row_base<DT>(x, row, ldx);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) g[c].opaque();
-    PK dv[MAXC], xv[MAXC];
-    float mu = 0.f, r = 0.f;
-    if (active) {
-      mu = mean[row];
-      r = rstd[row];
-    }
+    int64_t row[R];
+    bool active[R];
+    float mu[R], r[R];
+    PK dv[R][MAXC], xv[R][MAXC];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e = (c * rg.tpr + rg.t) * VEC;
-      dv[c].zero();
-      xv[c].zero();
-      if (active && c < chunks && e < N) {
-        ld<DT, VEC, true>(dv[c], dyr, e);
-        ld<DT, VEC, true>(xv[c], xr, e);
+    for (int j = 0; j < R; ++j) {
+      row[j] = r0 + it * step + j * rg.G + rg.group;
+      active[j] = row[j] < r1;
+      mu[j] = active[j] ? mean[row[j]] : 0.f;
+      r[j] = active[j] ? rstd[row[j]] : 0.f;
+      const char* dyr = row_base<DT>(dy, row[j], lddy);
+      const char* xr = row_base<DT>(x, row[j], ldx);
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = (c * rg.tpr + rg.t) * VEC;
+        dv[j][c].zero();
+        xv[j][c].zero();
+        if (active[j] && c < chunks && e < N) {
+          ld<DT, VEC, true>(dv[j][c], dyr, e);
+          ld<DT, VEC, true>(xv[j][c], xr, e);
+        }
       }
     }
     // Lanes past N hold x = dy = 0, so they add 0 to every sum.
-    double sx = 0.0;
-    float s1 = 0.f, s2 = 0.f;
+    double sx[R];
+    float s12[2 * R];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
+    for (int j = 0; j < R; ++j) {
+      sx[j] = 0.0;
+      float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) {
-        const float xf = xv[c].get(k);
-        const float u = dv[c].get(k) * g[c].get(k);
-        sx += static_cast<double>(xf);
-        s1 += u;
-        s2 = fmaf(u, xf - mu, s2);
-      }
-    row_sum3(sx, s1, s2, slots64, slots, parity, wpr, rg.first_wave, rg.wave, rg.lane);
-    const float cm =
-        active ? static_cast<float>(sx / static_cast<double>(N) - static_cast<double>(mu)) : 0.f;
-    const float c1 = s1 / n_f;
-    const float c2 = (r * (s2 - cm * s1)) / n_f;
+      for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float xf = xv[j][c].get(k);
+          const float u = dv[j][c].get(k) * g[c].get(k);
+          sx[j] += static_cast<double>(xf);
+          s1 += u;
+          s2 = fmaf(u, xf - mu[j], s2);
+        }
+      s12[2 * j] = s1;
+      s12[2 * j + 1] = s2;
+    }
+    row_sums<R, 2 * R, R, 2 * R>(sx, s12, slots64, slots, parity, wpr, rg);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      dv[c].opaque();
-      xv[c].opaque();
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        dv[j][c].opaque();
+        xv[j][c].opaque();
+      }
     }
-    if (active) {
-      const char* dxr = row_base<DT>(dx, row, lddx);
+    // Rows in order (j = 0, 1, ...), so each column sum adds its rows in
+    // row order.
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (!active[j]) continue;
+      const float cm = static_cast<float>(sx[j] / static_cast<double>(N) -
+                                          static_cast<double>(mu[j]));
+      const float s1 = s12[2 * j], s2 = s12[2 * j + 1];
+      const float c1 = s1 / n_f;
+      const float c2 = (r[j] * (s2 - cm * s1)) / n_f;
+      const char* dxr = row_base<DT>(dx, row[j], lddx);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = (c * rg.tpr + rg.t) * VEC;
@@ -327,10 +388,10 @@ __global__ __launch_bounds__(kLnBlock) void ln_bwd_kernel(
           float o[VEC];
 #pragma unroll
           for (int k = 0; k < VEC; ++k) {
-            const float dyf = dv[c].get(k);
-            const float xh = ((xv[c].get(k) - mu) - cm) * r;
+            const float dyf = dv[j][c].get(k);
+            const float xh = ((xv[j][c].get(k) - mu[j]) - cm) * r[j];
             const float u = dyf * g[c].get(k);
-            o[k] = r * ((u - c1) - xh * c2);
+            o[k] = r[j] * ((u - c1) - xh * c2);
             ag[c][k] = fmaf(dyf, xh, ag[c][k]);
             ab[c][k] += dyf;
           }
@@ -379,7 +440,8 @@ __global__ __launch_bounds__(kLnBlock) void ln_bwd_kernel(
 template <int DT, int VEC, int MAXC>
 hipError_t ln_fwd_maxc(const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
-  return launch(ln_fwd_kernel<DT, VEC, MAXC>, p.grid, kLnBlock, 0, s, a.x, a.gamma, a.beta, a.y,
+  auto* k = p.block == 256 ? ln_fwd_kernel<DT, VEC, MAXC, 256> : ln_fwd_kernel<DT, VEC, MAXC, 1024>;
+  return launch(k, p.grid, p.block, 0, s, a.x, a.gamma, a.beta, a.y,
                 a.mean, a.rstd, a.M, a.N, p.chunks, p.wpr, a.eps, a.x_pitch / es,
                 a.y_pitch / es);
 }
@@ -387,7 +449,8 @@ hipError_t ln_fwd_maxc(const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
 template <int DT, int VEC, int MAXC>
 hipError_t ln_bwd_maxc(const LnPlan& p, const LnBwdArgs& a, hipStream_t s) {
   constexpr int es = ElemBytes<DT>::value;
-  return launch(ln_bwd_kernel<DT, VEC, MAXC>, p.grid, kLnBlock, static_cast<size_t>(p.lds), s,
+  auto* k = p.block == 256 ? ln_bwd_kernel<DT, VEC, MAXC, 256> : ln_bwd_kernel<DT, VEC, MAXC, 1024>;
+  return launch(k, p.grid, p.block, static_cast<size_t>(p.lds), s,
                 a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, a.part, a.M, a.N, p.chunks, p.wpr,
                 p.grid, a.dy_pitch / es, a.x_pitch / es, a.dx_pitch / es);
 }
@@ -464,8 +527,6 @@ hipError_t ln_bwd_dt(const LnPlan& p, const LnBwdArgs& a, hipStream_t s) {
 #undef LN_MAXC_CASE
 
 }  // namespace
-
-int ln_block_threads() { return kLnBlock; }
 
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
   switch (dtype) {

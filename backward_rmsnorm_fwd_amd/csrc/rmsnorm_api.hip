@@ -868,8 +868,11 @@ int bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const voi
 // lane over 16 wavefronts.  The backward's P (rows of each partial block) is a
 // function of (M, N, dtype): it is computed with the vector width N alone
 // allows, so pointer alignment changes only the kernel variant.
-constexpr int64_t kLnFwdWorkgroups = 512;
-constexpr int64_t kLnBwdWorkgroups = 256;
+// Workgroups of 256 threads (64*wpr for rows over more than four
+// wavefronts): several per compute unit, so one waiting at a row barrier
+// does not idle the unit.
+constexpr int64_t kLnFwdWorkgroups = 2048;  // of 256 threads; fewer when larger
+constexpr int64_t kLnBwdWorkgroups = 512;
 
 LnPlan ln_plan(int64_t M, int64_t N, int es, bool backward, int align) {
   LnPlan p{};
@@ -879,14 +882,15 @@ LnPlan ln_plan(int64_t M, int64_t N, int es, bool backward, int align) {
                               : std::max(1, std::min(4, 32 / p.vec));
   p.wpr = std::min(16, pow2_at_least(ceil_div(nvec, int64_t(kWave) * target)));
   p.chunks = static_cast<int>(ceil_div(nvec, int64_t(kWave) * p.wpr));
-  const int64_t G = ln_block_threads() / (kWave * p.wpr);
+  p.block = std::max(256, kWave * p.wpr);
+  const int64_t G = p.block / (kWave * p.wpr);
   if (backward) {
-    p.lds = G > 1 ? int64_t(ln_block_threads()) * p.vec * 4 : 0;
+    p.lds = G > 1 ? int64_t(p.block) * p.vec * 4 : 0;
     const LnPlan base = p.vec == pick_vec(N, es, 16) ? p : ln_plan(M, N, es, true, 16);
-    const int64_t Gb = ln_block_threads() / (kWave * base.wpr);
+    const int64_t Gb = base.block / (kWave * base.wpr);
     p.grid = std::min(ceil_div(M, Gb), kLnBwdWorkgroups);
   } else {
-    p.grid = std::min(ceil_div(M, G), kLnFwdWorkgroups);
+    p.grid = std::min(ceil_div(M, G), kLnFwdWorkgroups * 256 / p.block);
   }
   return p;
 }
@@ -1028,7 +1032,7 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
   out->kernel = bwd ? LAYERNORM_KERNEL_BWD : LAYERNORM_KERNEL_FWD;
   out->vec = p.vec;
   out->threads_per_row = kWave * p.wpr;
-  out->block_threads = ln_block_threads();
+  out->block_threads = p.block;
   out->chunks = p.chunks;
   out->weight_in_regs = 1;
   out->grid = p.grid;

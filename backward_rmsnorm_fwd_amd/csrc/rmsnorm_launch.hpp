@@ -98,12 +98,13 @@ hipError_t split_bwd_launch(int dtype, const SplitPlan& sp, const FastBwdArgs& a
                             float* coef, hipStream_t s);
 
 // LayerNorm (layernorm.hip): row-resident kernels, `wpr` wavefronts per row,
-// `chunks` vector accesses of `vec` elements per lane, 1024-thread
-// workgroups.  Backward: grid = P row blocks, `lds` bytes for the combine.
+// `chunks` vector accesses of `vec` elements per lane, `block` threads per
+// workgroup.  Backward: grid = P row blocks, `lds` bytes for the combine.
 struct LnPlan {
   int vec;
   int wpr;
   int chunks;
+  int block;
   int64_t grid;
   int64_t lds;
 };
@@ -137,7 +138,6 @@ struct LnBwdArgs {
   int64_t dx_pitch;
 };
 
-int ln_block_threads();
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
 hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
 

@@ -88,7 +88,8 @@ def _ceil(a, b):
 @pytest.mark.parametrize("dt", [0, 1, 2])
 def test_plans_cover_rows(dt):
     """Every N gets a plan whose lanes cover the row with no empty chunk,
-    within the register-slot caps, in 1024-thread workgroups; P does not
+    within the register-slot caps, in workgroups of max(256, row lanes)
+    threads; P does not
     depend on alignment; the workspace holds two [P, N] blocks."""
     es = 4 if dt == 0 else 2
     for n in list(range(1, 130)) + [255, 256, 257, 1000, 1024, 4095, 4096, 4097, 5120, 8191,
@@ -105,16 +106,17 @@ def test_plans_cover_rows(dt):
                     vec, tpr, ch = p["vec"], p["threads_per_row"], p["chunks"]
                     assert n % vec == 0 and vec * es <= align
                     assert tpr * ch * vec >= n > tpr * (ch - 1) * vec
-                    assert p["block_threads"] == 1024 and 64 <= tpr <= 1024
+                    assert p["block_threads"] == max(256, tpr) and 64 <= tpr <= 1024
                     cap = max(target(vec), 16 // vec)
                     assert ch <= cap
                     if which == rn.PASS_BWD_ROWS:
                         if P is None:
                             P = p["partials"]
                         assert p["partials"] == P == p["grid"]
-                        assert p["lds_bytes"] == (0 if tpr == 1024 else 1024 * vec * 4)
-            assert P == min(256, _ceil(m, 1024 // rn.layernorm_query_plan(
-                m, n, dt, which=rn.PASS_BWD_ROWS)["threads_per_row"]))
+                        bt = p["block_threads"]
+                        assert p["lds_bytes"] == (0 if tpr == bt else bt * vec * 4)
+            base = rn.layernorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)
+            assert P == min(512, _ceil(m, base["block_threads"] // base["threads_per_row"]))
             assert rn.layernorm_bwd_workspace_bytes(m, n, dt) == 2 * P * n * 4
             red = rn.layernorm_query_plan(m, n, dt, which=rn.PASS_BWD_REDUCE)
             assert red["partials"] == P
