@@ -208,3 +208,24 @@ def make_layernorm_tile_case(shape, dtype, seed, scale=1.0, shift_std=1.0):
     x = x + _normal(rng, shape[:-1] + (1,), shift_std)
     return {"x": _cast(x, dtype), "w": _cast(g, dtype), "dy": _cast(dy, dtype),
             "b": _cast(b, dtype), "offset": False, "eps": 1e-6, "dtype": dtype}
+
+
+def make_add_inputs(name, M=None, N=None, seed=None, dtype=None):
+    """Inputs of the residual add fused with RMSNorm for workload ``name``:
+    the recipe's x, weight and dy (same draws), then from the same generator
+    a residual stream ``res ~ N(0, 1)`` [M, N] and the gradient arriving on
+    it ``dh`` [M, N], drawn like the recipe's dy (N(0, 1e-2) for the LLM
+    recipes, N(0, 1) otherwise).  Returns the dict of ``make_inputs`` plus
+    ``res`` and ``dh``."""
+    out, arrays, rng = _draw(name, M, N, seed, dtype)
+    x, g, dy = arrays
+    M, N = out["M"], out["N"]
+    if rng is None:
+        res = np.array([[0.5, -1.0]], dtype=np.float32)
+        dh = np.array([[0.25, 0.5]], dtype=np.float32)
+    else:
+        res = _normal(rng, (M, N))
+        dh = _normal(rng, (M, N), 1e-2 if WORKLOADS[name].recipe in ("llm", "offset") else 1.0)
+    T = out["dtype"]
+    out.update(x=_cast(x, T), w=_cast(g, T), dy=_cast(dy, T), res=_cast(res, T), dh=_cast(dh, T))
+    return out
