@@ -28,6 +28,9 @@ __all__ = [
     "rmsnorm_bwd_strided", "row_layout", "fwd", "bwd", "EXPORTED_SYMBOLS",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
     "layernorm_bwd_rows", "layernorm_bwd_reduce", "ln_fwd", "ln_bwd", "LAYERNORM_MAX_N",
+    "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
+    "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce", "add_fwd",
+    "add_bwd", "RMSNORM_ADD_MAX_N",
 ]
 
 RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
@@ -38,8 +41,9 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
                 9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
                 13: "bwd_split", 14: "bwd_reduce_wide", 15: "ln_fwd",
-                16: "ln_bwd"}
+                16: "ln_bwd", 17: "add_fwd", 18: "add_bwd"}
 LAYERNORM_MAX_N = 16384
+RMSNORM_ADD_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
 
 EXPORTED_SYMBOLS = (
@@ -48,6 +52,8 @@ EXPORTED_SYMBOLS = (
     "rmsnorm_fwd_strided", "rmsnorm_bwd_strided",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
     "layernorm_bwd_rows", "layernorm_bwd_reduce",
+    "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
+    "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce",
 )
 
 _DTYPES = {torch.float32: RMSNORM_F32, torch.float16: RMSNORM_F16,
@@ -127,6 +133,21 @@ def load_library():
     lib.layernorm_bwd_rows.restype = i32
     lib.layernorm_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp, vp]
     lib.layernorm_bwd_reduce.restype = i32
+    lib.rmsnorm_add_fwd.argtypes = [vp, i64, vp, i64, vp, f32, i64, i64, i32, u32, vp, i64, vp,
+                                    i64, vp, vp]
+    lib.rmsnorm_add_fwd.restype = i32
+    lib.rmsnorm_add_bwd.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i32, u32, vp,
+                                    i64, vp, vp, sz, vp]
+    lib.rmsnorm_add_bwd.restype = i32
+    lib.rmsnorm_add_bwd_workspace_bytes.argtypes = [i64, i64, i32, u32]
+    lib.rmsnorm_add_bwd_workspace_bytes.restype = sz
+    lib.rmsnorm_add_query_plan.argtypes = [i64, i64, i32, u32, i32, i32, ctypes.POINTER(Plan)]
+    lib.rmsnorm_add_query_plan.restype = i32
+    lib.rmsnorm_add_bwd_rows.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i32, u32,
+                                         vp, i64, vp, sz, vp]
+    lib.rmsnorm_add_bwd_rows.restype = i32
+    lib.rmsnorm_add_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp]
+    lib.rmsnorm_add_bwd_reduce.restype = i32
     _LIB = lib
     return lib
 
@@ -437,3 +458,104 @@ def ln_bwd(dy, x, gamma, mean, rstd, stream=None, poison=False, workspace=None,
         workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
     layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace, stream)
     return dx, dgamma, dbeta
+
+
+# ---- RMSNorm with the residual add fused before it (include/rmsnorm_add.h) -------
+
+def rmsnorm_add_query_plan(M, N, dtype, offset=False, which=PASS_FWD, align_bytes=16):
+    p = Plan()
+    _check("rmsnorm_add_query_plan", load_library().rmsnorm_add_query_plan(
+        int(M), int(N), _code(dtype), _flags(offset), int(which), int(align_bytes),
+        ctypes.byref(p)))
+    return p.as_dict()
+
+
+def rmsnorm_add_bwd_workspace_bytes(M, N, dtype, offset=False):
+    return int(load_library().rmsnorm_add_bwd_workspace_bytes(int(M), int(N), _code(dtype),
+                                                              _flags(offset)))
+
+
+def rmsnorm_add_fwd(x, res, gamma, eps, y, h, rstd, offset=False, stream=None):
+    """y, h, rstd <- RMSNorm(h) with h = x + res; row strides from the tensors."""
+    m, n, ldx = _layout(x, "x")
+    _, _, ldr = _layout(res, "res")
+    _, _, ldy = _layout(y, "y")
+    _, _, ldh = _layout(h, "h")
+    _check("rmsnorm_add_fwd", load_library().rmsnorm_add_fwd(
+        _ptr(x), ldx, _ptr(res), ldr, _ptr(gamma), float(eps), m, n, _dtype_code(x),
+        _flags(offset), _ptr(y), ldy, _ptr(h), ldh, _ptr(rstd), _stream(x.device, stream)))
+
+
+def rmsnorm_add_bwd(dy, dh, h, gamma, rstd, dx, dgamma, workspace, offset=False, stream=None):
+    """dx (the gradient of x and of res), dgamma <- backward; dh may be None."""
+    m, n, ldh = _layout(h, "h")
+    _, _, lddy = _layout(dy, "dy")
+    lddh = _layout(dh, "dh")[2] if dh is not None else n
+    _, _, lddx = _layout(dx, "dx")
+    in_dtype = dgamma.dtype != torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_add_bwd", load_library().rmsnorm_add_bwd(
+        _ptr(dy), lddy, _ptr(dh), lddh, _ptr(h), ldh, _ptr(gamma), _ptr(rstd), m, n,
+        _dtype_code(h), _flags(offset, in_dtype), _ptr(dx), lddx, _ptr(dgamma),
+        _ptr(workspace), ws_bytes, _stream(h.device, stream)))
+
+
+def rmsnorm_add_bwd_rows(dy, dh, h, gamma, rstd, dx, workspace, offset=False, stream=None):
+    m, n, ldh = _layout(h, "h")
+    _, _, lddy = _layout(dy, "dy")
+    lddh = _layout(dh, "dh")[2] if dh is not None else n
+    _, _, lddx = _layout(dx, "dx")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_add_bwd_rows", load_library().rmsnorm_add_bwd_rows(
+        _ptr(dy), lddy, _ptr(dh), lddh, _ptr(h), ldh, _ptr(gamma), _ptr(rstd), m, n,
+        _dtype_code(h), _flags(offset), _ptr(dx), lddx, _ptr(workspace), ws_bytes,
+        _stream(h.device, stream)))
+
+
+def rmsnorm_add_bwd_reduce(workspace, M, N, dtype, dgamma, offset=False, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    in_dtype = dgamma.dtype != torch.float32
+    _check("rmsnorm_add_bwd_reduce", load_library().rmsnorm_add_bwd_reduce(
+        _ptr(workspace), ws_bytes, int(M), int(N), _code(dtype), _flags(offset, in_dtype),
+        _ptr(dgamma), _stream(dgamma.device, stream)))
+
+
+def add_fwd(x, res, gamma, eps=1e-6, offset=False, stream=None, poison=False):
+    """Returns ``(y, h, rstd)``: h = x + res (the new residual stream),
+    y = RMSNorm(h), rstd float32 per row."""
+    _check_inputs(x, gamma)
+    _require(res.shape == x.shape and res.dtype == x.dtype and res.device == x.device
+             and row_layout(res) is not None, "res must match x")
+    m, _, _ = row_layout(x)
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    y = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)
+    h = fill(x.shape, float("nan"), device=x.device, dtype=x.dtype)
+    rstd = fill((m,), float("nan"), device=x.device, dtype=torch.float32)
+    rmsnorm_add_fwd(x, res, gamma, eps, y, h, rstd, offset, stream)
+    return y, h, rstd
+
+
+def add_bwd(dy, dh, h, gamma, rstd, offset=False, stream=None, poison=False, workspace=None,
+            dgamma_dtype=torch.float32):
+    """Returns ``(dx, dgamma)``: dx is the gradient of both x and res."""
+    _check_inputs(h, gamma)
+    for t, name in ((dy, "dy"), (dh, "dh")):
+        if t is not None:
+            _require(t.shape == h.shape and t.dtype == h.dtype and t.device == h.device,
+                     f"{name} must match h in shape, dtype and device")
+    if row_layout(dy) is None:
+        dy = dy.contiguous()
+    if dh is not None and row_layout(dh) is None:
+        dh = dh.contiguous()
+    m, n, _ = row_layout(h)
+    _require(rstd.dtype == torch.float32 and rstd.numel() == m and rstd.is_contiguous(),
+             "rstd must be a contiguous float32 tensor with one value per row")
+    _require(dgamma_dtype in (torch.float32, h.dtype), "dgamma_dtype must be float32 or h's dtype")
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    dx = fill(h.shape, float("nan"), device=h.device, dtype=h.dtype)
+    dgamma = fill((n,), float("nan"), device=h.device, dtype=dgamma_dtype)
+    if workspace is None:
+        nbytes = rmsnorm_add_bwd_workspace_bytes(m, n, h.dtype, offset)
+        workspace = torch.empty((max(nbytes, 4) // 4,), device=h.device, dtype=torch.float32)
+    rmsnorm_add_bwd(dy, dh, h, gamma, rstd, dx, dgamma, workspace, offset, stream)
+    return dx, dgamma

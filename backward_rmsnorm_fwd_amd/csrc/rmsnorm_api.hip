@@ -19,6 +19,7 @@
 
 #include "../../include/layernorm.h"
 #include "../../include/rmsnorm.h"
+#include "../../include/rmsnorm_add.h"
 #include "rmsnorm_fast.hpp"
 #include "rmsnorm_fast_table.hpp"
 #include "rmsnorm_launch.hpp"
@@ -1040,6 +1041,136 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
   out->lds_bytes = bwd ? p.lds : 0;
 }
 
+// ---- RMSNorm with the residual add fused before it (fused_add.hip) ----------
+//
+// The row-resident plan of LayerNorm (same targets, workgroups and P); the
+// backward's workspace is one [P, N] block.
+
+int check_add_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
+  if (dtype != RMSNORM_F32 && dtype != RMSNORM_F16 && dtype != RMSNORM_BF16)
+    return RMSNORM_ERR_DTYPE;
+  if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
+  if (N < 1 || N > RMSNORM_ADD_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  return RMSNORM_OK;
+}
+
+size_t add_workspace_bytes(int64_t M, int64_t N, int dtype) {
+  return static_cast<size_t>(ln_partials(M, N, elem_bytes(dtype)) * N * 4);
+}
+
+int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
+                 float eps, int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y,
+                 int64_t ldy, void* h, int64_t ldh, float* rstd, hipStream_t stream) {
+  int st = check_add_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_ERR_EPS;
+  if (bad_stride(ldx, N) || bad_stride(ldr, N) || bad_stride(ldy, N) || bad_stride(ldh, N))
+    return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!x || !res || !gamma || !y || !h || !rstd) return RMSNORM_ERR_NULL_POINTER;
+  const int es = elem_bytes(dtype);
+  if (misaligned(x, es) || misaligned(res, es) || misaligned(gamma, es) || misaligned(y, es) ||
+      misaligned(h, es) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(y, M, ldy * es, N * es), matrix(h, M, ldh * es, N * es),
+                   vec(rstd, M * 4)},
+                  {matrix(x, M, ldx * es, N * es), matrix(res, M, ldr * es, N * es),
+                   vec(gamma, N * es)}))
+    return RMSNORM_ERR_OVERLAP;
+  const LnPlan p = ln_plan(M, N, es, false,
+                           layout_alignment({x, res, gamma, y, h},
+                                            {ldx * es, ldr * es, ldy * es, ldh * es}));
+  const AddFwdArgs a{x, res, gamma, y, h, rstd, M, static_cast<int>(N), eps,
+                     (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * es, ldr * es, ldy * es,
+                     ldh * es};
+  return status_of(add_fwd_launch(dtype, p, a, stream));
+}
+
+int check_add_rows_args(const void* dy, int64_t lddy, const void* dh, int64_t lddh,
+                        const void* h, int64_t ldh, const void* gamma, const float* rstd,
+                        int64_t M, int64_t N, int dtype, uint32_t flags, const void* dx,
+                        int64_t lddx, const void* workspace, size_t workspace_bytes) {
+  int st = check_add_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (bad_stride(lddy, N) || bad_stride(ldh, N) || bad_stride(lddx, N) ||
+      (dh && bad_stride(lddh, N)))
+    return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!dy || !h || !gamma || !rstd || !dx) return RMSNORM_ERR_NULL_POINTER;
+  const int es = elem_bytes(dtype);
+  if (misaligned(dy, es) || misaligned(dh, es) || misaligned(h, es) || misaligned(gamma, es) ||
+      misaligned(dx, es) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  const size_t need = add_workspace_bytes(M, N, dtype);
+  if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(dh, dh ? M : 0, lddh * es, N * es),
+                   matrix(h, M, ldh * es, N * es), vec(gamma, N * es), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int add_rows_launch(const void* dy, int64_t lddy, const void* dh, int64_t lddh, const void* h,
+                    int64_t ldh, const void* gamma, const float* rstd, int64_t M, int64_t N,
+                    rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx,
+                    void* workspace, hipStream_t stream) {
+  if (M == 0) return RMSNORM_OK;
+  const int es = elem_bytes(dtype);
+  const LnPlan p = ln_plan(M, N, es, true,
+                           layout_alignment({dy, dh, h, gamma, dx},
+                                            {lddy * es, dh ? lddh * es : 16, ldh * es,
+                                             lddx * es}));
+  const AddBwdArgs a{dy, dh, h, gamma, rstd, dx, static_cast<float*>(workspace), M,
+                     static_cast<int>(N), (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * es,
+                     lddh * es, ldh * es, lddx * es};
+  return status_of(add_bwd_launch(dtype, p, a, stream));
+}
+
+int check_add_reduce_args(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                          int dtype, uint32_t flags, const void* dgamma) {
+  int st = check_add_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  st = check_dgamma_args(dgamma, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  const size_t need = add_workspace_bytes(M, N, dtype);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
+                  {vec(workspace, static_cast<int64_t>(need))}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int add_bwd_impl(const void* dy, int64_t lddy, const void* dh, int64_t lddh, const void* h,
+                 int64_t ldh, const void* gamma, const float* rstd, int64_t M, int64_t N,
+                 rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx, void* dgamma,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_add_rows_args(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx,
+                               lddx, workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  st = check_add_reduce_args(workspace, workspace_bytes, M, N, dtype, flags, dgamma);
+  if (st != RMSNORM_OK) return st;
+  const int es = elem_bytes(dtype);
+  const size_t need = add_workspace_bytes(M, N, dtype);
+  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
+                   matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * es, N * es), matrix(dh, dh ? M : 0, lddh * es, N * es),
+                   matrix(h, M, ldh * es, N * es), vec(gamma, N * es), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  st = add_rows_launch(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx, lddx,
+                       workspace, stream);
+  if (st != RMSNORM_OK) return st;
+  return reduce_columns(static_cast<const float*>(workspace), ln_partials(M, N, es), N, dtype,
+                        flags, dgamma, stream);
+}
+
+void fill_add_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* out) {
+  fill_ln_plan(M, N, dtype, pass, align, out);
+  if (pass == RMSNORM_PASS_BWD_REDUCE) return;
+  out->kernel = pass == RMSNORM_PASS_BWD_ROWS ? RMSNORM_KERNEL_ADD_BWD : RMSNORM_KERNEL_ADD_FWD;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1184,6 +1315,62 @@ int layernorm_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t f
   if (align_bytes < 1 || align_bytes > 4096 || (align_bytes & (align_bytes - 1)))
     return RMSNORM_ERR_ARGUMENT;
   fill_ln_plan(M, N, dtype, pass, std::min(align_bytes, 16), plan);
+  return RMSNORM_OK;
+}
+
+int rmsnorm_add_fwd(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
+                    float eps, int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
+                    void* y, int64_t ldy, void* h, int64_t ldh, float* rstd,
+                    hipStream_t stream) {
+  return add_fwd_impl(x, ldx, res, ldr, gamma, eps, M, N, dtype, flags, y, ldy, h, ldh, rstd,
+                      stream);
+}
+
+size_t rmsnorm_add_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                                       uint32_t flags) {
+  if (check_add_common(M, N, dtype, flags) != RMSNORM_OK || M == 0) return 0;
+  return add_workspace_bytes(M, N, dtype);
+}
+
+int rmsnorm_add_bwd(const void* dy, int64_t lddy, const void* dh, int64_t lddh, const void* h,
+                    int64_t ldh, const void* gamma, const float* rstd, int64_t M, int64_t N,
+                    rmsnorm_dtype_t dtype, uint32_t flags, void* dx, int64_t lddx,
+                    void* dgamma, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return add_bwd_impl(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx, lddx,
+                      dgamma, workspace, workspace_bytes, stream);
+}
+
+int rmsnorm_add_bwd_rows(const void* dy, int64_t lddy, const void* dh, int64_t lddh,
+                         const void* h, int64_t ldh, const void* gamma, const float* rstd,
+                         int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
+                         int64_t lddx, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const int st = check_add_rows_args(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags,
+                                     dx, lddx, workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  return add_rows_launch(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx, lddx,
+                         workspace, stream);
+}
+
+int rmsnorm_add_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                           rmsnorm_dtype_t dtype, uint32_t flags, void* dgamma,
+                           hipStream_t stream) {
+  const int st = check_add_reduce_args(workspace, workspace_bytes, M, N, dtype, flags, dgamma);
+  if (st != RMSNORM_OK) return st;
+  return reduce_columns(static_cast<const float*>(workspace),
+                        ln_partials(M, N, elem_bytes(dtype)), N, dtype, flags, dgamma, stream);
+}
+
+int rmsnorm_add_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
+                           int pass, int align_bytes, rmsnorm_plan_t* plan) {
+  const int st = check_add_common(M, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!plan) return RMSNORM_ERR_NULL_POINTER;
+  if (pass < RMSNORM_PASS_FWD || pass > RMSNORM_PASS_BWD_REDUCE) return RMSNORM_ERR_ARGUMENT;
+  if (align_bytes < 1 || align_bytes > 4096 || (align_bytes & (align_bytes - 1)))
+    return RMSNORM_ERR_ARGUMENT;
+  fill_add_plan(M, N, dtype, pass, std::min(align_bytes, 16), plan);
   return RMSNORM_OK;
 }
 

@@ -139,6 +139,45 @@ struct LnBwdArgs {
 };
 
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
+
+// RMSNorm with the residual add fused before it (fused_add.hip), on the
+// row-resident plan of LayerNorm.
+struct AddFwdArgs {
+  const void* x;
+  const void* res;
+  const void* gamma;
+  void* y;
+  void* h;  // x + res in the dtype
+  float* rstd;
+  int64_t M;
+  int N;
+  float eps;
+  int offset;
+  int64_t x_pitch;  // bytes between row starts
+  int64_t res_pitch;
+  int64_t y_pitch;
+  int64_t h_pitch;
+};
+
+struct AddBwdArgs {
+  const void* dy;
+  const void* dh;  // may be null
+  const void* h;
+  const void* gamma;
+  const float* rstd;
+  void* dx;
+  float* part;  // [P, N]
+  int64_t M;
+  int N;
+  int offset;
+  int64_t dy_pitch;
+  int64_t dh_pitch;
+  int64_t h_pitch;
+  int64_t dx_pitch;
+};
+
+hipError_t add_fwd_launch(int dtype, const LnPlan& p, const AddFwdArgs& a, hipStream_t s);
+hipError_t add_bwd_launch(int dtype, const LnPlan& p, const AddBwdArgs& a, hipStream_t s);
 hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
 
 }  // namespace rmsnorm_hip

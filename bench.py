@@ -23,6 +23,13 @@ inputs of the workload (the same x, gamma and dy draws plus a bias and
 per-row mean shifts).  Algorithmic bytes: forward 2*M*N*s + 2*N*s + 8*M
 (x, gamma, beta read; y, mean, rstd written), backward stage 1
 3*M*N*s + N*s + 8*M, stage 2 8*N (dgamma and dbeta).
+
+``--op add_rmsnorm`` measures the residual add fused with RMSNorm
+(rmsnorm_add_fwd, rmsnorm_add_bwd_rows, rmsnorm_add_bwd_reduce): forward
+4*M*N*s + N*s + 4*M (x and res read, y and h written), backward stage 1
+4*M*N*s + N*s + 4*M (dy, dh and h read, dx written), stage 2 4*N.  The
+same step unfused (torch's add, rmsnorm_fwd, rmsnorm_bwd, torch's add of
+dh) is timed beside it as ``unfused_step_us``.
 """
 import argparse
 import hashlib
@@ -72,6 +79,8 @@ def measured_traffic(workload):
 
 
 def alg_bytes(M, N, s, op="rmsnorm"):
+    if op == "add_rmsnorm":
+        return 4 * M * N * s + N * s + 4 * M, 4 * M * N * s + N * s + 4 * M, 4 * N
     if op == "layernorm":
         return 2 * M * N * s + 2 * N * s + 8 * M, 3 * M * N * s + N * s + 8 * M, 8 * N
     fwd = 2 * M * N * s + N * s + 4 * M
@@ -88,7 +97,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
-    ap.add_argument("--op", choices=("rmsnorm", "layernorm"), default="rmsnorm")
+    ap.add_argument("--op", choices=("rmsnorm", "layernorm", "add_rmsnorm"), default="rmsnorm")
     ap.add_argument("--cold-samples", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1 << 62,
@@ -114,7 +123,10 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     t0 = time.time()
     ln = args.op == "layernorm"
-    inp = (workloads.make_layernorm_inputs if ln else workloads.make_inputs)(args.workload)
+    fused = args.op == "add_rmsnorm"
+    make = {"layernorm": workloads.make_layernorm_inputs,
+            "add_rmsnorm": workloads.make_add_inputs}.get(args.op, workloads.make_inputs)
+    inp = make(args.workload)
     M, N, T, off, eps = inp["M"], inp["N"], inp["dtype"], inp["offset"], inp["eps"]
     s = torch.tensor([], dtype=T).element_size()
     x, w, dy = (inp[k].to(dev) for k in ("x", "w", "dy"))
@@ -127,13 +139,26 @@ def main():
         mean = torch.empty(M, device=dev, dtype=torch.float32)
         dbeta = torch.empty(N, device=dev, dtype=torch.float32)
         nbytes = rn.layernorm_bwd_workspace_bytes(M, N, T)
+    elif fused:
+        res, dh = inp["res"].to(dev), inp["dh"].to(dev)
+        h = torch.empty_like(x)
+        nbytes = rn.rmsnorm_add_bwd_workspace_bytes(M, N, T, off)
     else:
         nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)
     ws = torch.empty(max(4, nbytes) // 4, device=dev, dtype=torch.float32)
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    if ln:
+    if fused:
+        def fwd():
+            rn.rmsnorm_add_fwd(x, res, w, eps, y, h, rstd, off)
+
+        def bwd_rows():
+            rn.rmsnorm_add_bwd_rows(dy, dh, h, w, rstd, dx, ws, off)
+
+        def bwd_reduce():
+            rn.rmsnorm_add_bwd_reduce(ws, M, N, T, dgamma, off)
+    elif ln:
         def fwd():
             rn.layernorm_fwd(x, w, bias, eps, y, mean, rstd)
 
@@ -205,6 +230,31 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = rb / (dominant_us * 1e-6) / 1e9
 
+    # ---- the same step unfused (add kernels around the plain norm) ----
+    unfused_us = None
+    if fused:
+        h2, y2, dx2 = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+        r2 = torch.empty(M, device=dev, dtype=torch.float32)
+        dg2 = torch.empty(N, device=dev, dtype=torch.float32)
+        ws2 = torch.empty(max(4, rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)) // 4, device=dev)
+
+        def unfused_step():
+            torch.add(x, res, out=h2)
+            rn.rmsnorm_fwd(h2, w, eps, y2, r2, off)
+            rn.rmsnorm_bwd(dy, h2, w, r2, dx2, dg2, ws2, off)
+            dx2.add_(dh)
+
+        for _ in range(max(10, args.warmup // 4)):
+            unfused_step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        n_unf = max(10, args.steps // 2)
+        for _ in range(n_unf):
+            unfused_step()
+        torch.cuda.synchronize()
+        unfused_us = (time.perf_counter() - t) * 1e6 / n_unf
+        del h2, y2, dx2, ws2
+
     # ---- cold-cache per-call samples ----
     # Before each sample a 1 GiB buffer is read (not written), so L2 and the
     # 256 MB Infinity Cache hold only clean, unrelated lines.
@@ -261,7 +311,11 @@ def main():
         times = []
         for _ in range(3):
             t = time.perf_counter()
-            if ln:
+            if fused:
+                from oracle import fused as fused_oracle
+                hs, _, _ = fused_oracle.golden_add_forward(xs, inp["res"][:R], inp["w"], eps, off)
+                fused_oracle.golden_add_backward(dys, inp["dh"][:R], hs, inp["w"], eps, off)
+            elif ln:
                 ln_oracle.golden_ln_forward(xs, inp["w"], inp["b"], eps)
                 ln_oracle.golden_ln_dx(dys, xs, inp["w"], eps)
                 ln_oracle.golden_ln_param_grads(dys, xs, eps)
@@ -281,7 +335,7 @@ def main():
                         "host_cores_available": len(os.sched_getaffinity(0))}
 
     result = {
-        "metric": ("LayerNorm" if ln else "RMSNorm")
+        "metric": ("LayerNorm" if ln else "residual add + RMSNorm" if fused else "RMSNorm")
         + " fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
         "value": round(value, 1),
         "unit": "GB/s",
@@ -295,7 +349,8 @@ def main():
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[T],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {wl.description}"
-                   + (" (LayerNorm inputs)" if ln else ""), "op": args.op, "M": M, "N": N,
+                   + (" (LayerNorm inputs)" if ln else " (with res and dh)" if fused else ""),
+                   "op": args.op, "M": M, "N": N,
                    "eps": eps, "offset_weight": off, "seed": inp["seed"],
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 1),
@@ -308,11 +363,13 @@ def main():
                                             + per_kernel_us["bwd_reduce"]) * 1e-6) / 1e9, 1)},
         "cold_cache": cold,
         "device_copy_GBps": round(copy_gbs, 1),
-        "roofline": {"kernel": "ln_bwd_rows" if ln else "bwd_rows", "bound": "hbm",
+        "unfused_step_us": None if unfused_us is None else round(unfused_us, 2),
+        "roofline": {"kernel": "ln_bwd_rows" if ln else "add_bwd_rows" if fused else "bwd_rows",
+                     "bound": "hbm",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if ln else measured_traffic(args.workload),
+                     "traffic": None if (ln or fused) else measured_traffic(args.workload),
                      "alg_bytes_per_launch": rb},
         "cpu_baseline": cpu_baseline,
     }

@@ -9,6 +9,7 @@ import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from oracle import gate, golden, reference
+from oracle import fused as fusedref
 from oracle import layernorm as lnref
 
 
@@ -157,4 +158,44 @@ def gate_ln_sampled(inp, out, rows, cols):
         gate.gate_tensor("dx[rows]", out["dx"][dr].cpu(), dx_r, dx_g, T),
         gate.gate_tensor("dgamma[cols]", out["dgamma"][dc].cpu(), dg_r, dg_g, torch.float32),
         gate.gate_tensor("dbeta[cols]", out["dbeta"][dc].cpu(), db_r, db_g, torch.float32),
+    ]
+
+
+# ---- residual add fused with RMSNorm -----------------------------------------------
+
+def run_add_target(inp, device, poison=True, with_dh=True):
+    x, res, w, dy = (inp[k].to(device) for k in ("x", "res", "w", "dy"))
+    dh = inp["dh"].to(device) if with_dh else None
+    off, eps = inp["offset"], inp["eps"]
+    y, h, rstd = rn.add_fwd(x, res, w, eps, off, poison=poison)
+    dx, dg = rn.add_bwd(dy, dh, h, w, rstd, off, poison=poison)
+    torch.cuda.synchronize()
+    return {"y": y, "h": h, "rstd": rstd, "dx": dx, "dgamma": dg}
+
+
+def gate_add_full(inp, out, with_dh=True):
+    """h bit-exact (the dtype's add, taken in the same precision on both
+    sides); y, rstd, dx and dgamma through the gate."""
+    x, res, w, dy, eps, off = inp["x"], inp["res"], inp["w"], inp["dy"], inp["eps"], inp["offset"]
+    dh = inp["dh"] if with_dh else None
+    T, n = x.dtype, x.shape[-1]
+    h_o = fusedref.residual_sum(x, res)
+    h_t = out["h"].cpu()
+    h_row = gate.GateRow(tensor="h", dtype=str(T).replace("torch.", ""), shape=tuple(h_o.shape))
+    h_row.gate_valid = True
+    h_row.target_error = float((h_t.double() - h_o.double()).abs().max()) if h_o.numel() else 0.0
+    h_row.verdict = "PASS" if torch.equal(h_t, h_o) else "FAIL"
+    h_row.note = "bitwise equal to the dtype's add"
+    _, y_r, r_r = fusedref.reference_add_forward(x, res, w, eps, off)
+    _, y_g, r_g = fusedref.golden_add_forward(x, res, w, eps, off)
+    dx_r, dg_r = fusedref.reference_add_backward(dy, dh, h_o, w, eps, off)
+    dx_g, dg_g = fusedref.golden_add_backward(dy, dh, h_o, w, eps, off)
+    worst = int(np.argmax(np.abs(out["dgamma"].double().cpu().numpy() - dg_g))) if n else 0
+    cond = golden.dgamma_condition(dy, h_o, eps, worst) if x.numel() else None
+    return [
+        h_row,
+        gate.gate_tensor("y", out["y"].cpu().reshape(-1, n), y_r, y_g, T),
+        gate.gate_rstd(out["rstd"].cpu(), r_g, r_r),
+        gate.gate_tensor("dx", out["dx"].cpu().reshape(-1, n), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32, condition=cond),
     ]

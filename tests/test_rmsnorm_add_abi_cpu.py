@@ -1,0 +1,90 @@
+"""Fused residual-add RMSNorm entry points (include/rmsnorm_add.h) on the
+host: argument checks and plans, no device work.  Every call below is
+invalid in exactly one way, so nothing is ever launched on the fake
+addresses."""
+import os
+
+import pytest
+
+import backward_rmsnorm_fwd_amd as rn
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rn.library_path()),
+                                reason="librmsnorm.so not built")
+
+OK, ENULL, EDTYPE, ESHAPE, EEPS, EFLAGS, EWS, EALIGN, EOVL = 0, -1, -2, -3, -4, -5, -6, -7, -8
+ESTRIDE = -11
+A = 0x10000000
+S = 1 << 24
+
+
+def lib():
+    return rn.load_library()
+
+
+def fwd_call(x=A, res=A + S, g=A + 2 * S, eps=1e-6, M=4, N=256, dtype=2, flags=0, y=A + 3 * S,
+             h=A + 4 * S, rstd=A + 5 * S, ldr=None, ldh=None):
+    ldr = N if ldr is None else ldr
+    ldh = N if ldh is None else ldh
+    return lib().rmsnorm_add_fwd(x, N, res, ldr, g, eps, M, N, dtype, flags, y, N, h, ldh, rstd,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 3}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": 0}, ESHAPE), ({"N": 16385}, ESHAPE),
+    ({"eps": -1.0}, EEPS), ({"ldr": 10}, ESTRIDE), ({"ldh": 255}, ESTRIDE),
+    ({"x": None}, ENULL), ({"res": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL),
+    ({"h": None}, ENULL), ({"rstd": None}, ENULL),
+    ({"res": A + S + 1}, EALIGN), ({"h": A + 4 * S + 1}, EALIGN),
+    ({"h": A + 64}, EOVL),                # h overlaps x
+    ({"h": A + S + 32}, EOVL),            # h overlaps res (in place is not accepted)
+    ({"y": A + 4 * S + 8}, EOVL),         # y overlaps h
+    ({"rstd": A + 2 * S}, EOVL),          # rstd overlaps gamma
+])
+def test_fwd_rejects(kw, code):
+    assert fwd_call(**kw) == code
+
+
+def test_fwd_m0_is_a_noop():
+    assert fwd_call(M=0, x=None, res=None, g=None, y=None, h=None, rstd=None) == OK
+
+
+def bwd_call(dy=A, dh=A + S, h=A + 2 * S, g=A + 3 * S, rstd=A + 4 * S, M=4, N=256, dtype=2,
+             flags=0, dx=A + 5 * S, dg=A + 6 * S, ws=A + 7 * S, ws_bytes=None, lddh=None):
+    if ws_bytes is None:
+        ws_bytes = lib().rmsnorm_add_bwd_workspace_bytes(M, N, dtype, flags)
+    lddh = N if lddh is None else lddh
+    return lib().rmsnorm_add_bwd(dy, N, dh, lddh, h, N, g, rstd, M, N, dtype, flags, dx, N, dg,
+                                 ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 7}, EDTYPE), ({"flags": 8}, EFLAGS), ({"N": 20000}, ESHAPE),
+    ({"lddh": 3}, ESTRIDE),
+    ({"dy": None}, ENULL), ({"h": None}, ENULL), ({"g": None}, ENULL), ({"rstd": None}, ENULL),
+    ({"dx": None}, ENULL), ({"dg": None}, ENULL),
+    ({"ws": None}, EWS), ({"ws_bytes": 8}, EWS), ({"ws": A + 7 * S + 8}, EALIGN),
+    ({"dh": A + S + 1}, EALIGN),
+    ({"dx": A + S + 16}, EOVL),           # dx overlaps dh
+    ({"dx": A + 2 * S}, EOVL),            # dx overlaps h
+    ({"dg": A + 4 * S + 4}, EOVL),        # dgamma overlaps rstd
+    ({"ws": A + 5 * S + 512}, EOVL),      # workspace overlaps dx
+])
+def test_bwd_rejects(kw, code):
+    assert bwd_call(**kw) == code
+
+
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_plans_follow_the_row_resident_plan(dt):
+    for n in (1, 128, 1000, 4096, 4097, 5120, 16384):
+        for m in (1, 1000, 32768):
+            for which in (rn.PASS_FWD, rn.PASS_BWD_ROWS, rn.PASS_BWD_REDUCE):
+                a = rn.rmsnorm_add_query_plan(m, n, dt, which=which)
+                b = rn.layernorm_query_plan(m, n, dt, which=which)
+                for k in ("vec", "threads_per_row", "block_threads", "chunks", "grid",
+                          "partials", "lds_bytes"):
+                    assert a[k] == b[k], (n, m, which, k)
+                want = {rn.PASS_FWD: "add_fwd", rn.PASS_BWD_ROWS: "add_bwd"}.get(which)
+                if want:
+                    assert a["kernel_name"] == want
+            P = rn.rmsnorm_add_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)["partials"]
+            assert rn.rmsnorm_add_bwd_workspace_bytes(m, n, dt) == P * n * 4
