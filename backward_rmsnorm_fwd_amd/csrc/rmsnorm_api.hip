@@ -109,6 +109,15 @@ bool listed_bwd(const Cfg& c) {
 
 Cfg plan_fast_fwd(int64_t nvec) {
   Cfg c{true, 1, 1, 256, 1, 0};
+  if (nvec == 640) {
+    // Rows of 640 vectors (bf16 5120): 5 wavefronts x 2 chunks fill the row
+    // exactly; 210.5 us against 215.9 us for 4 x 3 in the 65536 x 5120 step.
+    c.wpr = 5;
+    c.ch = 2;
+    c.block = 640;
+    c.ok = listed_fwd(c);
+    return c;
+  }
   c.wpr = std::min(8, pow2_at_most(std::max<int64_t>(1, nvec / 128)));
   c.ch = static_cast<int>(ceil_div(nvec, 64 * c.wpr));
   if (c.ch > 16) {
@@ -196,6 +205,15 @@ PipeCfg plan_pipe_bwd(int64_t nvec) {
   PipeCfg c{false, 1, 1, 1024, 0};
   if (nvec <= 256) {
     c.wpr = pow2_at_least(ceil_div(nvec, 64));
+  } else if (nvec == 640) {
+    // Rows of 640 vectors (bf16 5120): 10 wavefronts x 1 chunk in a
+    // 640-thread workgroup fill the row exactly, where 16 wavefronts leave
+    // 384 of 1024 lanes idle; 332.5 us against 362.5 us for stage 1 in the
+    // 65536 x 5120 step (step 547.2 against 577.2 us).  512 workgroups
+    // instead of 256 measured slower (394.5 us).
+    c.wpr = 10;
+    c.block = 640;
+    c.lds_flag = 1;
   } else if (nvec > 512 && nvec <= 1024) {
     c.wpr = 16;
     c.lds_flag = 1;

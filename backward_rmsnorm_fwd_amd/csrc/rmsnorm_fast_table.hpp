@@ -16,6 +16,7 @@
 #pragma once
 
 #define RMSNORM_FWD_FAST_LIST(X)                                                  \
+  X(5, 2, 640, 1)                                                                 \
   X(1, 1, 256, 1) X(1, 2, 256, 1) X(1, 3, 256, 1) X(1, 4, 256, 1)                 \
   X(2, 2, 256, 1) X(2, 3, 256, 1) X(2, 4, 256, 1)                                 \
   X(4, 2, 512, 1) X(4, 3, 512, 1) X(4, 4, 512, 1)                                 \
@@ -31,7 +32,7 @@
 #define RMSNORM_FWD_PIPE_LIST(X) X(2, 3, 1024, 1) X(2, 4, 1024, 1)
 
 #define RMSNORM_BWD_PIPE_LIST(X) \
-  X(1, 1, 1024, 0) X(2, 1, 1024, 0) X(4, 1, 1024, 0) X(16, 1, 1024, 1)
+  X(1, 1, 1024, 0) X(2, 1, 1024, 0) X(4, 1, 1024, 0) X(16, 1, 1024, 1) X(10, 1, 640, 1)
 
 #define RMSNORM_BWD_LONG_LIST(X) \
   X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)

@@ -220,10 +220,12 @@ def test_plans_for_the_workloads():
     assert c4["chunks"] == 16 and c4["partials"] == 256
     assert c4["x_in_lds"] == 1 and c4["lds_bytes"] == 65536 * 2
     c5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_BWD_ROWS)
-    assert c5["kernel_name"] == "bwd_pipe" and (c5["threads_per_row"], c5["chunks"]) == (1024, 1)
+    assert c5["kernel_name"] == "bwd_pipe" and (c5["threads_per_row"], c5["chunks"]) == (640, 1)
+    assert c5["block_threads"] == 640
     assert c5["dy_in_lds"] == 1 and c5["partials"] == 256 and c5["lds_bytes"] == 2 * 2 * 5120 * 2
     f5 = rn.rmsnorm_query_plan(65536, 5120, 2, offset=True, which=rn.PASS_FWD)
-    assert f5["kernel_name"] == "fwd_rows" and (f5["threads_per_row"], f5["chunks"]) == (256, 3)
+    assert f5["kernel_name"] == "fwd_rows" and (f5["threads_per_row"], f5["chunks"]) == (320, 2)
+    assert f5["block_threads"] == 640
     # odd N forces element-wide accesses; misaligned pointers narrow the vector
     odd = rn.rmsnorm_query_plan(3, 257, 2, which=rn.PASS_FWD)
     assert odd["vec"] == 1 and odd["kernel_name"] == "fwd_wave"

@@ -44,7 +44,8 @@ TILE_CASES = [((3, 255), torch.float32, 1), ((3, 256), torch.bfloat16, 2),
               ((8, 5120), torch.bfloat16, 8), ((37, 2048), torch.float32, 12),
               ((13, 1100), torch.float32, 13), ((11, 3000), torch.float16, 14),
               ((7, 8200), torch.bfloat16, 15), ((6, 20000), torch.float32, 16),
-              ((5, 40000), torch.float16, 17)]
+              ((5, 40000), torch.float16, 17), ((9, 2560), torch.float32, 18),
+              ((9, 5120), torch.float16, 19)]
 
 
 @pytest.mark.parametrize("shape,dtype,seed", TILE_CASES)
