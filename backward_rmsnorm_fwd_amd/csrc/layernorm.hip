@@ -18,10 +18,13 @@
 //   backward  xhat = (x - mu)*r;  u = dy*gamma
 //             dx = r*((u - sum(u)/N) - xhat*(sum(u*xhat)/N))
 //             dgamma += dy*xhat;  dbeta += dy   (column sums over rows)
-// The backward recomputes the row sum of x in float64 alongside sum(u) and
-// sum(u*(x - mean)) (one exchange) and takes the offset c = sum/N - mean of
-// the stored float32 mean out of x - mean, as the forward does: with
-// xhat = ((x - mean) - c)*r, sum(u*xhat) = r*(sum(u*(x - mean)) - c*sum(u)).
+// The backward takes the offset c = sum(x)/N - mean of the stored float32
+// mean out of x - mean, as the forward does, with c = sum(x - mean)/N from
+// the float32 deviations d = x - mean: where the mean is large against the
+// spread d is exact (x and mean within a factor of two), and elsewhere c is
+// below the rounding of xhat anyway.  With xhat = (d - c)*r,
+// sum(u*xhat) = r*(sum(u*d) - c*sum(u)).  sum(u), sum(u*d) and sum(d) share
+// one exchange.
 //
 // Geometry: a row is spread over `wpr` wavefronts (64*wpr lanes, a power of
 // two up to 16); lane t of a row owns vectors c*64*wpr + t for c < chunks,
@@ -46,7 +49,6 @@ namespace rmsnorm_hip {
 namespace {
 
 using namespace rowres;
-constexpr int kLnMaxBlock = kRowMaxBlock;
 constexpr int kLnWaves = kRowWaves;
 
 // BLK: 256 for 256-thread workgroups (at least 3 wavefronts per SIMD, up to
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
 }
 
 template <int DT, int VEC, int MAXC, int BLK>
-__global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
+__global__ __launch_bounds__(BLK, BLK == 256 ? 2 : 1) void ln_bwd_kernel(
     const void* __restrict__ dy, const void* __restrict__ x, const void* __restrict__ gamma,
     const float* __restrict__ mean, const float* __restrict__ rstd, void* __restrict__ dx,
     float* __restrict__ part, int64_t M, int N, int chunks, int wpr, int64_t P, int64_t lddy,
@@ -166,11 +168,11 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
 #pragma clang fp contract(off)
   using PK = Pack<DT, VEC>;
   constexpr int R = rows_per_step<DT, VEC, MAXC, 2, BLK>();
+  constexpr bool kTwoSets = BLK == 256;  // larger workgroups have 128 VGPRs: one set
   extern __shared__ __align__(16) float comb[];  // [blockDim.x * VEC] when G > 1
-  __shared__ float slots[2 * kLnWaves * 2 * R];
-  __shared__ double slots64[2 * kLnWaves * R];
+  __shared__ float slots[2 * kLnWaves * 3 * R];
   const RowGeom rg = row_geom(wpr);
-  const float n_f = static_cast<float>(N);
+  const float inv_n = 1.0f / static_cast<float>(N);
   int parity = 0;
   const int64_t w = blockIdx.x;
   const int64_t r0 = block_row_begin(w, M, P);
@@ -187,72 +189,107 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
 #pragma unroll
     for (int k = 0; k < VEC; ++k) ag[c][k] = ab[c][k] = 0.f;
   }
-  for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) g[c].opaque();
-    int64_t row[R];
-    bool active[R];
-    float mu[R], r[R];
+
+  // The rows of one step, held in registers.  In 256-thread workgroups two
+  // sets alternate: the next step's loads are issued into one while the
+  // other is reduced and written, so every row group keeps a step of loads
+  // in flight across its barriers.  Those loads carry no condition (a row
+  // past the workgroup's range reads its last row, a lane past the row reads
+  // the row's first vector, and both are masked where the values are used),
+  // so the compiler can count them and wait for the older set alone.  With
+  // one set, out-of-row lanes skip their loads and hold zeros.
+  struct Rows {
     PK dv[R][MAXC], xv[R][MAXC];
+    float mu[R], r[R];
+  };
+  auto row_of = [&](int64_t it, int j) __attribute__((always_inline)) {
+    return r0 + it * step + j * rg.G + rg.group;
+  };
+  auto load_rows = [&](int64_t it, Rows& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      row[j] = r0 + it * step + j * rg.G + rg.group;
-      active[j] = row[j] < r1;
-      mu[j] = active[j] ? mean[row[j]] : 0.f;
-      r[j] = active[j] ? rstd[row[j]] : 0.f;
-      const char* dyr = row_base<DT>(dy, row[j], lddy);
-      const char* xr = row_base<DT>(x, row[j], ldx);
+      const int64_t row = row_of(it, j);
+      const int64_t rr = row < r1 ? row : r1 - 1;
+      s.mu[j] = mean[rr];
+      s.r[j] = rstd[rr];
+      const char* dyr = row_base<DT>(dy, rr, lddy);
+      const char* xr = row_base<DT>(x, rr, ldx);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = (c * rg.tpr + rg.t) * VEC;
-        dv[j][c].zero();
-        xv[j][c].zero();
-        if (active[j] && c < chunks && e < N) {
-          ld<DT, VEC, true>(dv[j][c], dyr, e);
-          ld<DT, VEC, true>(xv[j][c], xr, e);
+        if constexpr (kTwoSets) {
+          const int el = c < chunks && e < N ? e : 0;
+          ld<DT, VEC, true>(s.dv[j][c], dyr, el);
+          ld<DT, VEC, true>(s.xv[j][c], xr, el);
+        } else if (c < chunks && e < N) {
+          ld<DT, VEC, true>(s.dv[j][c], dyr, e);
+          ld<DT, VEC, true>(s.xv[j][c], xr, e);
+        } else {
+          s.dv[j][c].zero();
+          s.xv[j][c].zero();
         }
       }
     }
-    // Lanes past N hold x = dy = 0, so they add 0 to every sum.
-    double sx[R];
-    float s12[2 * R];
+  };
+  auto process = [&](int64_t it, Rows& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      g[c].opaque();
+      const int e = (c * rg.tpr + rg.t) * VEC;
+      if (kTwoSets && !(c < chunks && e < N)) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          s.dv[j][c].zero();
+          s.xv[j][c].zero();
+        }
+      }
+    }
+    // Lanes past N hold x = dy = 0 and add 0 to sum(u) and sum(u*d); their
+    // d = -mean is left out of sum(d).
+    float sums[3 * R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      sx[j] = 0.0;
-      float s1 = 0.f, s2 = 0.f;
+      float s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c)
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = (c * rg.tpr + rg.t) * VEC;
+        float t = 0.f;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-          const float xf = xv[j][c].get(k);
-          const float u = dv[j][c].get(k) * g[c].get(k);
-          sx[j] += static_cast<double>(xf);
+          const float d = s.xv[j][c].get(k) - s.mu[j];
+          const float u = s.dv[j][c].get(k) * g[c].get(k);
           s1 += u;
-          s2 = fmaf(u, xf - mu[j], s2);
+          s2 = fmaf(u, d, s2);
+          t += d;
         }
-      s12[2 * j] = s1;
-      s12[2 * j + 1] = s2;
+        if (c < chunks && e < N) s3 += t;
+      }
+      sums[3 * j] = s1;
+      sums[3 * j + 1] = s2;
+      sums[3 * j + 2] = s3;
     }
-    row_sums<R, 2 * R, R, 2 * R>(sx, s12, slots64, slots, parity, wpr, rg);
+    row_sums<0, 3 * R, 1, 3 * R>(nullptr, sums, nullptr, slots, parity, wpr, rg);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
-        dv[j][c].opaque();
-        xv[j][c].opaque();
+        s.dv[j][c].opaque();
+        s.xv[j][c].opaque();
       }
     }
     // Rows in order (j = 0, 1, ...), so each column sum adds its rows in
     // row order.
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (!active[j]) continue;
-      const float cm = static_cast<float>(sx[j] / static_cast<double>(N) -
-                                          static_cast<double>(mu[j]));
-      const float s1 = s12[2 * j], s2 = s12[2 * j + 1];
-      const float c1 = s1 / n_f;
-      const float c2 = (r[j] * (s2 - cm * s1)) / n_f;
-      const char* dxr = row_base<DT>(dx, row[j], lddx);
+      const int64_t row = row_of(it, j);
+      if (row >= r1) continue;
+      const float mu = s.mu[j], r = s.r[j];
+      const float s1 = sums[3 * j], s2 = sums[3 * j + 1];
+      const float cm = sums[3 * j + 2] * inv_n;
+      const float c1 = s1 * inv_n;
+      const float c2 = (r * (s2 - cm * s1)) * inv_n;
+      const float rcm = r * cm;
+      const char* dxr = row_base<DT>(dx, row, lddx);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = (c * rg.tpr + rg.t) * VEC;
@@ -260,10 +297,10 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
           float o[VEC];
 #pragma unroll
           for (int k = 0; k < VEC; ++k) {
-            const float dyf = dv[j][c].get(k);
-            const float xh = ((xv[j][c].get(k) - mu[j]) - cm) * r[j];
+            const float dyf = s.dv[j][c].get(k);
+            const float xh = fmaf(s.xv[j][c].get(k) - mu, r, -rcm);
             const float u = dyf * g[c].get(k);
-            o[k] = r[j] * ((u - c1) - xh * c2);
+            o[k] = r * fmaf(-xh, c2, u - c1);
             ag[c][k] = fmaf(dyf, xh, ag[c][k]);
             ab[c][k] += dyf;
           }
@@ -273,6 +310,31 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
         }
       }
     }
+  };
+
+  Rows a;
+  if constexpr (kTwoSets) {
+    Rows b;
+    int64_t it = 0;
+    if (iters > 0) load_rows(0, a);
+    for (; it + 2 < iters; it += 2) {
+      load_rows(it + 1, b);
+      process(it, a);
+      load_rows(it + 2, a);
+      process(it + 1, b);
+    }
+    if (it + 1 < iters) {
+      load_rows(it + 1, b);
+      process(it, a);
+      process(it + 1, b);
+    } else if (it < iters) {
+      process(it, a);
+    }
+  } else {
+    for (int64_t it = 0; it < iters; ++it) {
+      load_rows(it, a);
+      process(it, a);
+    }
   }
 
   // Column sums of the G row groups, added in group order: dgamma partials
@@ -281,7 +343,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_bwd_kernel(
     float* dst = part + (which * P + w) * static_cast<int64_t>(N);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      if (c >= chunks) break;  // uniform: chunks is a kernel argument
+      if (c >= chunks) continue;  // uniform: chunks is a kernel argument
       const int e = (c * rg.tpr + rg.t) * VEC;
       float v[VEC];
 #pragma unroll

@@ -890,7 +890,7 @@ int bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const voi
 // Workgroups of 256 threads (64*wpr for rows over more than four
 // wavefronts): several per compute unit, so one waiting at a row barrier
 // does not idle the unit.
-constexpr int64_t kLnFwdWorkgroups = 2048;  // of 256 threads; fewer when larger
+constexpr int64_t kLnFwdWorkgroups = 8192;  // of 256 threads; fewer when larger
 constexpr int64_t kLnBwdWorkgroups = 512;
 
 LnPlan ln_plan(int64_t M, int64_t N, int es, bool backward, int align) {

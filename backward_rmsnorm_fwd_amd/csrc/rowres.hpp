@@ -72,12 +72,44 @@ __device__ __forceinline__ RowGeom row_geom(int wpr) {
   return g;
 }
 
+// Adds slot[first], ..., slot[first + W - 1] in that order.  With a
+// compile-time W every LDS read is issued before the first is needed; W = 0
+// takes the count `w` at run time (one read at a time, few registers: the
+// wide rows of 512- and 1024-thread workgroups, whose register budget is
+// already spent on the row).
+template <int W, typename T>
+__device__ __forceinline__ T sum_slots(const T* slot, int first, int w) {
+  if constexpr (W == 0) {
+    T t = slot[first];
+    for (int i = 1; i < w; ++i) t += slot[first + i];
+    return t;
+  } else {
+    T v[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = slot[first + i];
+    T t = v[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) t += v[i];
+    return t;
+  }
+}
+
+template <int W, int KD, int KF>
+__device__ __forceinline__ void gather_sums(double* a, float* b, const double* d,
+                                            const float* f, int first, int w) {
+#pragma unroll
+  for (int i = 0; i < KD; ++i) a[i] = sum_slots<W>(d + i * kRowWaves, first, w);
+#pragma unroll
+  for (int i = 0; i < KF; ++i) b[i] = sum_slots<W>(f + i * kRowWaves, first, w);
+}
+
 // KD float64 and KF float32 row sums in one exchange.  The slot arrays are
-// [2][kRowWaves][SD] doubles and [2][kRowWaves][SF] floats with the same
+// [2][SD][kRowWaves] doubles and [2][SF][kRowWaves] floats with the same
 // SD >= KD, SF >= KF in every call of a kernel, so the two parity halves are
 // disjoint whatever KD and KF are: an exchange writes only the half the
 // previous one did not read, and the half it reads is rewritten two
-// exchanges later, after a barrier every reader has passed.
+// exchanges later, after a barrier every reader has passed.  Sum i of wave
+// w sits at [i][w], so a row's wpr partial sums are adjacent.
 template <int KD, int KF, int SD, int SF>
 __device__ __forceinline__ void row_sums(double* a, float* b, double* s64, float* s32,
                                          int& parity, int wpr, const RowGeom& rg) {
@@ -87,36 +119,23 @@ __device__ __forceinline__ void row_sums(double* a, float* b, double* s64, float
 #pragma unroll
   for (int i = 0; i < KF; ++i) b[i] = wave_sum(b[i]);
   if (wpr == 1) return;
+  double* d = KD > 0 ? s64 + parity * kRowWaves * SD : nullptr;
+  float* f = KF > 0 ? s32 + parity * kRowWaves * SF : nullptr;
   if (rg.lane == 0) {
     if constexpr (KD > 0) {
-      double* d = s64 + parity * kRowWaves * SD;
 #pragma unroll
-      for (int i = 0; i < KD; ++i) d[rg.wave * SD + i] = a[i];
+      for (int i = 0; i < KD; ++i) d[i * kRowWaves + rg.wave] = a[i];
     }
     if constexpr (KF > 0) {
-      float* f = s32 + parity * kRowWaves * SF;
 #pragma unroll
-      for (int i = 0; i < KF; ++i) f[rg.wave * SF + i] = b[i];
+      for (int i = 0; i < KF; ++i) f[i * kRowWaves + rg.wave] = b[i];
     }
   }
   __syncthreads();
-  if constexpr (KD > 0) {
-    const double* d = s64 + parity * kRowWaves * SD;
-#pragma unroll
-    for (int i = 0; i < KD; ++i) {
-      double t = 0.0;
-      for (int w = 0; w < wpr; ++w) t += d[(rg.first_wave + w) * SD + i];
-      a[i] = t;
-    }
-  }
-  if constexpr (KF > 0) {
-    const float* f = s32 + parity * kRowWaves * SF;
-#pragma unroll
-    for (int i = 0; i < KF; ++i) {
-      float t = 0.f;
-      for (int w = 0; w < wpr; ++w) t += f[(rg.first_wave + w) * SF + i];
-      b[i] = t;
-    }
+  switch (wpr) {  // uniform across the workgroup
+    case 2: gather_sums<2, KD, KF>(a, b, d, f, rg.first_wave, 2); break;
+    case 4: gather_sums<4, KD, KF>(a, b, d, f, rg.first_wave, 4); break;
+    default: gather_sums<0, KD, KF>(a, b, d, f, rg.first_wave, wpr); break;
   }
   parity ^= 1;
 }
