@@ -136,11 +136,13 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_bwd_kernel(
   const RowGeom rg = row_geom(wpr);
   const float n_f = static_cast<float>(N);
   int parity = 0;
+  // Steps of G*R consecutive rows; workgroup w takes steps w, w+P, w+2P, ...
+  // (one contiguous window of the matrices at a time across the grid), and
+  // each row group adds its rows to the column sums in row order.
   const int64_t w = blockIdx.x;
-  const int64_t r0 = block_row_begin(w, M, P);
-  const int64_t r1 = block_row_begin(w + 1, M, P);
   const int64_t step = static_cast<int64_t>(rg.G) * R;
-  const int64_t iters = (r1 - r0 + step - 1) / step;
+  const int64_t nsteps = (M + step - 1) / step;
+  const int64_t iters = w < nsteps ? (nsteps - w + P - 1) / P : 0;
   const bool has_dh = dh != nullptr;
   PK g[MAXC];
   float acc[MAXC][VEC];
@@ -161,8 +163,8 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_bwd_kernel(
     PK dv[R][MAXC], hv[R][MAXC], ev[R][MAXC];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      row[j] = r0 + it * step + j * rg.G + rg.group;
-      active[j] = row[j] < r1;
+      row[j] = (it * P + w) * step + j * rg.G + rg.group;
+      active[j] = row[j] < M;
       r[j] = active[j] ? rstd[row[j]] : 0.f;
       const char* dyr = row_base<DT>(dy, row[j], lddy);
       const char* hr = row_base<DT>(h, row[j], ldh);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_bwd_kernel(
   float* dst = part + w * static_cast<int64_t>(N);
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    if (c >= chunks) break;  // uniform: chunks is a kernel argument
+    if (c >= chunks) continue;  // uniform: chunks is a kernel argument
     const int e = (c * rg.tpr + rg.t) * VEC;
     if (rg.G == 1) {
       if (e < N) store_f32<VEC>(dst + e, acc[c]);

@@ -32,10 +32,12 @@
 // 64*wpr for longer rows; at most 1024) holds G = B/(64*wpr) rows at a time.  Elements past N are loaded as 0 and left out of
 // the variance and of every store.
 //
-// Backward stage 1: workgroup w owns rows [w*M/P, (w+1)*M/P) (its G row
-// groups take them in turn), accumulates the column sums of dy*xhat and dy in
-// float32 registers, adds its G groups in group order through LDS and writes
-// part[w, :] (dgamma) and part[P + w, :] (dbeta).  Stage 2 adds each [P, N]
+// Backward stage 1: the rows are cut into steps of G*R consecutive rows (R
+// rows per row group) and workgroup w takes steps w, w+P, w+2P, ..., so the
+// P workgroups stream one contiguous window of the matrices at a time.  It
+// accumulates the column sums of dy*xhat and dy in float32 registers (each
+// row group adds its rows in row order), adds its G groups in group order
+// through LDS and writes part[w, :] (dgamma) and part[P + w, :] (dbeta).  Stage 2 adds each [P, N]
 // block by column in float64 (the RMSNorm reduce kernels).
 #include <hip/hip_runtime.h>
 
@@ -175,10 +177,9 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 2 : 1) void ln_bwd_kernel(
   const float inv_n = 1.0f / static_cast<float>(N);
   int parity = 0;
   const int64_t w = blockIdx.x;
-  const int64_t r0 = block_row_begin(w, M, P);
-  const int64_t r1 = block_row_begin(w + 1, M, P);
   const int64_t step = static_cast<int64_t>(rg.G) * R;
-  const int64_t iters = (r1 - r0 + step - 1) / step;
+  const int64_t nsteps = (M + step - 1) / step;
+  const int64_t iters = w < nsteps ? (nsteps - w + P - 1) / P : 0;
   PK g[MAXC];
   float ag[MAXC][VEC], ab[MAXC][VEC];
 #pragma unroll
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 2 : 1) void ln_bwd_kernel(
   // sets alternate: the next step's loads are issued into one while the
   // other is reduced and written, so every row group keeps a step of loads
   // in flight across its barriers.  Those loads carry no condition (a row
-  // past the workgroup's range reads its last row, a lane past the row reads
+  // past the matrix reads its last row, a lane past the row reads
   // the row's first vector, and both are masked where the values are used),
   // so the compiler can count them and wait for the older set alone.  With
   // one set, out-of-row lanes skip their loads and hold zeros.
@@ -203,13 +204,13 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 2 : 1) void ln_bwd_kernel(
     float mu[R], r[R];
   };
   auto row_of = [&](int64_t it, int j) __attribute__((always_inline)) {
-    return r0 + it * step + j * rg.G + rg.group;
+    return (it * P + w) * step + j * rg.G + rg.group;
   };
   auto load_rows = [&](int64_t it, Rows& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int64_t row = row_of(it, j);
-      const int64_t rr = row < r1 ? row : r1 - 1;
+      const int64_t rr = row < M ? row : M - 1;
       s.mu[j] = mean[rr];
       s.r[j] = rstd[rr];
       const char* dyr = row_base<DT>(dy, rr, lddy);
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 2 : 1) void ln_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int64_t row = row_of(it, j);
-      if (row >= r1) continue;
+      if (row >= M) continue;
       const float mu = s.mu[j], r = s.r[j];
       const float s1 = sums[3 * j], s2 = sums[3 * j + 1];
       const float cm = sums[3 * j + 2] * inv_n;
