@@ -131,3 +131,18 @@ def test_query_plan_rejects():
     assert L.layernorm_query_plan(4, 256, 2, 0, 0, 16, None) == ENULL
     assert rn.layernorm_bwd_workspace_bytes(0, 256, 2) == 0
     assert rn.layernorm_bwd_workspace_bytes(4, 16385, 2) == 0
+
+
+@pytest.mark.parametrize("dt,n,tpr,ch", [(2, 5120, 320, 2), (1, 5120, 320, 2), (0, 5120, 320, 4),
+                                         (1, 12288, 768, 2), (2, 4096, 256, 2), (0, 16384, 1024, 4)])
+def test_backward_exact_fit(dt, n, tpr, ch):
+    """Rows wider than four wavefronts whose 64-lane sweeps the power-of-two
+    plan would leave partly idle take the fewest wavefronts (over four) that
+    divide them exactly; the forward keeps its power-of-two plan."""
+    p = rn.layernorm_query_plan(65536, n, dt, which=rn.PASS_BWD_ROWS)
+    assert (p["threads_per_row"], p["chunks"], p["block_threads"]) == (tpr, ch, max(256, tpr))
+    assert p["threads_per_row"] * p["chunks"] * p["vec"] == n
+    a = rn.rmsnorm_add_query_plan(65536, n, dt, which=rn.PASS_BWD_ROWS)
+    assert (a["threads_per_row"], a["chunks"]) == (tpr, ch)
+    f = rn.layernorm_query_plan(65536, 5120, 2, which=rn.PASS_FWD)
+    assert (f["threads_per_row"], f["chunks"], f["block_threads"]) == (256, 3, 256)
