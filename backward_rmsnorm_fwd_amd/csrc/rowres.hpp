@@ -169,13 +169,17 @@ __device__ __forceinline__ void st(const Pack<DT, VEC>& v, const char* row, int 
 // VGPRs per row in 256-thread workgroups (8 in larger ones, whose register
 // budget is 128): both rows' loads are then in flight at once and their
 // reductions share one exchange.  Else one.
-template <int DT, int VEC, int MAXC, int MATRICES, int BLK>
-constexpr int rows_per_step() {
-  constexpr int regs = (VEC * ElemBytes<DT>::value + 3) / 4;
-  return MAXC * regs * MATRICES <= (BLK == 256 ? 16 : 8) ? 2 : 1;
+__host__ __device__ constexpr int row_step_rows(int vec_bytes, int maxc, int matrices,
+                                                 bool blk256) {
+  return maxc * ((vec_bytes + 3) / 4) * matrices <= (blk256 ? 16 : 8) ? 2 : 1;
 }
 
-inline int pow2_ceil(int v) {
+template <int DT, int VEC, int MAXC, int MATRICES, int BLK>
+constexpr int rows_per_step() {
+  return row_step_rows(VEC * ElemBytes<DT>::value, MAXC, MATRICES, BLK == 256);
+}
+
+__host__ __device__ constexpr int pow2_ceil(int v) {
   int p = 1;
   while (p < v) p <<= 1;
   return p;

@@ -80,9 +80,24 @@ def test_plans_follow_the_row_resident_plan(dt):
             for which in (rn.PASS_FWD, rn.PASS_BWD_ROWS, rn.PASS_BWD_REDUCE):
                 a = rn.rmsnorm_add_query_plan(m, n, dt, which=which)
                 b = rn.layernorm_query_plan(m, n, dt, which=which)
-                for k in ("vec", "threads_per_row", "block_threads", "chunks", "grid",
-                          "partials", "lds_bytes"):
+                keys = ["vec", "threads_per_row", "block_threads", "chunks", "partials",
+                        "lds_bytes"] + ([] if which == rn.PASS_FWD else ["grid"])
+                for k in keys:
                     assert a[k] == b[k], (n, m, which, k)
+                if which == rn.PASS_FWD:
+                    # One row step per workgroup: G row groups x R rows, where a
+                    # row group takes two rows per step when their operands fit
+                    # in 16 VGPRs (8 in workgroups over 256 threads); LayerNorm
+                    # reads one row operand, the fused add two.
+                    es = 4 if dt == 0 else 2
+                    G = b["block_threads"] // b["threads_per_row"]
+                    maxc = 1 << (b["chunks"] - 1).bit_length()
+                    regs = -(-(b["vec"] * es) // 4)
+                    lim = 16 if b["block_threads"] == 256 else 8
+                    cap = 65536 * 256 // b["block_threads"]
+                    for plan, mats in ((b, 1), (a, 2)):
+                        R = 2 if maxc * regs * mats <= lim else 1
+                        assert plan["grid"] == min(-(-m // (G * R)), cap), (n, m, mats)
                 want = {rn.PASS_FWD: "add_fwd", rn.PASS_BWD_ROWS: "add_bwd"}.get(which)
                 if want:
                     assert a["kernel_name"] == want
