@@ -229,3 +229,25 @@ def make_add_inputs(name, M=None, N=None, seed=None, dtype=None):
     T = out["dtype"]
     out.update(x=_cast(x, T), w=_cast(g, T), dy=_cast(dy, T), res=_cast(res, T), dh=_cast(dh, T))
     return out
+
+
+def make_cast_inputs(name, M=None, N=None, seed=None, out_dtype=torch.bfloat16):
+    """Inputs of RMSNorm with its output cast to ``out_dtype`` for workload
+    ``name``: the recipe's draws (x, weight, dy, in that order), with x and
+    the weight in float32 (the wide input) and dy in ``out_dtype`` (the
+    gradient arrives in the dtype the forward wrote).  Returns the dict of
+    ``make_inputs`` with ``dtype`` float32 plus ``out_dtype``."""
+    out, arrays, _ = _draw(name, M, N, seed, torch.float32)
+    x, g, dy = arrays
+    out.update(x=_cast(x, torch.float32), w=_cast(g, torch.float32), dy=_cast(dy, out_dtype),
+               out_dtype=out_dtype)
+    return out
+
+
+def make_cast_tile_case(shape, out_dtype, seed, scale=1.0):
+    """``make_tile_case`` for the cast path: float32 x and gamma, dy in
+    ``out_dtype``."""
+    case = make_tile_case(shape, torch.float32, seed, scale)
+    case["dy"] = case["dy"].to(out_dtype)
+    case["out_dtype"] = out_dtype
+    return case

@@ -17,12 +17,18 @@ page, section "核心方法" (core method): golden / reference / target):
                    same-precision implementation gets to the golden.
 * ``layernorm`` -- the same two roles (float64 golden, float32 same-dtype
                    reference) for LayerNorm, the sibling operation.
+* ``fused``     -- the neighbours fused with RMSNorm: the residual add before
+                   it and the cast of its output to a narrower dtype after
+                   it, composed from the pinned RMSNorm golden and reference
+                   with PyTorch's own add and cast.
 * ``gate``      -- the correctness gate of that page (section "正确性判据",
                    the correctness criterion) with its conditioning check,
                    plus the constants it uses, fixed before any kernel ran.
 
-Parity status: every public function of ``golden`` and ``layernorm`` is
-pinned (``tests/test_layernorm_oracle.py`` for the latter) by the
+Parity status: every public function of ``golden``, ``layernorm`` and
+``fused`` is pinned (``tests/test_layernorm_oracle.py``,
+``tests/test_fused_oracle.py`` and ``tests/test_cast_oracle.py`` for the
+latter two) by the
 ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py`` (printed worked
 examples, closed forms, invariants, central differences, and PyTorch's own
 ``rms_norm`` with autograd in float64).  ``reference`` is pinned against the

@@ -1,4 +1,4 @@
-"""Residual add fused with RMSNorm -- TEST INFRASTRUCTURE ONLY.
+"""Neighbours fused with RMSNorm -- TEST INFRASTRUCTURE ONLY.
 
 The neighbour fused before the norm (the page "PyTorch torch.compile ...
 LayerNorm and RMSNorm" argues, in its introduction, that a normalisation
@@ -20,6 +20,18 @@ stream (None means 0):
 h is formed with PyTorch's own CPU add so it is exactly the tensor an
 unfused model would normalise; everything after it reuses the pinned RMSNorm
 golden (float64) and reference (float32) functions.
+
+The neighbour fused after the norm is a cast of its output to a narrower
+dtype (float32 in, bfloat16 or float16 out: a float32 residual stream feeding
+a lower-precision consumer):
+
+    y  = T_out(RMSNorm(x))   the norm in float32 as in oracle.reference,
+                             then one round-to-nearest-even cast to T_out
+                             (torch's ``.to``); the golden stays float64
+    dx = dRMSNorm/dx (dy)    dy arrives in T_out; a dtype conversion passes
+                             its gradient through unchanged (PyTorch's
+                             convention), so dy is widened, exactly, and the
+                             RMSNorm backward runs on it; dgamma likewise
 """
 from __future__ import annotations
 
@@ -79,3 +91,37 @@ def reference_add_backward(dy, dh, h, weight, eps=reference.DEFAULT_EPS, offset=
     if dh is not None:
         dx = dx + reference._rows2d(dh.detach().to("cpu")).float()
     return dx.to(h.dtype), (dyf * hf * r).sum(0)
+
+
+# ---- the output cast fused after the norm -----------------------------------
+
+def golden_cast_forward(x, weight, eps=golden.DEFAULT_EPS, offset=False, rows=None):
+    """float64 ``(y, r)``: the RMSNorm golden; a cast has no golden of its
+    own (the gate compares the cast output with this exact value)."""
+    return golden.golden_forward(x, weight, eps, offset, rows=rows)
+
+
+def golden_cast_dx(dy, x, weight, eps=golden.DEFAULT_EPS, offset=False, rows=None):
+    """float64 gradient of x: dy (in the narrow dtype) widened exactly."""
+    return golden.golden_dx(dy, x, weight, eps, offset, rows=rows)
+
+
+def golden_cast_backward(dy, x, weight, eps=golden.DEFAULT_EPS, offset=False):
+    """Returns ``(dx, dgamma)`` in float64."""
+    return golden.golden_backward(dy, x, weight, eps, offset)
+
+
+def reference_cast_forward(x, weight, out_dtype, eps=reference.DEFAULT_EPS, offset=False):
+    """Returns ``(y, rstd)``: the float32 reference norm, y rounded once to
+    ``out_dtype``; rstd float32."""
+    x2 = reference._rows2d(x.detach().to("cpu"))
+    xf = x2.float()
+    g = reference._weight32(weight, offset)
+    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
+    return (xf * r * g).to(out_dtype), r.squeeze(-1)
+
+
+def reference_cast_backward(dy, x, weight, eps=reference.DEFAULT_EPS, offset=False):
+    """float32 backward with dy widened from its narrow dtype.  Returns
+    ``(dx, dgamma)``: dx in x's dtype, dgamma float32."""
+    return reference.reference_backward(dy.detach().to("cpu").float(), x, weight, eps, offset)
