@@ -31,6 +31,9 @@ __all__ = [
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
     "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce", "add_fwd",
     "add_bwd", "RMSNORM_ADD_MAX_N",
+    "rmsnorm_cast_fwd", "rmsnorm_cast_bwd", "rmsnorm_cast_bwd_workspace_bytes",
+    "rmsnorm_cast_query_plan", "rmsnorm_cast_bwd_rows", "rmsnorm_cast_bwd_reduce", "cast_fwd",
+    "cast_bwd", "RMSNORM_CAST_MAX_N",
 ]
 
 RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
@@ -41,9 +44,10 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
                 9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
                 13: "bwd_split", 14: "bwd_reduce_wide", 15: "ln_fwd",
-                16: "ln_bwd", 17: "add_fwd", 18: "add_bwd"}
+                16: "ln_bwd", 17: "add_fwd", 18: "add_bwd", 19: "cast_fwd", 20: "cast_bwd"}
 LAYERNORM_MAX_N = 16384
 RMSNORM_ADD_MAX_N = 16384
+RMSNORM_CAST_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
 
 EXPORTED_SYMBOLS = (
@@ -54,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "layernorm_bwd_rows", "layernorm_bwd_reduce",
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
     "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce",
+    "rmsnorm_cast_fwd", "rmsnorm_cast_bwd", "rmsnorm_cast_bwd_workspace_bytes",
+    "rmsnorm_cast_query_plan", "rmsnorm_cast_bwd_rows", "rmsnorm_cast_bwd_reduce",
 )
 
 _DTYPES = {torch.float32: RMSNORM_F32, torch.float16: RMSNORM_F16,
@@ -148,6 +154,21 @@ def load_library():
     lib.rmsnorm_add_bwd_rows.restype = i32
     lib.rmsnorm_add_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp]
     lib.rmsnorm_add_bwd_reduce.restype = i32
+    lib.rmsnorm_cast_fwd.argtypes = [vp, i64, vp, f32, i64, i64, i32, i32, u32, vp, i64, vp, vp]
+    lib.rmsnorm_cast_fwd.restype = i32
+    lib.rmsnorm_cast_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, u32, vp, i64,
+                                     vp, vp, sz, vp]
+    lib.rmsnorm_cast_bwd.restype = i32
+    lib.rmsnorm_cast_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, u32]
+    lib.rmsnorm_cast_bwd_workspace_bytes.restype = sz
+    lib.rmsnorm_cast_query_plan.argtypes = [i64, i64, i32, i32, u32, i32, i32,
+                                            ctypes.POINTER(Plan)]
+    lib.rmsnorm_cast_query_plan.restype = i32
+    lib.rmsnorm_cast_bwd_rows.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, u32, vp,
+                                          i64, vp, sz, vp]
+    lib.rmsnorm_cast_bwd_rows.restype = i32
+    lib.rmsnorm_cast_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, i32, u32, vp, vp]
+    lib.rmsnorm_cast_bwd_reduce.restype = i32
     _LIB = lib
     return lib
 
@@ -558,4 +579,95 @@ def add_bwd(dy, dh, h, gamma, rstd, offset=False, stream=None, poison=False, wor
         nbytes = rmsnorm_add_bwd_workspace_bytes(m, n, h.dtype, offset)
         workspace = torch.empty((max(nbytes, 4) // 4,), device=h.device, dtype=torch.float32)
     rmsnorm_add_bwd(dy, dh, h, gamma, rstd, dx, dgamma, workspace, offset, stream)
+    return dx, dgamma
+
+
+# ---- RMSNorm with its output cast to a narrower dtype (include/rmsnorm_cast.h) ----
+
+def rmsnorm_cast_query_plan(M, N, out_dtype, offset=False, which=PASS_FWD, align_bytes=16):
+    p = Plan()
+    _check("rmsnorm_cast_query_plan", load_library().rmsnorm_cast_query_plan(
+        int(M), int(N), RMSNORM_F32, _code(out_dtype), _flags(offset), int(which),
+        int(align_bytes), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def rmsnorm_cast_bwd_workspace_bytes(M, N, out_dtype, offset=False):
+    return int(load_library().rmsnorm_cast_bwd_workspace_bytes(
+        int(M), int(N), RMSNORM_F32, _code(out_dtype), _flags(offset)))
+
+
+def rmsnorm_cast_fwd(x, gamma, eps, y, rstd, offset=False, stream=None):
+    """y (its own dtype), rstd <- RMSNorm(x) cast to y's dtype; row strides
+    from the tensors."""
+    m, n, ldx = _layout(x, "x")
+    _, _, ldy = _layout(y, "y")
+    _check("rmsnorm_cast_fwd", load_library().rmsnorm_cast_fwd(
+        _ptr(x), ldx, _ptr(gamma), float(eps), m, n, _dtype_code(x), _dtype_code(y),
+        _flags(offset), _ptr(y), ldy, _ptr(rstd), _stream(x.device, stream)))
+
+
+def rmsnorm_cast_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=None):
+    """dx, dgamma <- backward from dy in the narrow dtype."""
+    m, n, ldx = _layout(x, "x")
+    _, _, lddy = _layout(dy, "dy")
+    _, _, lddx = _layout(dx, "dx")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_cast_bwd", load_library().rmsnorm_cast_bwd(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
+        _dtype_code(dy), _flags(offset), _ptr(dx), lddx, _ptr(dgamma), _ptr(workspace),
+        ws_bytes, _stream(x.device, stream)))
+
+
+def rmsnorm_cast_bwd_rows(dy, x, gamma, rstd, dx, workspace, offset=False, stream=None):
+    m, n, ldx = _layout(x, "x")
+    _, _, lddy = _layout(dy, "dy")
+    _, _, lddx = _layout(dx, "dx")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_cast_bwd_rows", load_library().rmsnorm_cast_bwd_rows(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
+        _dtype_code(dy), _flags(offset), _ptr(dx), lddx, _ptr(workspace), ws_bytes,
+        _stream(x.device, stream)))
+
+
+def rmsnorm_cast_bwd_reduce(workspace, M, N, out_dtype, dgamma, offset=False, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("rmsnorm_cast_bwd_reduce", load_library().rmsnorm_cast_bwd_reduce(
+        _ptr(workspace), ws_bytes, int(M), int(N), RMSNORM_F32, _code(out_dtype),
+        _flags(offset), _ptr(dgamma), _stream(dgamma.device, stream)))
+
+
+def cast_fwd(x, gamma, out_dtype=torch.bfloat16, eps=1e-6, offset=False, stream=None,
+             poison=False):
+    """Returns ``(y, rstd)``: y = RMSNorm(x) in ``out_dtype`` (x and gamma
+    float32), rstd float32 per row."""
+    _check_inputs(x, gamma)
+    _require(x.dtype == torch.float32, "x must be float32")
+    _require(out_dtype in (torch.bfloat16, torch.float16), "out_dtype must be bf16 or fp16")
+    m, _, _ = row_layout(x)
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    y = fill(x.shape, float("nan"), device=x.device, dtype=out_dtype)
+    rstd = fill((m,), float("nan"), device=x.device, dtype=torch.float32)
+    rmsnorm_cast_fwd(x, gamma, eps, y, rstd, offset, stream)
+    return y, rstd
+
+
+def cast_bwd(dy, x, gamma, rstd, offset=False, stream=None, poison=False, workspace=None):
+    """Returns ``(dx, dgamma)``, both float32, from dy in the narrow dtype."""
+    _check_inputs(x, gamma)
+    _require(dy.shape == x.shape and dy.device == x.device
+             and dy.dtype in (torch.bfloat16, torch.float16),
+             "dy must match x in shape and device and be bf16 or fp16")
+    if row_layout(dy) is None:
+        dy = dy.contiguous()
+    m, n, _ = row_layout(x)
+    _require(rstd.dtype == torch.float32 and rstd.numel() == m and rstd.is_contiguous(),
+             "rstd must be a contiguous float32 tensor with one value per row")
+    fill = torch.full if poison else (lambda shape, _v, **kw: torch.empty(shape, **kw))
+    dx = fill(x.shape, float("nan"), device=x.device, dtype=torch.float32)
+    dgamma = fill((n,), float("nan"), device=x.device, dtype=torch.float32)
+    if workspace is None:
+        nbytes = rmsnorm_cast_bwd_workspace_bytes(m, n, dy.dtype, offset)
+        workspace = torch.empty((max(nbytes, 4) // 4,), device=x.device, dtype=torch.float32)
+    rmsnorm_cast_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset, stream)
     return dx, dgamma

@@ -20,6 +20,7 @@
 #include "../../include/layernorm.h"
 #include "../../include/rmsnorm.h"
 #include "../../include/rmsnorm_add.h"
+#include "../../include/rmsnorm_cast.h"
 #include "rmsnorm_fast.hpp"
 #include "rmsnorm_fast_table.hpp"
 #include "rmsnorm_launch.hpp"
@@ -1215,6 +1216,134 @@ void fill_add_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm
   out->kernel = pass == RMSNORM_PASS_BWD_ROWS ? RMSNORM_KERNEL_ADD_BWD : RMSNORM_KERNEL_ADD_FWD;
 }
 
+// ---- RMSNorm with its output cast to a narrower dtype (fused_cast.hip) ------
+//
+// float32 x, gamma and dx; y and dy in the output dtype.  The row-resident
+// plan of LayerNorm at float32 (same targets, workgroups and P); the
+// backward's workspace is one [P, N] block.  Vector widths follow the common
+// alignment of all operands, so the narrow operands are aligned for their
+// half-width accesses too.
+constexpr int kCastIn = 4;  // bytes per input element
+
+int check_cast_common(int64_t M, int64_t N, int dtype, int out_dtype, uint32_t flags) {
+  if (dtype != RMSNORM_F32 || (out_dtype != RMSNORM_BF16 && out_dtype != RMSNORM_F16))
+    return RMSNORM_ERR_DTYPE;
+  if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
+  if (N < 1 || N > RMSNORM_CAST_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  return RMSNORM_OK;
+}
+
+size_t cast_workspace_bytes(int64_t M, int64_t N) {
+  return static_cast<size_t>(ln_partials(M, N, kCastIn) * N * 4);
+}
+
+int cast_fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M,
+                  int64_t N, rmsnorm_dtype_t dtype, rmsnorm_dtype_t out_dtype, uint32_t flags,
+                  void* y, int64_t ldy, float* rstd, hipStream_t stream) {
+  int st = check_cast_common(M, N, dtype, out_dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return RMSNORM_ERR_EPS;
+  if (bad_stride(ldx, N) || bad_stride(ldy, N)) return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!x || !gamma || !y || !rstd) return RMSNORM_ERR_NULL_POINTER;
+  const int eo = elem_bytes(out_dtype);
+  if (misaligned(x, kCastIn) || misaligned(gamma, kCastIn) || misaligned(y, eo) ||
+      misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(y, M, ldy * eo, N * eo), vec(rstd, M * 4)},
+                  {matrix(x, M, ldx * kCastIn, N * kCastIn), vec(gamma, N * kCastIn)}))
+    return RMSNORM_ERR_OVERLAP;
+  const LnPlan p = ln_plan(M, N, kCastIn, false,
+                           layout_alignment({x, gamma, y}, {ldx * kCastIn, ldy * eo}));
+  const CastFwdArgs a{x, gamma, y, rstd, M, static_cast<int>(N), eps,
+                      (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * kCastIn, ldy * eo};
+  return status_of(cast_fwd_launch(out_dtype, p, a, stream));
+}
+
+int check_cast_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                         const void* gamma, const float* rstd, int64_t M, int64_t N, int dtype,
+                         int out_dtype, uint32_t flags, const void* dx, int64_t lddx,
+                         const void* workspace, size_t workspace_bytes) {
+  int st = check_cast_common(M, N, dtype, out_dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (bad_stride(lddy, N) || bad_stride(ldx, N) || bad_stride(lddx, N))
+    return RMSNORM_ERR_STRIDE;
+  if (M == 0) return RMSNORM_OK;
+  if (!dy || !x || !gamma || !rstd || !dx) return RMSNORM_ERR_NULL_POINTER;
+  const int eo = elem_bytes(out_dtype);
+  if (misaligned(dy, eo) || misaligned(x, kCastIn) || misaligned(gamma, kCastIn) ||
+      misaligned(dx, kCastIn) || misaligned(rstd, 4))
+    return RMSNORM_ERR_ALIGNMENT;
+  const size_t need = cast_workspace_bytes(M, N);
+  if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({matrix(dx, M, lddx * kCastIn, N * kCastIn),
+                   vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * eo, N * eo), matrix(x, M, ldx * kCastIn, N * kCastIn),
+                   vec(gamma, N * kCastIn), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int cast_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                     const void* gamma, const float* rstd, int64_t M, int64_t N,
+                     rmsnorm_dtype_t out_dtype, uint32_t flags, void* dx, int64_t lddx,
+                     void* workspace, hipStream_t stream) {
+  if (M == 0) return RMSNORM_OK;
+  const int eo = elem_bytes(out_dtype);
+  const LnPlan p = ln_plan(M, N, kCastIn, true,
+                           layout_alignment({dy, x, gamma, dx},
+                                            {lddy * eo, ldx * kCastIn, lddx * kCastIn}));
+  const CastBwdArgs a{dy, x, gamma, rstd, dx, static_cast<float*>(workspace), M,
+                      static_cast<int>(N), (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * eo,
+                      ldx * kCastIn, lddx * kCastIn};
+  return status_of(cast_bwd_launch(out_dtype, p, a, stream));
+}
+
+int check_cast_reduce_args(const void* workspace, size_t workspace_bytes, int64_t M,
+                           int64_t N, int dtype, int out_dtype, uint32_t flags,
+                           const void* dgamma) {
+  int st = check_cast_common(M, N, dtype, out_dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  st = check_dgamma_args(dgamma, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  const size_t need = cast_workspace_bytes(M, N);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  if (any_overlap({vec(dgamma, N * 4)}, {vec(workspace, static_cast<int64_t>(need))}))
+    return RMSNORM_ERR_OVERLAP;
+  return RMSNORM_OK;
+}
+
+int cast_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* gamma,
+                  const float* rstd, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                  rmsnorm_dtype_t out_dtype, uint32_t flags, void* dx, int64_t lddx,
+                  void* dgamma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_cast_rows_args(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, out_dtype, flags, dx,
+                                lddx, workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  st = check_cast_reduce_args(workspace, workspace_bytes, M, N, dtype, out_dtype, flags, dgamma);
+  if (st != RMSNORM_OK) return st;
+  const int eo = elem_bytes(out_dtype);
+  const size_t need = cast_workspace_bytes(M, N);
+  if (any_overlap({vec(dgamma, N * 4), matrix(dx, M, lddx * kCastIn, N * kCastIn),
+                   vec(workspace, static_cast<int64_t>(need))},
+                  {matrix(dy, M, lddy * eo, N * eo), matrix(x, M, ldx * kCastIn, N * kCastIn),
+                   vec(gamma, N * kCastIn), vec(rstd, M * 4)}))
+    return RMSNORM_ERR_OVERLAP;
+  st = cast_rows_launch(dy, lddy, x, ldx, gamma, rstd, M, N, out_dtype, flags, dx, lddx,
+                        workspace, stream);
+  if (st != RMSNORM_OK) return st;
+  return reduce_columns(static_cast<const float*>(workspace), ln_partials(M, N, kCastIn), N,
+                        dtype, flags, dgamma, stream);
+}
+
+void fill_cast_plan(int64_t M, int64_t N, int pass, int align, rmsnorm_plan_t* out) {
+  fill_ln_plan(M, N, RMSNORM_F32, pass, align, out);
+  if (pass == RMSNORM_PASS_BWD_REDUCE) return;
+  out->kernel = pass == RMSNORM_PASS_BWD_ROWS ? RMSNORM_KERNEL_CAST_BWD : RMSNORM_KERNEL_CAST_FWD;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1415,6 +1544,62 @@ int rmsnorm_add_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t
   if (align_bytes < 1 || align_bytes > 4096 || (align_bytes & (align_bytes - 1)))
     return RMSNORM_ERR_ARGUMENT;
   fill_add_plan(M, N, dtype, pass, std::min(align_bytes, 16), plan);
+  return RMSNORM_OK;
+}
+
+int rmsnorm_cast_fwd(const void* x, int64_t ldx, const void* gamma, float eps, int64_t M,
+                     int64_t N, rmsnorm_dtype_t dtype, rmsnorm_dtype_t out_dtype,
+                     uint32_t flags, void* y, int64_t ldy, float* rstd, hipStream_t stream) {
+  return cast_fwd_impl(x, ldx, gamma, eps, M, N, dtype, out_dtype, flags, y, ldy, rstd, stream);
+}
+
+size_t rmsnorm_cast_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                                        rmsnorm_dtype_t out_dtype, uint32_t flags) {
+  if (check_cast_common(M, N, dtype, out_dtype, flags) != RMSNORM_OK || M == 0) return 0;
+  return cast_workspace_bytes(M, N);
+}
+
+int rmsnorm_cast_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                     const void* gamma, const float* rstd, int64_t M, int64_t N,
+                     rmsnorm_dtype_t dtype, rmsnorm_dtype_t out_dtype, uint32_t flags,
+                     void* dx, int64_t lddx, void* dgamma, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return cast_bwd_impl(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, out_dtype, flags, dx, lddx,
+                       dgamma, workspace, workspace_bytes, stream);
+}
+
+int rmsnorm_cast_bwd_rows(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                          const void* gamma, const float* rstd, int64_t M, int64_t N,
+                          rmsnorm_dtype_t dtype, rmsnorm_dtype_t out_dtype, uint32_t flags,
+                          void* dx, int64_t lddx, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const int st = check_cast_rows_args(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, out_dtype,
+                                      flags, dx, lddx, workspace, workspace_bytes);
+  if (st != RMSNORM_OK) return st;
+  return cast_rows_launch(dy, lddy, x, ldx, gamma, rstd, M, N, out_dtype, flags, dx, lddx,
+                          workspace, stream);
+}
+
+int rmsnorm_cast_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M,
+                            int64_t N, rmsnorm_dtype_t dtype, rmsnorm_dtype_t out_dtype,
+                            uint32_t flags, void* dgamma, hipStream_t stream) {
+  const int st = check_cast_reduce_args(workspace, workspace_bytes, M, N, dtype, out_dtype,
+                                        flags, dgamma);
+  if (st != RMSNORM_OK) return st;
+  return reduce_columns(static_cast<const float*>(workspace), ln_partials(M, N, kCastIn), N,
+                        dtype, flags, dgamma, stream);
+}
+
+int rmsnorm_cast_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
+                            rmsnorm_dtype_t out_dtype, uint32_t flags, int pass,
+                            int align_bytes, rmsnorm_plan_t* plan) {
+  const int st = check_cast_common(M, N, dtype, out_dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  if (!plan) return RMSNORM_ERR_NULL_POINTER;
+  if (pass < RMSNORM_PASS_FWD || pass > RMSNORM_PASS_BWD_REDUCE) return RMSNORM_ERR_ARGUMENT;
+  if (align_bytes < 1 || align_bytes > 4096 || (align_bytes & (align_bytes - 1)))
+    return RMSNORM_ERR_ARGUMENT;
+  fill_cast_plan(M, N, pass, std::min(align_bytes, 16), plan);
   return RMSNORM_OK;
 }
 

@@ -180,4 +180,40 @@ hipError_t add_fwd_launch(int dtype, const LnPlan& p, const AddFwdArgs& a, hipSt
 hipError_t add_bwd_launch(int dtype, const LnPlan& p, const AddBwdArgs& a, hipStream_t s);
 hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
 
+// RMSNorm with its output cast to a narrower dtype (fused_cast.hip): float32
+// x, gamma and dx; y and dy in the output dtype.  Row-resident plan of
+// LayerNorm at float32.
+struct CastFwdArgs {
+  const void* x;
+  const void* gamma;
+  void* y;
+  float* rstd;
+  int64_t M;
+  int N;
+  float eps;
+  int offset;
+  int64_t x_pitch;  // bytes between row starts
+  int64_t y_pitch;
+};
+
+struct CastBwdArgs {
+  const void* dy;
+  const void* x;
+  const void* gamma;
+  const float* rstd;
+  void* dx;
+  float* part;  // [P, N]
+  int64_t M;
+  int N;
+  int offset;
+  int64_t dy_pitch;
+  int64_t x_pitch;
+  int64_t dx_pitch;
+};
+
+hipError_t cast_fwd_launch(int out_dtype, const LnPlan& p, const CastFwdArgs& a,
+                           hipStream_t s);
+hipError_t cast_bwd_launch(int out_dtype, const LnPlan& p, const CastBwdArgs& a,
+                           hipStream_t s);
+
 }  // namespace rmsnorm_hip

@@ -30,6 +30,14 @@ per-row mean shifts).  Algorithmic bytes: forward 2*M*N*s + 2*N*s + 8*M
 4*M*N*s + N*s + 4*M (dy, dh and h read, dx written), stage 2 4*N.  The
 same step unfused (torch's add, rmsnorm_fwd, rmsnorm_bwd, torch's add of
 dh) is timed beside it as ``unfused_step_us``.
+
+``--op rmsnorm_cast`` measures RMSNorm with its output cast to a narrower
+dtype (rmsnorm_cast_fwd, rmsnorm_cast_bwd_rows, rmsnorm_cast_bwd_reduce) on
+the workload's draws with float32 x and gamma and y, dy in the workload's
+16-bit dtype: forward 6*M*N + 4*N + 4*M (x read, y written), backward
+stage 1 10*M*N + 4*N + 4*M (dy and x read, dx written in float32), stage 2
+4*N.  The unfused step (float32 rmsnorm_fwd, torch's cast of y, torch's
+widening of dy, float32 rmsnorm_bwd) is timed beside it.
 """
 import argparse
 import hashlib
@@ -79,6 +87,8 @@ def measured_traffic(workload):
 
 
 def alg_bytes(M, N, s, op="rmsnorm"):
+    if op == "rmsnorm_cast":  # float32 x, gamma, dx; 16-bit y and dy
+        return 6 * M * N + 4 * N + 4 * M, 10 * M * N + 4 * N + 4 * M, 4 * N
     if op == "add_rmsnorm":
         return 4 * M * N * s + N * s + 4 * M, 4 * M * N * s + N * s + 4 * M, 4 * N
     if op == "layernorm":
@@ -97,7 +107,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
-    ap.add_argument("--op", choices=("rmsnorm", "layernorm", "add_rmsnorm"), default="rmsnorm")
+    ap.add_argument("--op", choices=("rmsnorm", "layernorm", "add_rmsnorm", "rmsnorm_cast"),
+                    default="rmsnorm")
     ap.add_argument("--cold-samples", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1 << 62,
@@ -124,13 +135,17 @@ def main():
     t0 = time.time()
     ln = args.op == "layernorm"
     fused = args.op == "add_rmsnorm"
+    cast = args.op == "rmsnorm_cast"
+    cast_to = wl.dtype if wl.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
     make = {"layernorm": workloads.make_layernorm_inputs,
-            "add_rmsnorm": workloads.make_add_inputs}.get(args.op, workloads.make_inputs)
+            "add_rmsnorm": workloads.make_add_inputs,
+            "rmsnorm_cast": lambda name: workloads.make_cast_inputs(name, out_dtype=cast_to),
+            }.get(args.op, workloads.make_inputs)
     inp = make(args.workload)
     M, N, T, off, eps = inp["M"], inp["N"], inp["dtype"], inp["offset"], inp["eps"]
     s = torch.tensor([], dtype=T).element_size()
     x, w, dy = (inp[k].to(dev) for k in ("x", "w", "dy"))
-    y = torch.empty_like(x)
+    y = torch.empty_like(x, dtype=cast_to) if cast else torch.empty_like(x)
     rstd = torch.empty(M, device=dev, dtype=torch.float32)
     dx = torch.empty_like(x)
     dgamma = torch.empty(N, device=dev, dtype=torch.float32)
@@ -143,6 +158,8 @@ def main():
         res, dh = inp["res"].to(dev), inp["dh"].to(dev)
         h = torch.empty_like(x)
         nbytes = rn.rmsnorm_add_bwd_workspace_bytes(M, N, T, off)
+    elif cast:
+        nbytes = rn.rmsnorm_cast_bwd_workspace_bytes(M, N, cast_to, off)
     else:
         nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)
     ws = torch.empty(max(4, nbytes) // 4, device=dev, dtype=torch.float32)
@@ -158,6 +175,15 @@ def main():
 
         def bwd_reduce():
             rn.rmsnorm_add_bwd_reduce(ws, M, N, T, dgamma, off)
+    elif cast:
+        def fwd():
+            rn.rmsnorm_cast_fwd(x, w, eps, y, rstd, off)
+
+        def bwd_rows():
+            rn.rmsnorm_cast_bwd_rows(dy, x, w, rstd, dx, ws, off)
+
+        def bwd_reduce():
+            rn.rmsnorm_cast_bwd_reduce(ws, M, N, cast_to, dgamma, off)
     elif ln:
         def fwd():
             rn.layernorm_fwd(x, w, bias, eps, y, mean, rstd)
@@ -254,6 +280,30 @@ def main():
         torch.cuda.synchronize()
         unfused_us = (time.perf_counter() - t) * 1e6 / n_unf
         del h2, y2, dx2, ws2
+    elif cast:
+        y32, dx2 = torch.empty_like(x), torch.empty_like(x)
+        y2 = torch.empty_like(x, dtype=cast_to)
+        dy32 = torch.empty_like(x)
+        r2 = torch.empty(M, device=dev, dtype=torch.float32)
+        dg2 = torch.empty(N, device=dev, dtype=torch.float32)
+        ws2 = torch.empty(max(4, rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)) // 4, device=dev)
+
+        def unfused_step():
+            rn.rmsnorm_fwd(x, w, eps, y32, r2, off)
+            y2.copy_(y32)
+            dy32.copy_(dy)
+            rn.rmsnorm_bwd(dy32, x, w, r2, dx2, dg2, ws2, off)
+
+        for _ in range(max(10, args.warmup // 4)):
+            unfused_step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        n_unf = max(10, args.steps // 2)
+        for _ in range(n_unf):
+            unfused_step()
+        torch.cuda.synchronize()
+        unfused_us = (time.perf_counter() - t) * 1e6 / n_unf
+        del y32, y2, dy32, dx2, ws2
 
     # ---- cold-cache per-call samples ----
     # Before each sample a 1 GiB buffer is read (not written), so L2 and the
@@ -315,6 +365,10 @@ def main():
                 from oracle import fused as fused_oracle
                 hs, _, _ = fused_oracle.golden_add_forward(xs, inp["res"][:R], inp["w"], eps, off)
                 fused_oracle.golden_add_backward(dys, inp["dh"][:R], hs, inp["w"], eps, off)
+            elif cast:
+                from oracle import fused as fused_oracle
+                fused_oracle.golden_cast_forward(xs, inp["w"], eps, off)
+                fused_oracle.golden_cast_backward(dys, xs, inp["w"], eps, off)
             elif ln:
                 ln_oracle.golden_ln_forward(xs, inp["w"], inp["b"], eps)
                 ln_oracle.golden_ln_dx(dys, xs, inp["w"], eps)
@@ -335,7 +389,8 @@ def main():
                         "host_cores_available": len(os.sched_getaffinity(0))}
 
     result = {
-        "metric": ("LayerNorm" if ln else "residual add + RMSNorm" if fused else "RMSNorm")
+        "metric": ("LayerNorm" if ln else "residual add + RMSNorm" if fused
+                   else "RMSNorm + output cast" if cast else "RMSNorm")
         + " fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
         "value": round(value, 1),
         "unit": "GB/s",
@@ -349,7 +404,9 @@ def main():
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[T],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {wl.description}"
-                   + (" (LayerNorm inputs)" if ln else " (with res and dh)" if fused else ""),
+                   + (" (LayerNorm inputs)" if ln else " (with res and dh)" if fused
+                      else f" (float32 x and gamma, y and dy in {str(cast_to)[6:]})" if cast
+                      else ""),
                    "op": args.op, "M": M, "N": N,
                    "eps": eps, "offset_weight": off, "seed": inp["seed"],
                    "parallelism": "single GPU"},
@@ -364,12 +421,13 @@ def main():
         "cold_cache": cold,
         "device_copy_GBps": round(copy_gbs, 1),
         "unfused_step_us": None if unfused_us is None else round(unfused_us, 2),
-        "roofline": {"kernel": "ln_bwd_rows" if ln else "add_bwd_rows" if fused else "bwd_rows",
+        "roofline": {"kernel": ("ln_bwd_rows" if ln else "add_bwd_rows" if fused
+                                else "cast_bwd_rows" if cast else "bwd_rows"),
                      "bound": "hbm",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if (ln or fused) else measured_traffic(args.workload),
+                     "traffic": None if (ln or fused or cast) else measured_traffic(args.workload),
                      "alg_bytes_per_launch": rb},
         "cpu_baseline": cpu_baseline,
     }

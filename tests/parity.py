@@ -199,3 +199,56 @@ def gate_add_full(inp, out, with_dh=True):
         gate.gate_tensor("dx", out["dx"].cpu().reshape(-1, n), dx_r, dx_g, T),
         gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32, condition=cond),
     ]
+
+
+def run_cast_target(inp, device, poison=True):
+    x, w, dy = (inp[k].to(device) for k in ("x", "w", "dy"))
+    off, eps = inp["offset"], inp["eps"]
+    y, rstd = rn.cast_fwd(x, w, inp["out_dtype"], eps, off, poison=poison)
+    dx, dg = rn.cast_bwd(dy, x, w, rstd, off, poison=poison)
+    torch.cuda.synchronize()
+    return {"y": y, "rstd": rstd, "dx": dx, "dgamma": dg}
+
+
+def gate_cast_full(inp, out):
+    """y (in the narrow dtype: its rounding floor), rstd, dx and dgamma
+    (float32) through the gate against the cast oracle."""
+    x, w, dy, eps, off = inp["x"], inp["w"], inp["dy"], inp["eps"], inp["offset"]
+    To, n = inp["out_dtype"], x.shape[-1]
+    y_r, r_r = fusedref.reference_cast_forward(x, w, To, eps, off)
+    y_g, r_g = fusedref.golden_cast_forward(x, w, eps, off)
+    dx_r, dg_r = fusedref.reference_cast_backward(dy, x, w, eps, off)
+    dx_g, dg_g = fusedref.golden_cast_backward(dy, x, w, eps, off)
+    worst = int(np.argmax(np.abs(out["dgamma"].double().cpu().numpy() - dg_g))) if n else 0
+    cond = golden.dgamma_condition(dy, x, eps, worst) if x.numel() else None
+    return [
+        gate.gate_tensor("y", out["y"].cpu().reshape(-1, n), y_r, y_g, To),
+        gate.gate_rstd(out["rstd"].cpu(), r_g, r_r),
+        gate.gate_tensor("dx", out["dx"].cpu().reshape(-1, n), dx_r, dx_g, torch.float32),
+        gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32,
+                         condition=cond),
+    ]
+
+
+def gate_cast_sampled(inp, out, rows, cols):
+    """Sampled rows of y, rstd and dx and sampled columns of dgamma (sums
+    over all rows) against the cast oracle."""
+    x, w, dy, eps, off = inp["x"], inp["w"], inp["dy"], inp["eps"], inp["offset"]
+    To = inp["out_dtype"]
+    rt = torch.as_tensor(rows, dtype=torch.long)
+    xs, dys = x[rt], dy[rt]
+    y_r, r_r = fusedref.reference_cast_forward(xs, w, To, eps, off)
+    dx_r, _ = fusedref.reference_cast_backward(dys, xs, w, eps, off)
+    y_g, r_g = fusedref.golden_cast_forward(xs, w, eps, off)
+    dx_g = fusedref.golden_cast_dx(dys, xs, w, eps, off)
+    dg_g = golden.golden_dgamma(dy, x, eps, cols=cols)
+    dg_r = reference.reference_dgamma(dy.float(), x, eps, cols=cols)
+    dev_rows = rt.to(out["y"].device)
+    dev_cols = torch.as_tensor(cols, dtype=torch.long, device=out["y"].device)
+    return [
+        gate.gate_tensor("y[rows]", out["y"][dev_rows].cpu(), y_r, y_g, To),
+        gate.gate_rstd(out["rstd"][dev_rows].cpu(), r_g, r_r),
+        gate.gate_tensor("dx[rows]", out["dx"][dev_rows].cpu(), dx_r, dx_g, torch.float32),
+        gate.gate_tensor("dgamma[cols]", out["dgamma"][dev_cols].cpu(), dg_r, dg_g,
+                         torch.float32),
+    ]

@@ -18,7 +18,7 @@ import backward_rmsnorm_fwd_amd as rn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("rmsnorm.h", "layernorm.h",
-                                                      "rmsnorm_add.h")]
+                                                      "rmsnorm_add.h", "rmsnorm_cast.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(rn.library_path()),
                                 reason="librmsnorm.so not built")

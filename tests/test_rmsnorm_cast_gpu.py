@@ -1,0 +1,165 @@
+"""RMSNorm with its output cast to a narrower dtype, on the GPU through the C
+ABI (include/rmsnorm_cast.h), against the cast oracle (oracle.fused): y in
+bfloat16 or float16 (gated at that dtype's rounding floor), rstd, dx and
+dgamma (float32, from dy in the narrow dtype) through the gate, at reduced
+sizes of each recipe, edge shapes, misaligned and strided layouts, the
+offset weight, c2's shape at full size on sampled rows and columns, and
+against the unfused pair (float32 RMSNorm, then PyTorch's cast)."""
+import pytest
+import torch
+
+import backward_rmsnorm_fwd_amd as rn
+from backward_rmsnorm_fwd_amd import workloads
+from parity import (assert_pass, gate_cast_full, gate_cast_sampled, log, run_cast_target,
+                    sample_cols, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+OUT = [torch.bfloat16, torch.float16]
+
+
+@pytest.mark.parametrize("out_dtype", OUT)
+@pytest.mark.parametrize("name,M,N", [("c1a", None, None), ("c1b", None, None),
+                                      ("c1c", None, None), ("c2", 2051, 4096),
+                                      ("c2", 517, 4104), ("c3", 3001, 1000),
+                                      ("c5", 1031, 5120), ("c5", 301, 5112),
+                                      ("c4", 37, 16384), ("c4", 9, 16376)])
+def test_recipes(cuda, name, M, N, out_dtype):
+    inp = workloads.make_cast_inputs(name, M=M, N=N, out_dtype=out_dtype)
+    log(f"case cast {name} M={inp['M']} N={inp['N']} -> {out_dtype}")
+    assert_pass(gate_cast_full(inp, run_cast_target(inp, cuda)),
+                f"cast {name} @ {M}x{N} -> {out_dtype}")
+
+
+@pytest.mark.parametrize("out_dtype,N", [(torch.bfloat16, 1), (torch.float16, 2),
+                                         (torch.bfloat16, 3), (torch.float16, 255),
+                                         (torch.bfloat16, 257), (torch.float16, 4095),
+                                         (torch.bfloat16, 4097), (torch.float16, 8193),
+                                         (torch.bfloat16, 12288), (torch.float16, 16383),
+                                         (torch.bfloat16, 16384)])
+def test_edge_shapes(cuda, out_dtype, N):
+    inp = workloads.make_cast_inputs("c1a", M=7, N=N, out_dtype=out_dtype)
+    log(f"case cast edge N={N} -> {out_dtype}")
+    assert_pass(gate_cast_full(inp, run_cast_target(inp, cuda)), f"cast edge N={N}")
+
+
+@pytest.mark.parametrize("out_dtype", OUT)
+def test_tiny_and_zero_rows(cuda, out_dtype):
+    """Rows whose mean square is at or below eps (c3's x1e-3 scale) and an
+    all-zero row (y = 0, rstd = 1/sqrt(eps))."""
+    inp = workloads.make_cast_tile_case((9, 1000), out_dtype, 43, scale=1e-3)
+    inp["x"][4] = 0.0
+    out = run_cast_target(inp, cuda)
+    assert_pass(gate_cast_full(inp, out), f"cast tiny rows -> {out_dtype}")
+    assert torch.equal(out["y"][4].cpu(), torch.zeros(1000, dtype=out_dtype))
+
+
+def test_full_size_c2_shape_sampled(cuda):
+    inp = workloads.make_cast_inputs("c2", out_dtype=torch.bfloat16)
+    log("case cast c2 shape full size generated")
+    out = run_cast_target(inp, cuda)
+    log("case cast c2 shape device run done")
+    rows = sample_rows(inp, 64)
+    cols = sample_cols(inp["N"], 96)
+    assert_pass(gate_cast_sampled(inp, out, rows, cols), "cast c2 shape full size, sampled")
+
+
+def test_reproducible_offset(cuda):
+    inp = workloads.make_cast_inputs("c5", M=999, N=5120, out_dtype=torch.bfloat16)
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    y0, r0 = rn.cast_fwd(x, w, torch.bfloat16, 1e-6, True)
+    runs = [rn.cast_bwd(dy, x, w, r0, True) for _ in range(3)]
+    y1, r1 = rn.cast_fwd(x, w, torch.bfloat16, 1e-6, True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(r0, r1)
+    for dx, dg in runs[1:]:
+        assert torch.equal(dx, runs[0][0]) and torch.equal(dg, runs[0][1])
+    out = {"y": y0, "rstd": r0, "dx": runs[0][0], "dgamma": runs[0][1]}
+    assert_pass(gate_cast_full(inp, out), "cast offset weight")
+
+
+@pytest.mark.parametrize("out_dtype", OUT)
+def test_matches_the_unfused_pair(cuda, out_dtype):
+    """The float32 RMSNorm of this library followed by PyTorch's cast, and
+    its backward fed the widened dy: the same y up to one unit of the narrow
+    dtype where the two float32 row sums (different kernels) straddle a
+    rounding boundary, and dx, dgamma within float32 rounding."""
+    inp = workloads.make_cast_inputs("c2", M=1024, N=4096, out_dtype=out_dtype)
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    y, r = rn.cast_fwd(x, w, out_dtype)
+    dx, dg = rn.cast_bwd(dy, x, w, r)
+    y32, r32 = rn.fwd(x, w)
+    dx32, dg32 = rn.bwd(dy.float(), x, w, r32)
+    torch.cuda.synchronize()
+    yu = y32.to(out_dtype)
+    ulp = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}[out_dtype]
+    d = (y.double() - yu.double()).abs()
+    assert bool((d <= ulp * yu.double().abs() + 2.0 ** -24).all())
+    assert (y == yu).double().mean().item() > 0.999
+    assert torch.allclose(r, r32, rtol=1e-6, atol=0)
+    assert torch.allclose(dx, dx32, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(dg, dg32, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("out_dtype", OUT)
+def test_misaligned_and_strided(cuda, out_dtype):
+    M, N = 33, 4096
+    inp = workloads.make_cast_inputs("c2", M=M, N=N, out_dtype=out_dtype)
+
+    def shifted(t, dtype=None):
+        dtype = t.dtype if dtype is None else dtype
+        buf = torch.empty(t.numel() + 1, dtype=dtype, device=cuda)
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to(cuda))
+        return v
+
+    x, w, dy = (shifted(inp[k]) for k in ("x", "w", "dy"))
+    y = shifted(torch.full((M, N), float("nan"), dtype=out_dtype))
+    rstd = torch.empty(M, device=cuda)
+    rn.rmsnorm_cast_fwd(x, w, inp["eps"], y, rstd)
+    dx, dg = rn.cast_bwd(dy, x, w, rstd, poison=True)
+    torch.cuda.synchronize()
+    out = {"y": y, "rstd": rstd, "dx": dx, "dgamma": dg}
+    assert_pass(gate_cast_full(inp, out), f"cast misaligned -> {out_dtype}")
+
+    wide = torch.full((M, 2 * N), -5.0, device=cuda)
+    wide[:, :N] = inp["x"].to(cuda)
+    xs = wide[:, :N]
+    ywide = torch.full((M, 3 * N), float("nan"), dtype=out_dtype, device=cuda)
+    ys = ywide[:, N:2 * N]
+    r2 = torch.empty(M, device=cuda)
+    rn.rmsnorm_cast_fwd(xs, inp["w"].to(cuda), inp["eps"], ys, r2)
+    dywide = torch.zeros((M, 2 * N), dtype=out_dtype, device=cuda)
+    dywide[:, N:] = inp["dy"].to(cuda)
+    dxwide = torch.full((M, 2 * N), float("nan"), device=cuda)
+    dx2 = dxwide[:, :N]
+    dg2 = torch.full((N,), float("nan"), device=cuda)
+    ws = torch.empty(rn.rmsnorm_cast_bwd_workspace_bytes(M, N, out_dtype) // 4, device=cuda)
+    rn.rmsnorm_cast_bwd(dywide[:, N:], xs, inp["w"].to(cuda), r2, dx2, dg2, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(ywide[:, :N]).all() and torch.isnan(ywide[:, 2 * N:]).all()
+    assert torch.isnan(dxwide[:, N:]).all()
+    out2 = {"y": ys, "rstd": r2, "dx": dx2, "dgamma": dg2}
+    assert_pass(gate_cast_full(inp, out2), f"cast strided -> {out_dtype}")
+
+
+def test_m_zero_and_rejections(cuda):
+    x = torch.empty((0, 64), device=cuda)
+    w = torch.ones(64, device=cuda)
+    y, r = rn.cast_fwd(x, w, torch.bfloat16)
+    dx, dg = rn.cast_bwd(torch.empty((0, 64), device=cuda, dtype=torch.bfloat16), x, w, r,
+                         poison=True)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16 and torch.equal(dg.cpu(), torch.zeros(64))
+    xb = torch.ones((2, 64), device=cuda, dtype=torch.bfloat16)
+    yb = torch.empty((2, 64), device=cuda, dtype=torch.bfloat16)
+    r2 = torch.empty(2, device=cuda)
+    with pytest.raises(rn.RmsnormError):  # a bf16 input is not a narrowing cast
+        rn.rmsnorm_cast_fwd(xb, xb[0], 1e-6, yb, r2)
+    x32 = torch.ones((2, 64), device=cuda)
+    with pytest.raises(rn.RmsnormError):  # float32 out is not a cast
+        rn.rmsnorm_cast_fwd(x32, x32[0], 1e-6, torch.empty_like(x32), r2)
+    n = rn.RMSNORM_CAST_MAX_N + 1
+    t = torch.ones(2, n, device=cuda)
+    with pytest.raises(rn.RmsnormError):
+        rn.cast_fwd(t, torch.ones(n, device=cuda), torch.bfloat16)
