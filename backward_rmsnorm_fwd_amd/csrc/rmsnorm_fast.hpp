@@ -669,12 +669,24 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
   const uint32_t dma_off = wave_in_row * kWave * 16;
   const GRow gbuf(gamma);
 
+  // With dy in registers the weight (gamma, or 1 + w in offset mode) is
+  // widened once and held in float32 registers for the whole kernel, instead
+  // of a conversion and an add per element and row (fp16 262144 x 1024: 271.5
+  // -> 268.8 us).  With dy staged in LDS that measured slower (bf16
+  // 65536 x 5120: 333 -> 352 us), so there the packed weight is re-widened
+  // per row as before.
+  constexpr bool kHoldW = !DLDS;
   PK g[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     if (c < CH - 1 || voff + c * kChunk < row_bytes) g[c].raw = gbuf.template load<false>(voff, c * kChunk);
     else g[c].zero();
   }
+  float gw[CH][VEC];
+  auto weight = [&](int c, int k) __attribute__((always_inline)) {
+    if constexpr (kHoldW) return gw[c][k];
+    else return weight_of(g[c].get(k), offset);
+  };
   float acc[CH][VEC];
 #pragma unroll
   for (int c = 0; c < CH; ++c)
@@ -733,7 +745,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
           else dv[c] = dc[c];
 #pragma unroll
           for (int k = 0; k < VEC; ++k)
-            dot = fmaf(dv[c].get(k) * weight_of(g[c].get(k), offset), xv[c].get(k), dot);
+            dot = fmaf(dv[c].get(k) * weight(c, k), xv[c].get(k), dot);
         } else {
           xv[c].zero();
           dv[c].zero();
@@ -752,7 +764,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
     for (int c = 0; c < CH; ++c) {
       xv[c].opaque();
       dv[c].opaque();
-      g[c].opaque();
+      if constexpr (!kHoldW) g[c].opaque();
     }
     const float r3c = ((r * r) * r) * (dot / n_f);
     if (active) {
@@ -765,7 +777,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
           for (int k = 0; k < VEC; ++k) {
             const float xf = xv[c].get(k);
             const float dyf = dv[c].get(k);
-            const float u = dyf * weight_of(g[c].get(k), offset);
+            const float u = dyf * weight(c, k);
             o[k] = fmaf(-xf, r3c, r * u);
             acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
           }
@@ -789,7 +801,12 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     if constexpr (!DLDS) da[c].opaque();
-    g[c].opaque();
+    if constexpr (kHoldW) {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) gw[c][k] = weight_of(g[c].get(k), offset);
+    } else {
+      g[c].opaque();
+    }
   }
   int64_t it = 0;
   for (; it + 1 < iters; it += 2) {
