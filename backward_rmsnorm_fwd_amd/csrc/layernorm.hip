@@ -26,19 +26,22 @@
 // sum(u*xhat) = r*(sum(u*d) - c*sum(u)).  sum(u), sum(u*d) and sum(d) share
 // one exchange.
 //
-// Geometry: a row is spread over `wpr` wavefronts (64*wpr lanes, a power of
-// two up to 16); lane t of a row owns vectors c*64*wpr + t for c < chunks,
-// so each chunk is one coalesced sweep.  A workgroup of B threads (256, or
-// 64*wpr for longer rows; at most 1024) holds G = B/(64*wpr) rows at a time.  Elements past N are loaded as 0 and left out of
-// the variance and of every store.
+// Geometry: a row is spread over `wpr` wavefronts (64*wpr lanes: a power of
+// two up to 16, or for backward rows over four wavefronts the exact divisor
+// of the row the plan picks); lane t of a row owns vectors c*64*wpr + t for
+// c < chunks, so each chunk is one coalesced sweep.  A workgroup of B
+// threads (256, or 64*wpr for longer rows; at most 1024) holds
+// G = B/(64*wpr) rows at a time.  Elements past N are loaded as 0 and left
+// out of the variance and of every store.
 //
 // Backward stage 1: the rows are cut into steps of G*R consecutive rows (R
 // rows per row group) and workgroup w takes steps w, w+P, w+2P, ..., so the
 // P workgroups stream one contiguous window of the matrices at a time.  It
 // accumulates the column sums of dy*xhat and dy in float32 registers (each
 // row group adds its rows in row order), adds its G groups in group order
-// through LDS and writes part[w, :] (dgamma) and part[P + w, :] (dbeta).  Stage 2 adds each [P, N]
-// block by column in float64 (the RMSNorm reduce kernels).
+// through LDS and writes part[w, :] (dgamma) and part[P + w, :] (dbeta).
+// Stage 2 adds each [P, N] block by column in float64 (the RMSNorm reduce
+// kernels).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
