@@ -2,7 +2,7 @@
 
 Usage: ``python -m backward_rmsnorm_fwd_amd.build [--resource-usage]``.
 ``--resource-usage`` also prints each kernel's VGPR/SGPR/LDS/spill figures
-(compiler remark ``kernel-resource-usage``) for this build.
+(compiler remark ``kernel-resource-usage``) of the compiled kernels.
 """
 from __future__ import annotations
 

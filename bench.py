@@ -119,8 +119,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the row-sharded multi-GPU path is a design, not code).",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not "
+              "supported (the row-sharded multi-GPU path is designed, not implemented).",
               file=sys.stderr, flush=True)
         sys.exit(2)
     import backward_rmsnorm_fwd_amd as rn
