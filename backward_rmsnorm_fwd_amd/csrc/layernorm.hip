@@ -31,8 +31,8 @@
 // of the row the plan picks); lane t of a row owns vectors c*64*wpr + t for
 // c < chunks, so each chunk is one coalesced sweep.  A workgroup of B
 // threads (256, or 64*wpr for longer rows; at most 1024) holds
-// G = B/(64*wpr) rows at a time.  Elements past N are loaded as 0 and left
-// out of the variance and of every store.
+// G = B/(64*wpr) rows at a time.  Lanes past N take no part in the row
+// sums or the stores.
 //
 // Backward stage 1: the rows are cut into steps of G*R consecutive rows (R
 // rows per row group) and workgroup w takes steps w, w+P, w+2P, ..., so the
@@ -81,6 +81,10 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
       if (beta) ld<DT, VEC, false>(b[c], static_cast<const char*>(beta), e);
     }
   }
+  // ok[c]: this lane's vector of chunk c lies inside the row.
+  bool ok[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) ok[c] = c < chunks && (c * rg.tpr + rg.t) * VEC < N;
   const int64_t step = static_cast<int64_t>(rg.G) * R;
   for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * step; row0 < M;
        row0 += static_cast<int64_t>(gridDim.x) * step) {
@@ -89,29 +93,45 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
       g[c].opaque();
       b[c].opaque();
     }
+    // The loads carry no lane condition (a row past the matrix reads its
+    // last row, a lane past the row reads the row's first vector); the
+    // values are masked where they are used.
     int64_t row[R];
-    bool active[R];
     PK xv[R][MAXC];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       row[j] = row0 + j * rg.G + rg.group;
-      active[j] = row[j] < M;
-      const char* xr = row_base<DT>(x, row[j], ldx);
+      const char* xr = row_base<DT>(x, row[j] < M ? row[j] : M - 1, ldx);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
         const int e = (c * rg.tpr + rg.t) * VEC;
-        xv[j][c].zero();
-        if (active[j] && c < chunks && e < N) ld<DT, VEC, true>(xv[j][c], xr, e);
+        if (c < chunks) ld<DT, VEC, true>(xv[j][c], xr, e < N ? e : 0);  // c is uniform
+        else xv[j][c].zero();
       }
     }
+    // Float64 row sums, pairwise within each vector and across chunks (a
+    // short dependency chain; the order does not matter to the exact sum
+    // of widened 16-bit elements, and float32 elements round at 2^-53).
     double s[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      s[j] = 0.0;
+      double cs[MAXC];
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c)
+      for (int c = 0; c < MAXC; ++c) {
+        double v[VEC];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) s[j] += static_cast<double>(xv[j][c].get(k));
+        for (int k = 0; k < VEC; ++k) v[k] = static_cast<double>(xv[j][c].get(k));
+#pragma unroll
+        for (int h = VEC / 2; h > 0; h /= 2)
+#pragma unroll
+          for (int k = 0; k < h; ++k) v[k] += v[k + h];
+        cs[c] = ok[c] ? v[0] : 0.0;
+      }
+#pragma unroll
+      for (int h = MAXC / 2; h > 0; h /= 2)
+#pragma unroll
+        for (int c = 0; c < h; ++c) cs[c] += cs[c + h];
+      s[j] = cs[0];
     }
     row_sums<R, 0, R, R>(s, nullptr, slots64, slots, parity, wpr, rg);
     float mu[R], cm[R], q[R];
@@ -123,38 +143,38 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
       q[j] = 0.f;
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
-        const int e = (c * rg.tpr + rg.t) * VEC;
-        if (c < chunks && e < N) {
+        float qc = 0.f;
 #pragma unroll
-          for (int k = 0; k < VEC; ++k) {
-            const float d = xv[j][c].get(k) - mu[j];
-            q[j] = fmaf(d, d, q[j]);
-          }
+        for (int k = 0; k < VEC; ++k) {
+          const float d = xv[j][c].get(k) - mu[j];
+          qc = fmaf(d, d, qc);
         }
+        q[j] += ok[c] ? qc : 0.f;
       }
     }
     row_sums<0, R, R, R>(nullptr, q, slots64, slots, parity, wpr, rg);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const float r = 1.0f / sqrtf((q[j] / n_f - cm[j] * cm[j]) + eps);
-      if (!active[j]) continue;
+      if (row[j] >= M) continue;
       if (rg.t == 0) {
         mean[row[j]] = mu[j];
         rstd[row[j]] = r;
       }
+      // xhat = (x - mu - c)*r as one fma from the deviation.
+      const float ncr = -(cm[j] * r);
       const char* yr = row_base<DT>(y, row[j], ldy);
 #pragma unroll
       for (int c = 0; c < MAXC; ++c) {
+        if (!ok[c]) continue;
         const int e = (c * rg.tpr + rg.t) * VEC;
-        if (c < chunks && e < N) {
-          float o[VEC];
+        float o[VEC];
 #pragma unroll
-          for (int k = 0; k < VEC; ++k)
-            o[k] = fmaf(((xv[j][c].get(k) - mu[j]) - cm[j]) * r, g[c].get(k), b[c].get(k));
-          PK out;
-          out.set(o);
-          st<DT, VEC>(out, yr, e);
-        }
+        for (int k = 0; k < VEC; ++k)
+          o[k] = fmaf(fmaf(xv[j][c].get(k) - mu[j], r, ncr), g[c].get(k), b[c].get(k));
+        PK out;
+        out.set(o);
+        st<DT, VEC>(out, yr, e);
       }
     }
   }
