@@ -1033,6 +1033,9 @@ static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce
   const int col = blockIdx.x * (kQuads * 4) + q * 4;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   if (col < N) {
+    // Unrolled so that a thread's loads are in flight together; the adds
+    // keep partial-row order.
+#pragma unroll 8
     for (int64_t p = s; p < P; p += kSlices) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(part + p * N + col);
       a0 += v[0];
