@@ -381,12 +381,38 @@ def main():
         torch.set_num_threads(nthreads)
         cpu_s = statistics.median(times)
         sb = sum(alg_bytes(R, N, s, args.op))
+        # The same-dtype eager reference (float32 intermediates, PyTorch CPU)
+        # on the same rows, with torch's own thread pool.
+        from oracle import fused as fused_oracle
+        from oracle import reference as ref_oracle
+        rtimes = []
+        for _ in range(3):
+            t = time.perf_counter()
+            if fused:
+                hs, _, _ = fused_oracle.reference_add_forward(xs, inp["res"][:R], inp["w"], eps, off)
+                fused_oracle.reference_add_backward(dys, inp["dh"][:R], hs, inp["w"], eps, off)
+            elif cast:
+                fused_oracle.reference_cast_forward(xs, inp["w"], cast_to, eps, off)
+                fused_oracle.reference_cast_backward(dys, xs, inp["w"], eps, off)
+            elif ln:
+                ln_oracle.reference_ln_forward(xs, inp["w"], inp["b"], eps)
+                ln_oracle.reference_ln_backward(dys, xs, inp["w"], eps)
+            else:
+                ref_oracle.reference_forward(xs, inp["w"], eps, off)
+                ref_oracle.reference_backward(dys, xs, inp["w"], eps, off)
+            rtimes.append(time.perf_counter() - t)
+        ref_s = statistics.median(rtimes)
         cpu_baseline = {"value": round(sb / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1,
                         "kind": "oracle",
                         "sample": f"float64 NumPy golden forward+backward over {R} of {M} rows "
                                   f"(all of them by default), median of 3 runs of {cpu_s:.1f} s, "
                                   "one thread",
-                        "host_cores_available": len(os.sched_getaffinity(0))}
+                        "host_cores_available": len(os.sched_getaffinity(0)),
+                        "torch_fp32_reference": {
+                            "value": round(sb / ref_s / 1e9, 4), "unit": "GB/s",
+                            "threads": nthreads,
+                            "sample": f"same rows, float32 torch CPU reference forward+backward, "
+                                      f"median of 3 runs of {ref_s:.2f} s"}}
 
     result = {
         "metric": ("LayerNorm" if ln else "residual add + RMSNorm" if fused
