@@ -1077,7 +1077,7 @@ static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduc
   const int64_t col = static_cast<int64_t>(blockIdx.x) * kCols + lane * 4;
   double a[4] = {0.0, 0.0, 0.0, 0.0};
   if (col < N) {
-#pragma unroll 4
+#pragma unroll 8
     for (int64_t p = s; p < P; p += S) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(part + p * N + col);
 #pragma unroll
