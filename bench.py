@@ -15,7 +15,8 @@ kernel, backward stage 1, timed with events on its launch stream inside the
 timed steps.  A cold-cache figure (each call preceded by a 1 GiB read that
 evicts L2 and the 256 MB Infinity Cache) is reported beside it, a 1 GiB
 device copy as an achievable-bandwidth reference, and the CPU oracle's
-throughput on the same workload as ``cpu_baseline``.
+throughput on the same workload as ``cpu_baseline`` (the float64 golden on
+one thread, with the float32 torch CPU reference timed beside it).
 
 ``--op layernorm`` measures the LayerNorm path of the same library instead
 (layernorm_fwd, layernorm_bwd_rows, layernorm_bwd_reduce) on the LayerNorm
