@@ -1354,10 +1354,12 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_NULL_POINTER: return "a required pointer is NULL";
     case RMSNORM_ERR_DTYPE: return "unsupported dtype (fp32, fp16 and bf16 are supported)";
     case RMSNORM_ERR_SHAPE:
-      return "unsupported shape (need 1 <= N <= 2^24, 0 <= M <= 2^40 and M*N <= 2^46)";
+      return "unsupported shape (need 0 <= M <= 2^40 and, for rmsnorm_*, 1 <= N <= 2^24 with "
+             "M*N <= 2^46; for layernorm_*, rmsnorm_add_* and rmsnorm_cast_*, 1 <= N <= 16384)";
     case RMSNORM_ERR_EPS: return "eps must be finite and positive";
     case RMSNORM_ERR_FLAGS: return "unknown flag bits";
-    case RMSNORM_ERR_WORKSPACE: return "workspace missing or smaller than rmsnorm_bwd_workspace_bytes()";
+    case RMSNORM_ERR_WORKSPACE:
+      return "workspace missing or smaller than the matching *_bwd_workspace_bytes()";
     case RMSNORM_ERR_ALIGNMENT: return "pointer not aligned to its element size (workspace: 16 bytes)";
     case RMSNORM_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
     case RMSNORM_ERR_LAUNCH: return "kernel launch failed";

@@ -127,6 +127,17 @@ def main():
     import backward_rmsnorm_fwd_amd as rn
     from backward_rmsnorm_fwd_amd import workloads
 
+    if args.workload not in workloads.WORKLOADS:
+        print(f"bench.py: unknown workload {args.workload!r} "
+              f"(known: {', '.join(sorted(workloads.WORKLOADS))})", file=sys.stderr, flush=True)
+        sys.exit(2)
+    row_cap = {"layernorm": rn.LAYERNORM_MAX_N, "add_rmsnorm": rn.RMSNORM_ADD_MAX_N,
+               "rmsnorm_cast": rn.RMSNORM_CAST_MAX_N}.get(args.op)
+    if row_cap is not None and workloads.WORKLOADS[args.workload].N > row_cap:
+        print(f"bench.py: --op {args.op} holds rows in registers (N <= {row_cap}); workload "
+              f"{args.workload} has N = {workloads.WORKLOADS[args.workload].N}",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)

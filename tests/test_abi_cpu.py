@@ -181,6 +181,11 @@ def test_bwd_strided_rejects():
     assert call(dg=None) == ENULL
 
 
+def test_shape_status_string_names_each_family_limit():
+    s = rn.rmsnorm_status_string(-3)
+    assert "2^24" in s and "16384" in s and "layernorm_" in s
+
+
 def test_stride_status_string():
     assert "stride" in rn.rmsnorm_status_string(ESTRIDE)
 

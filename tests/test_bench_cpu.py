@@ -89,3 +89,16 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+@pytest.mark.parametrize("argv,needle", [
+    (["--op", "layernorm", "--workload", "c4"], "N <= 16384"),
+    (["--op", "rmsnorm_cast", "--workload", "c4"], "N <= 16384"),
+    (["--workload", "c9"], "unknown workload"),
+])
+def test_unsupported_workloads_are_refused_before_any_gpu_work(argv, needle):
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 2
+    assert needle in res.stderr
+    assert res.stdout == ""
