@@ -1,8 +1,8 @@
 """bench.py's host-side logic, without a GPU: the algorithmic byte counts
 behind ``value`` and ``roofline.achieved``, the reader of the committed
 counter summary behind ``roofline.traffic`` (used only while the kernel
-sources match the ones the counters were taken on), and the refusal of
-more than one GPU."""
+sources match the ones the counters were taken on), and the refusals of
+more than one GPU and of workloads an op cannot take."""
 import os
 import subprocess
 import sys
