@@ -45,7 +45,11 @@ TILE_CASES = [((3, 255), torch.float32, 1), ((3, 256), torch.bfloat16, 2),
               ((13, 1100), torch.float32, 13), ((11, 3000), torch.float16, 14),
               ((7, 8200), torch.bfloat16, 15), ((6, 20000), torch.float32, 16),
               ((5, 40000), torch.float16, 17), ((9, 2560), torch.float32, 18),
-              ((9, 5120), torch.float16, 19)]
+              ((9, 5120), torch.float16, 19),
+              # Long rows that are whole 8 KiB sweeps (3, 4 and 8 chunks),
+              # more rows than workgroups: some take two rows, some one.
+              ((300, 12288), torch.bfloat16, 20), ((270, 8192), torch.float32, 21),
+              ((513, 32768), torch.float16, 22)]
 
 
 @pytest.mark.parametrize("shape,dtype,seed", TILE_CASES)
