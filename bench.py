@@ -364,8 +364,10 @@ def main():
     # ---- CPU oracle on the same workload ----
     cpu_baseline = None
     if not args.no_cpu_baseline:
+        from oracle import fused as fused_oracle
         from oracle import golden
         from oracle import layernorm as ln_oracle
+        from oracle import reference as ref_oracle
         R = min(args.cpu_rows, M)
         xs, dys = inp["x"][:R], inp["dy"][:R]
         nthreads = torch.get_num_threads()
@@ -374,11 +376,9 @@ def main():
         for _ in range(3):
             t = time.perf_counter()
             if fused:
-                from oracle import fused as fused_oracle
                 hs, _, _ = fused_oracle.golden_add_forward(xs, inp["res"][:R], inp["w"], eps, off)
                 fused_oracle.golden_add_backward(dys, inp["dh"][:R], hs, inp["w"], eps, off)
             elif cast:
-                from oracle import fused as fused_oracle
                 fused_oracle.golden_cast_forward(xs, inp["w"], eps, off)
                 fused_oracle.golden_cast_backward(dys, xs, inp["w"], eps, off)
             elif ln:
@@ -395,8 +395,6 @@ def main():
         sb = sum(alg_bytes(R, N, s, args.op))
         # The same-dtype eager reference (float32 intermediates, PyTorch CPU)
         # on the same rows, with torch's own thread pool.
-        from oracle import fused as fused_oracle
-        from oracle import reference as ref_oracle
         rtimes = []
         for _ in range(3):
             t = time.perf_counter()
