@@ -201,6 +201,40 @@ def gate_add_full(inp, out, with_dh=True):
     ]
 
 
+def gate_add_sampled(inp, out, rows, cols):
+    """Sampled rows of h (bit-exact), y, rstd and dx, and sampled columns of
+    dgamma (sums over all rows), against the fused-add oracle."""
+    x, res, w, dy, dh = inp["x"], inp["res"], inp["w"], inp["dy"], inp["dh"]
+    eps, off, T = inp["eps"], inp["offset"], inp["x"].dtype
+    rt = torch.as_tensor(rows, dtype=torch.long)
+    xs, rs, dys, dhs = x[rt], res[rt], dy[rt], dh[rt]
+    dev_rows = rt.to(out["y"].device)
+    dev_cols = torch.as_tensor(cols, dtype=torch.long, device=out["y"].device)
+    h_o = fusedref.residual_sum(xs, rs)
+    h_t = out["h"][dev_rows].cpu()
+    h_row = gate.GateRow(tensor="h[rows]", dtype=str(T).replace("torch.", ""),
+                         shape=tuple(h_o.shape))
+    h_row.gate_valid = True
+    h_row.target_error = float((h_t.double() - h_o.double()).abs().max())
+    h_row.verdict = "PASS" if torch.equal(h_t, h_o) else "FAIL"
+    h_row.note = "bitwise equal to the dtype's add"
+    _, y_r, r_r = fusedref.reference_add_forward(xs, rs, w, eps, off)
+    _, y_g, r_g = fusedref.golden_add_forward(xs, rs, w, eps, off)
+    dx_r, _ = fusedref.reference_add_backward(dys, dhs, h_o, w, eps, off)
+    dx_g = fusedref.golden_add_dx(dys, dhs, h_o, w, eps, off)
+    h_all = fusedref.residual_sum(x, res)
+    dg_g = golden.golden_dgamma(dy, h_all, eps, cols=cols)
+    dg_r = reference.reference_dgamma(dy, h_all, eps, cols=cols)
+    return [
+        h_row,
+        gate.gate_tensor("y[rows]", out["y"][dev_rows].cpu(), y_r, y_g, T),
+        gate.gate_rstd(out["rstd"][dev_rows].cpu(), r_g, r_r),
+        gate.gate_tensor("dx[rows]", out["dx"][dev_rows].cpu(), dx_r, dx_g, T),
+        gate.gate_tensor("dgamma[cols]", out["dgamma"][dev_cols].cpu(), dg_r, dg_g,
+                         torch.float32),
+    ]
+
+
 def run_cast_target(inp, device, poison=True):
     x, w, dy = (inp[k].to(device) for k in ("x", "w", "dy"))
     off, eps = inp["offset"], inp["eps"]

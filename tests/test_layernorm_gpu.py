@@ -1,7 +1,7 @@
 """LayerNorm on the GPU through the C ABI (include/layernorm.h), gated
 against the LayerNorm oracle (oracle.layernorm): every element of y, mean,
 rstd, dx, dgamma and dbeta at reduced sizes of each recipe, tile-boundary
-and degenerate rows, misaligned and strided layouts, and the c2 and c3
+and degenerate rows, misaligned and strided layouts, and the c2, c3 and c5
 shapes at full size on sampled rows and columns."""
 import numpy as np
 import pytest
@@ -106,7 +106,8 @@ def test_no_bias(cuda):
     assert_pass(gate_ln_full(inp, out, bias=False), "ln without bias")
 
 
-@pytest.mark.parametrize("name,M,N", [("c2", None, None), ("c3", None, None)])
+@pytest.mark.parametrize("name,M,N", [("c2", None, None), ("c3", None, None),
+                                      ("c5", None, None)])
 def test_full_size_sampled(cuda, name, M, N):
     inp = workloads.make_layernorm_inputs(name, M=M, N=N)
     log(f"case ln {name} full size M={inp['M']} N={inp['N']} generated")

@@ -2,13 +2,15 @@
 ABI (include/rmsnorm_add.h), against the fused oracle (oracle.fused): h
 bitwise equal to the dtype's add, y, rstd, dx (RMSNorm's gradient plus dh)
 and dgamma through the gate, at reduced sizes of each recipe, tile and edge
-shapes, misaligned and strided layouts, without dh, and c2 at full size."""
+shapes, misaligned and strided layouts, without dh, c2 at full size on
+every element and c3, c5 at full size on sampled rows and columns."""
 import pytest
 import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from backward_rmsnorm_fwd_amd import workloads
-from parity import assert_pass, gate_add_full, log, run_add_target
+from parity import (assert_pass, gate_add_full, gate_add_sampled, log, run_add_target,
+                    sample_cols, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +49,21 @@ def test_full_size_c2(cuda):
     out = run_add_target(inp, cuda)
     log("case add c2 device run done")
     assert_pass(gate_add_full(inp, out), "add c2 full size, every element")
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_full_size_sampled(cuda, name):
+    """The fp16 262144 x 1024 and offset bf16 65536 x 5120 shapes at full
+    size, default plan; sampled rows and dgamma columns against the oracle."""
+    inp = workloads.make_add_inputs(name)
+    log(f"case add {name} full size M={inp['M']} N={inp['N']} generated")
+    out = run_add_target(inp, cuda)
+    log(f"case add {name} device run done")
+    rows = sample_rows(inp, 1024)
+    cols = sample_cols(inp["N"], 64)
+    assert_pass(gate_add_sampled(inp, out, rows, cols), f"add {name} full size, sampled")
+    for k in ("y", "h", "dx", "rstd", "dgamma"):
+        assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
 
 
 def test_reproducible_offset_and_dgamma_in_dtype(cuda):

@@ -3,8 +3,9 @@ ABI (include/rmsnorm_cast.h), against the cast oracle (oracle.fused): y in
 bfloat16 or float16 (gated at that dtype's rounding floor), rstd, dx and
 dgamma (float32, from dy in the narrow dtype) through the gate, at reduced
 sizes of each recipe, edge shapes, misaligned and strided layouts, the
-offset weight, c2's shape at full size on sampled rows and columns, and
-against the unfused pair (float32 RMSNorm, then PyTorch's cast)."""
+offset weight, the c2, c3 and c5 shapes at full size on sampled rows and
+columns, and against the unfused pair (float32 RMSNorm, then PyTorch's
+cast)."""
 import pytest
 import torch
 
@@ -54,14 +55,18 @@ def test_tiny_and_zero_rows(cuda, out_dtype):
     assert torch.equal(out["y"][4].cpu(), torch.zeros(1000, dtype=out_dtype))
 
 
-def test_full_size_c2_shape_sampled(cuda):
-    inp = workloads.make_cast_inputs("c2", out_dtype=torch.bfloat16)
-    log("case cast c2 shape full size generated")
+@pytest.mark.parametrize("name,out_dtype", [("c2", torch.bfloat16), ("c3", torch.float16),
+                                            ("c5", torch.bfloat16)])
+def test_full_size_shape_sampled(cuda, name, out_dtype):
+    """Each benchmarked shape at full size (float32 x, y and dy in the
+    shape's 16-bit dtype), default plan, sampled rows and dgamma columns."""
+    inp = workloads.make_cast_inputs(name, out_dtype=out_dtype)
+    log(f"case cast {name} shape full size generated")
     out = run_cast_target(inp, cuda)
-    log("case cast c2 shape device run done")
+    log(f"case cast {name} shape device run done")
     rows = sample_rows(inp, 64)
     cols = sample_cols(inp["N"], 96)
-    assert_pass(gate_cast_sampled(inp, out, rows, cols), "cast c2 shape full size, sampled")
+    assert_pass(gate_cast_sampled(inp, out, rows, cols), f"cast {name} shape full size, sampled")
 
 
 def test_reproducible_offset(cuda):
