@@ -51,6 +51,19 @@ struct GRow {
     if constexpr (NT) __builtin_nontemporal_store(v, a);
     else *a = v;
   }
+  // The same load issued by an asm statement, so the compiler does not
+  // track it: the caller waits for it with an explicit count and then ties
+  // the register (an asm with it as operand) before any use.  A tracked
+  // load read after stores were issued makes the compiler wait for every
+  // access in flight (it cannot count loads past pending stores).
+  template <bool NT>
+  __device__ __forceinline__ u32x4 load_untracked(uint32_t voff, uint32_t soff) const {
+    const char* a = p + soff + voff;
+    u32x4 v;
+    if constexpr (NT) asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v) : "v"(a) : "memory");
+    else asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(a) : "memory");
+    return v;
+  }
   __device__ __forceinline__ void to_lds(void* lds_wave_base, uint32_t voff, uint32_t soff) const {
     __builtin_amdgcn_global_load_lds(p + soff + voff, (lds_void_t*)lds_wave_base, 16, 0, 0);
   }
@@ -702,7 +715,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
       if (c < CH - 1 || voff + c * kChunk < row_bytes) {
         xb.to_lds(xs + c * kChunk + dma_off, voff, c * kChunk);
         if constexpr (DLDS) db.to_lds(xs + dy_off + c * kChunk + dma_off, voff, c * kChunk);
-        else dv[c].raw = db.template load<NT>(voff, c * kChunk);
+        else dv[c].raw = db.template load_untracked<NT>(voff, c * kChunk);
       } else if constexpr (!DLDS) {
         dv[c].zero();
       }
@@ -715,7 +728,9 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
   const bool has_last = uniform(static_cast<uint32_t>(wave_in_row * kWave * 16) +
                                 (CH - 1) * kChunk) < row_bytes;
 
-  auto step = [&](int64_t it, PK(&dc)[CH], PK(&dn)[CH]) __attribute__((always_inline)) {
+  // `last`: the final step, which has no next row to prefetch (stated so
+  // that no load is emitted there at all).
+  auto step = [&](int64_t it, PK(&dc)[CH], PK(&dn)[CH], bool last) __attribute__((always_inline)) {
     const int64_t row = rs.base + it * rs.stride + group;
     const bool active = row < rs.limit;
     const char* xs = xstage + (it & 1) * stage_stride;
@@ -727,10 +742,15 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
       if (has_last) wait_vmem<CH>();
       else wait_vmem<CH - 1>();
     }
+    // The dy registers were loaded untracked: their uses follow the wait.
+    if constexpr (!DLDS) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) dc[c].opaque();
+    }
     // Prefetch row it+1 into the other stage buffer (and register set); it
     // has the whole of this step to arrive.
     order_fence();
-    if (it + 1 < iters && row + rs.stride < rs.limit) issue(row + rs.stride, it + 1, dn);
+    if (!last && it + 1 < iters && row + rs.stride < rs.limit) issue(row + rs.stride, it + 1, dn);
     order_fence();
     float r = 0.f;
     PK xv[CH], dv[CH];
@@ -810,10 +830,10 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
   }
   int64_t it = 0;
   for (; it + 1 < iters; it += 2) {
-    step(it, da, db2);
-    step(it + 1, db2, da);
+    step(it, da, db2, false);
+    step(it + 1, db2, da, false);
   }
-  if (it < iters) step(it, da, db2);
+  if (it < iters) step(it, da, db2, true);
 
   float* dst = part + w * static_cast<int64_t>(N);
   if constexpr (G == 1) {
