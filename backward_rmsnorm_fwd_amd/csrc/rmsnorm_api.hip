@@ -664,41 +664,62 @@ Region matrix(const void* p, int64_t rows, int64_t pitch, int64_t width) {
 
 Region vec(const void* p, int64_t bytes) { return matrix(p, bytes > 0 ? 1 : 0, bytes, bytes); }
 
+// Spans are measured in 128-bit integers: with up to 2^40 rows of a pitch up
+// to 2^40 elements, (rows - 1) * pitch alone can pass 2^63.
+using wide_t = __int128;
+
+// One past the last byte of a region (its base when it is empty).
+wide_t region_end(const Region& r) {
+  if (r.rows == 0 || r.width == 0) return r.base;
+  return wide_t(r.base) + wide_t(r.rows - 1) * r.pitch + r.width;
+}
+
+// Every address a kernel forms is base + row * pitch + column, in 64-bit
+// integers; a region that reaches past 2^57 bytes (beyond any virtual
+// address space the GPU or the host maps) would make those sums meaningless.
+constexpr int64_t kAddressLimit = int64_t(1) << 57;
+
+bool region_fits(const Region& r) { return region_end(r) <= wide_t(kAddressLimit); }
+
 // Whether two regions share a byte.  Extents are compared first; two matrices
 // with one common pitch are then compared row against row, so interleaved
 // layouts (say x in the first N columns of a buffer, y in the next N) are
 // recognised as disjoint.  Other layouts with overlapping extents count as
-// overlapping.
+// overlapping.  All products are formed in 128 bits.
 bool overlaps(const Region& a, const Region& b) {
   if (a.base == 0 || b.base == 0 || a.rows == 0 || b.rows == 0 || a.width == 0 || b.width == 0)
     return false;
-  const int64_t a_end = a.base + (a.rows - 1) * a.pitch + a.width;
-  const int64_t b_end = b.base + (b.rows - 1) * b.pitch + b.width;
+  const wide_t a_end = region_end(a), b_end = region_end(b);
   if (a_end <= b.base || b_end <= a.base) return false;
   if (a.pitch != b.pitch || a.rows == 1 || b.rows == 1) return true;
   // Row i of a meets row j of b iff -b.width < d + k*pitch < a.width with
   // d = a.base - b.base and k = i - j in [-(b.rows-1), a.rows-1]; the middle
   // term grows with k, so only the first k past -b.width needs a look.
-  const int64_t d = a.base - b.base, p = a.pitch;
-  const int64_t k_lo = -(b.rows - 1), k_hi = a.rows - 1;
-  const int64_t num = -b.width - d;  // need k*p > num
-  int64_t k = num >= 0 ? num / p + 1 : -((-num) / p);
+  const wide_t d = wide_t(a.base) - b.base, p = a.pitch;
+  const wide_t k_lo = -wide_t(b.rows - 1), k_hi = a.rows - 1;
+  const wide_t num = -wide_t(b.width) - d;  // need k*p > num
+  wide_t k = num >= 0 ? num / p + 1 : -((-num) / p);
   if (k * p <= num) ++k;
   if (k < k_lo) k = k_lo;
   if (k > k_hi) return false;
   return d + k * p < a.width;
 }
 
-// Every output region must be disjoint from every input region and from every
-// other output region.
-bool any_overlap(std::initializer_list<Region> outs, std::initializer_list<Region> ins) {
+// Status of a call's buffers: a region past the address limit is a stride
+// error when its rows are padded (a shape error otherwise); any output that
+// shares a byte with an input or with another output is an overlap.
+int span_status(std::initializer_list<Region> outs, std::initializer_list<Region> ins) {
+  for (std::initializer_list<Region> group : {outs, ins})
+    for (const Region& r : group)
+      if (!region_fits(r))
+        return (r.rows > 1 && r.pitch != r.width) ? RMSNORM_ERR_STRIDE : RMSNORM_ERR_SHAPE;
   for (auto o = outs.begin(); o != outs.end(); ++o) {
     for (const Region& i : ins)
-      if (overlaps(*o, i)) return true;
+      if (overlaps(*o, i)) return RMSNORM_ERR_OVERLAP;
     for (auto o2 = o + 1; o2 != outs.end(); ++o2)
-      if (overlaps(*o, *o2)) return true;
+      if (overlaps(*o, *o2)) return RMSNORM_ERR_OVERLAP;
   }
-  return false;
+  return RMSNORM_OK;
 }
 
 bool bad_stride(int64_t ld, int64_t N) { return ld < N || ld > (int64_t(1) << 40); }
@@ -715,9 +736,9 @@ int check_fwd_args(const void* x, int64_t ldx, const void* gamma, float eps, int
   const int es = elem_bytes(dtype);
   if (misaligned(x, es) || misaligned(gamma, es) || misaligned(y, es) || misaligned(rstd, 4))
     return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(y, M, ldy * es, N * es), vec(rstd, M * 4)},
+  if (const int sp = span_status({matrix(y, M, ldy * es, N * es), vec(rstd, M * 4)},
                   {matrix(x, M, ldx * es, N * es), vec(gamma, N * es)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -737,10 +758,10 @@ int check_bwd_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, static_cast<rmsnorm_dtype_t>(dtype), flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+  if (const int sp = span_status({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
                    vec(gamma, N * es), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -868,11 +889,11 @@ int bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const voi
   if (st != RMSNORM_OK) return st;
   const int es = elem_bytes(dtype);
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype, flags);
-  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
+  if (const int sp = span_status({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
                    matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
                    vec(gamma, N * es), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   st = bwd_rows_launch(dy, lddy, x, ldx, gamma, rstd, M, N, dtype, flags, dx, lddx, workspace,
                        stream);
   if (st != RMSNORM_OK) return st;
@@ -962,10 +983,10 @@ int ln_fwd_impl(const void* x, int64_t ldx, const void* gamma, const void* beta,
   if (misaligned(x, es) || misaligned(gamma, es) || misaligned(beta, es) ||
       misaligned(y, es) || misaligned(mean, 4) || misaligned(rstd, 4))
     return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(y, M, ldy * es, N * es), vec(mean, M * 4), vec(rstd, M * 4)},
+  if (const int sp = span_status({matrix(y, M, ldy * es, N * es), vec(mean, M * 4), vec(rstd, M * 4)},
                   {matrix(x, M, ldx * es, N * es), vec(gamma, N * es),
                    vec(beta, beta ? N * es : 0)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   const LnPlan p = ln_plan(M, N, es, false,
                            layout_alignment({x, gamma, beta, y}, {ldx * es, ldy * es}));
   const LnFwdArgs a{x, gamma, beta, y, mean, rstd, M, static_cast<int>(N), eps, ldx * es,
@@ -994,10 +1015,10 @@ int check_ln_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx,
   const size_t need = ln_workspace_bytes(M, N, dtype);
   if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+  if (const int sp = span_status({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
                    vec(gamma, N * es), vec(mean, M * 4), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1033,9 +1054,9 @@ int check_ln_reduce_args(const void* workspace, size_t workspace_bytes, int64_t 
   const size_t need = ln_workspace_bytes(M, N, dtype);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0)},
+  if (const int sp = span_status({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0)},
                   {vec(workspace, static_cast<int64_t>(need))}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1051,11 +1072,11 @@ int ln_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, const 
   const int es = elem_bytes(dtype);
   const int gb = dgamma_elem_bytes(dtype, flags);
   const size_t need = ln_workspace_bytes(M, N, dtype);
-  if (any_overlap({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0),
+  if (const int sp = span_status({vec(dgamma, N * gb), vec(dbeta, dbeta ? N * gb : 0),
                    matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
                    vec(gamma, N * es), vec(mean, M * 4), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   st = ln_rows_launch(dy, lddy, x, ldx, gamma, mean, rstd, M, N, dtype, dx, lddx, workspace,
                       stream);
   if (st != RMSNORM_OK) return st;
@@ -1116,11 +1137,11 @@ int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const
   if (misaligned(x, es) || misaligned(res, es) || misaligned(gamma, es) || misaligned(y, es) ||
       misaligned(h, es) || misaligned(rstd, 4))
     return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(y, M, ldy * es, N * es), matrix(h, M, ldh * es, N * es),
+  if (const int sp = span_status({matrix(y, M, ldy * es, N * es), matrix(h, M, ldh * es, N * es),
                    vec(rstd, M * 4)},
                   {matrix(x, M, ldx * es, N * es), matrix(res, M, ldr * es, N * es),
                    vec(gamma, N * es)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   const LnPlan p = ln_plan(M, N, es, false,
                            layout_alignment({x, res, gamma, y, h},
                                             {ldx * es, ldr * es, ldy * es, ldh * es}),
@@ -1149,10 +1170,10 @@ int check_add_rows_args(const void* dy, int64_t lddy, const void* dh, int64_t ld
   const size_t need = add_workspace_bytes(M, N, dtype);
   if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
+  if (const int sp = span_status({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(dh, dh ? M : 0, lddh * es, N * es),
                    matrix(h, M, ldh * es, N * es), vec(gamma, N * es), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1181,9 +1202,9 @@ int check_add_reduce_args(const void* workspace, size_t workspace_bytes, int64_t
   const size_t need = add_workspace_bytes(M, N, dtype);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
+  if (const int sp = span_status({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
                   {vec(workspace, static_cast<int64_t>(need))}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1198,11 +1219,11 @@ int add_bwd_impl(const void* dy, int64_t lddy, const void* dh, int64_t lddh, con
   if (st != RMSNORM_OK) return st;
   const int es = elem_bytes(dtype);
   const size_t need = add_workspace_bytes(M, N, dtype);
-  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
+  if (const int sp = span_status({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
                    matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(dh, dh ? M : 0, lddh * es, N * es),
                    matrix(h, M, ldh * es, N * es), vec(gamma, N * es), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   st = add_rows_launch(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx, lddx,
                        workspace, stream);
   if (st != RMSNORM_OK) return st;
@@ -1250,9 +1271,9 @@ int cast_fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int6
   if (misaligned(x, kCastIn) || misaligned(gamma, kCastIn) || misaligned(y, eo) ||
       misaligned(rstd, 4))
     return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(y, M, ldy * eo, N * eo), vec(rstd, M * 4)},
+  if (const int sp = span_status({matrix(y, M, ldy * eo, N * eo), vec(rstd, M * 4)},
                   {matrix(x, M, ldx * kCastIn, N * kCastIn), vec(gamma, N * kCastIn)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   const LnPlan p = ln_plan(M, N, kCastIn, false,
                            layout_alignment({x, gamma, y}, {ldx * kCastIn, ldy * eo}));
   const CastFwdArgs a{x, gamma, y, rstd, M, static_cast<int>(N), eps,
@@ -1277,11 +1298,11 @@ int check_cast_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ld
   const size_t need = cast_workspace_bytes(M, N);
   if (workspace_bytes < need || !workspace) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({matrix(dx, M, lddx * kCastIn, N * kCastIn),
+  if (const int sp = span_status({matrix(dx, M, lddx * kCastIn, N * kCastIn),
                    vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * eo, N * eo), matrix(x, M, ldx * kCastIn, N * kCastIn),
                    vec(gamma, N * kCastIn), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1310,8 +1331,8 @@ int check_cast_reduce_args(const void* workspace, size_t workspace_bytes, int64_
   const size_t need = cast_workspace_bytes(M, N);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({vec(dgamma, N * 4)}, {vec(workspace, static_cast<int64_t>(need))}))
-    return RMSNORM_ERR_OVERLAP;
+  if (const int sp = span_status({vec(dgamma, N * 4)}, {vec(workspace, static_cast<int64_t>(need))}))
+    return sp;
   return RMSNORM_OK;
 }
 
@@ -1326,11 +1347,11 @@ int cast_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, cons
   if (st != RMSNORM_OK) return st;
   const int eo = elem_bytes(out_dtype);
   const size_t need = cast_workspace_bytes(M, N);
-  if (any_overlap({vec(dgamma, N * 4), matrix(dx, M, lddx * kCastIn, N * kCastIn),
+  if (const int sp = span_status({vec(dgamma, N * 4), matrix(dx, M, lddx * kCastIn, N * kCastIn),
                    vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * eo, N * eo), matrix(x, M, ldx * kCastIn, N * kCastIn),
                    vec(gamma, N * kCastIn), vec(rstd, M * 4)}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   st = cast_rows_launch(dy, lddy, x, ldx, gamma, rstd, M, N, out_dtype, flags, dx, lddx,
                         workspace, stream);
   if (st != RMSNORM_OK) return st;
@@ -1355,7 +1376,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_DTYPE: return "unsupported dtype (fp32, fp16 and bf16 are supported)";
     case RMSNORM_ERR_SHAPE:
       return "unsupported shape (need 0 <= M <= 2^40 and, for rmsnorm_*, 1 <= N <= 2^24 with "
-             "M*N <= 2^46; for layernorm_*, rmsnorm_add_* and rmsnorm_cast_*, 1 <= N <= 16384)";
+             "M*N <= 2^46; for layernorm_*, rmsnorm_add_* and rmsnorm_cast_*, 1 <= N <= 16384), "
+             "or a buffer ending past byte address 2^57";
     case RMSNORM_ERR_EPS: return "eps must be finite and positive";
     case RMSNORM_ERR_FLAGS: return "unknown flag bits";
     case RMSNORM_ERR_WORKSPACE:
@@ -1364,7 +1386,9 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
     case RMSNORM_ERR_LAUNCH: return "kernel launch failed";
     case RMSNORM_ERR_ARGUMENT: return "invalid argument";
-    case RMSNORM_ERR_STRIDE: return "a row stride is smaller than N (or above 2^40)";
+    case RMSNORM_ERR_STRIDE:
+      return "a row stride is smaller than N or above 2^40, or a padded matrix ends past byte "
+             "address 2^57";
     default: return "unknown status";
   }
 }
@@ -1419,9 +1443,9 @@ int rmsnorm_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_t M,
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
   if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
-  if (any_overlap({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
+  if (const int sp = span_status({vec(dgamma, N * dgamma_elem_bytes(dtype, flags))},
                   {vec(workspace, static_cast<int64_t>(need))}))
-    return RMSNORM_ERR_OVERLAP;
+    return sp;
   return bwd_reduce_launch(workspace, M, N, dtype, flags, dgamma, stream);
 }
 

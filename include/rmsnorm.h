@@ -42,6 +42,11 @@
  *    invalid call returns a negative status and writes nothing.  There is no
  *    fallback path: an unsupported input is an error.
  *  - Outputs must not overlap inputs or each other (RMSNORM_ERR_OVERLAP).
+ *  - Every buffer must end below byte address 2^57 (base + (M-1)*pitch +
+ *    row bytes, formed without overflow); a matrix past that limit is
+ *    RMSNORM_ERR_STRIDE when its rows are padded (ld > N) and
+ *    RMSNORM_ERR_SHAPE otherwise, so the kernels' 64-bit address sums
+ *    cannot wrap.
  *  - Pointers must be aligned to their element size (RMSNORM_ERR_ALIGNMENT);
  *    the workspace to 16 bytes.  Wider alignment lets the kernels use wider
  *    (up to 16-byte) accesses.
@@ -67,7 +72,12 @@ extern "C" {
 typedef enum {
   RMSNORM_F32 = 0,
   RMSNORM_F16 = 1,
-  RMSNORM_BF16 = 2
+  RMSNORM_BF16 = 2,
+  /* Not dtypes.  They widen the enum to every 32-bit value, so that any code
+   * a C or foreign-function caller passes is a defined value of the type,
+   * which the library then rejects with RMSNORM_ERR_DTYPE. */
+  RMSNORM_DTYPE_ENUM_MIN_ = -2147483647 - 1,
+  RMSNORM_DTYPE_ENUM_MAX_ = 2147483647
 } rmsnorm_dtype_t;
 
 /* flags */
@@ -92,7 +102,8 @@ typedef enum {
 #define RMSNORM_ERR_OVERLAP (-8)
 #define RMSNORM_ERR_LAUNCH (-9)
 #define RMSNORM_ERR_ARGUMENT (-10)
-#define RMSNORM_ERR_STRIDE (-11) /* a row stride below N (or above 2^40) */
+#define RMSNORM_ERR_STRIDE (-11) /* a row stride below N or above 2^40, or a
+                                   padded matrix ending past byte 2^57 */
 
 /*
  * Forward: y = x * r * g per row, and rstd[i] = r_i (float32) kept for the

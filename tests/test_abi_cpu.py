@@ -181,6 +181,38 @@ def test_bwd_strided_rejects():
     assert call(dg=None) == ENULL
 
 
+# Layouts whose span (M - 1) * pitch passes 2^63 (or the 2^57 address limit)
+# with y == x: validation must refuse them (a stride error), never let them
+# reach a launch.  Before spans were formed in 128 bits, (M - 1) * pitch
+# wrapped and M = 2^40, ld = 2^40 passed validation.
+@pytest.mark.parametrize("ld", [1 << 40, 1 << 22, 1 << 30])
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_fwd_strided_span_past_the_address_limit(ld, dtype):
+    M = 1 << 40
+    assert fwd_strided_call(x=A, ldx=ld, y=A, ldy=ld, M=M, N=1, dtype=dtype) == ESTRIDE
+    assert fwd_strided_call(x=A, ldx=ld, M=M, N=1, dtype=dtype) == ESTRIDE
+
+
+def test_bwd_strided_span_past_the_address_limit():
+    L = lib()
+    for ld in (1 << 40, 1 << 22):
+        st = L.rmsnorm_bwd_strided(A, ld, A, ld, A + 64, A + 128, 1 << 40, 1, 2, 0, A, ld,
+                                   A + 256, A + 512, 1 << 40, None)
+        assert st == ESTRIDE
+
+
+def test_dense_rows_past_the_address_limit():
+    top = (1 << 57) - 1024
+    assert fwd_call(x=top) == ESHAPE
+
+
+def test_overlap_found_at_large_pitches():
+    # y's row 0 is x's row 1 with a pitch of 2^40 elements (2^41 bytes):
+    # the extent (about 2^55 bytes) fits, the rows meet.
+    ld = 1 << 40
+    assert fwd_strided_call(x=A, ldx=ld, y=A + 2 * ld, ldy=ld, M=1 << 14, N=8) == EOVL
+
+
 def test_shape_status_string_names_each_family_limit():
     s = rn.rmsnorm_status_string(-3)
     assert "2^24" in s and "16384" in s and "layernorm_" in s

@@ -39,6 +39,11 @@ def fwd_call(x=A, ldx=None, g=A + S, b=A + 2 * S, eps=1e-5, M=4, N=256, dtype=2,
     ({"mean": A + S + 8}, EOVL),            # mean overlaps gamma
     ({"rstd": A + 2 * S + 4}, EOVL),        # rstd overlaps beta
     ({"rstd": A + 4 * S + 8}, EOVL),        # rstd overlaps mean
+    # spans past the 2^57 address limit ((M - 1) * pitch passes 2^63 at the
+    # first two pitches), y == x: a stride error, never a launch
+    ({"M": 1 << 40, "N": 1, "ldx": 1 << 40, "ldy": 1 << 40, "y": A}, ESTRIDE),
+    ({"M": 1 << 40, "N": 1, "ldx": 1 << 22, "ldy": 1 << 22, "y": A}, ESTRIDE),
+    ({"M": 1 << 40, "N": 1, "ldx": 1 << 30}, ESTRIDE),
 ])
 def test_fwd_rejects(kw, code):
     assert fwd_call(**kw) == code

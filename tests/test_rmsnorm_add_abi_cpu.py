@@ -39,6 +39,9 @@ def fwd_call(x=A, res=A + S, g=A + 2 * S, eps=1e-6, M=4, N=256, dtype=2, flags=0
     ({"h": A + S + 32}, EOVL),            # h overlaps res (in place is not accepted)
     ({"y": A + 4 * S + 8}, EOVL),         # y overlaps h
     ({"rstd": A + 2 * S}, EOVL),          # rstd overlaps gamma
+    # spans past the 2^57 address limit, h == res: a stride error, never a launch
+    ({"M": 1 << 40, "N": 1, "ldr": 1 << 40, "ldh": 1 << 40, "h": A + S}, ESTRIDE),
+    ({"M": 1 << 40, "N": 1, "ldr": 1 << 22, "ldh": 1 << 22, "h": A + S}, ESTRIDE),
 ])
 def test_fwd_rejects(kw, code):
     assert fwd_call(**kw) == code

@@ -42,6 +42,9 @@ def fwd_call(x=A, g=A + S, eps=1e-6, M=4, N=256, dtype=F32, out=BF16, flags=0, y
     ({"y": A + 64}, EOVL),                  # y overlaps x
     ({"rstd": A + S + 8}, EOVL),            # rstd overlaps gamma
     ({"rstd": A + 2 * S + 16}, EOVL),       # rstd overlaps y
+    # spans past the 2^57 address limit, y == x: a stride error, never a launch
+    ({"M": 1 << 40, "N": 1, "ldx": 1 << 40, "ldy": 1 << 40, "y": A}, ESTRIDE),
+    ({"M": 1 << 40, "N": 1, "ldx": 1 << 22, "ldy": 1 << 22, "y": A}, ESTRIDE),
 ])
 def test_fwd_rejects(kw, code):
     assert fwd_call(**kw) == code
