@@ -7,12 +7,19 @@ dtype and whose intermediates are float32.  Its distance to the float64 golden
 this precision makes; the gate lets the kernel have at most a fixed multiple of
 it (see ``oracle.gate``).
 
-The forward follows ``rmsnorm_reference`` and the backward the explicit
-``manual_backward`` formula of the page "Check an AI model calculation before
-accelerating it", section "PyTorch reference: the numerical oracle", with the
-inputs promoted to float32 first (section "Why convert before reducing?").
-Offset mode forms ``1 + w`` after promotion to float32, as the torchtitan
-page's ``_offset_rms_norm_reference`` does.  rstd and dgamma are float32.
+The arithmetic is the definition of RMSNorm and of its exact gradient, as the
+page "Check an AI model calculation before accelerating it" states them
+(sections "Problem and reference formula", "Input backward pass: keep the
+right N" and "A sum is not an average"), evaluated in float32 after the
+inputs are promoted (section "Why convert before reducing?"):
+
+* ``ss = sum_j x_j^2``, ``r = 1/sqrt(ss/N + eps)``, ``xhat = x*r``,
+  ``y = xhat*g``;
+* ``u = dy*g``, ``c = sum_j u_j*x_j / N``, ``dx = r*(u - x*r^2*c)``;
+* ``dgamma_j = sum_i dy_ij*xhat_ij``.
+
+Offset mode forms ``g = 1 + w`` after promotion to float32, as the torchtitan
+page's offset reference does.  rstd and dgamma are float32.
 
 ``reference_backward_autograd`` is the torchtitan page's variant (autograd of
 the eager float32 formula); it is logged beside the explicit formula, while the
@@ -34,14 +41,27 @@ def _weight32(weight, offset):
     return 1.0 + g if offset else g
 
 
+def _row_rstd32(xf, eps):
+    """Per-row r = 1/sqrt(sum(x^2)/N + eps) in float32, kept as a column."""
+    n = xf.shape[-1]
+    ss = (xf * xf).sum(-1, keepdim=True)
+    return torch.rsqrt(ss / n + eps)
+
+
+def _column_sums32(t):
+    """float32 sums over the rows of t, one per column.  Each column is summed
+    as its own contiguous vector, so its result does not depend on which other
+    columns are summed beside it."""
+    return t.t().contiguous().sum(-1)
+
+
 def reference_forward(x, weight, eps=DEFAULT_EPS, offset=False):
     """Returns ``(y, rstd)``: y in x's dtype [M, N], rstd float32 [M]."""
-    x2 = _rows2d(x.detach().to("cpu"))
-    xf = x2.float()
+    xf = _rows2d(x.detach().to("cpu")).float()
     g = _weight32(weight, offset)
-    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
-    y = (xf * r * g).to(x.dtype)
-    return y, r.squeeze(-1)
+    r = _row_rstd32(xf, eps)
+    y = (xf * r) * g
+    return y.to(x.dtype), r.squeeze(-1)
 
 
 def reference_backward(dy, x, weight, eps=DEFAULT_EPS, offset=False):
@@ -49,34 +69,31 @@ def reference_backward(dy, x, weight, eps=DEFAULT_EPS, offset=False):
 
     dx has x's dtype [M, N]; dgamma is float32 [N] (a sum over rows).
     """
-    x2 = _rows2d(x.detach().to("cpu"))
-    dy2 = _rows2d(dy.detach().to("cpu"))
-    xf = x2.float()
-    dyf = dy2.float()
+    xf = _rows2d(x.detach().to("cpu")).float()
+    dyf = _rows2d(dy.detach().to("cpu")).float()
     g = _weight32(weight, offset)
-    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
+    n = xf.shape[-1]
+    r = _row_rstd32(xf, eps)
     u = dyf * g
-    dx = r * u - xf * r.pow(3) * (u * xf).mean(-1, keepdim=True)
-    dgamma = (dyf * xf * r).sum(0)
+    c = (u * xf).sum(-1, keepdim=True) / n
+    dx = r * (u - xf * (r * r) * c)
+    dgamma = _column_sums32(dyf * (xf * r))
     return dx.to(x.dtype), dgamma
 
 
 def reference_dgamma(dy, x, eps=DEFAULT_EPS, cols=None):
     """dgamma of ``reference_backward`` restricted to some columns.
 
-    Same float32 arithmetic: r from whole rows, then (dy*x*r) summed over
+    Same float32 arithmetic: r from whole rows, then dy*(x*r) summed over
     rows for the selected columns only."""
-    x2 = _rows2d(x.detach().to("cpu"))
+    xf = _rows2d(x.detach().to("cpu")).float()
     dy2 = _rows2d(dy.detach().to("cpu"))
-    xf = x2.float()
-    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
+    r = _row_rstd32(xf, eps)
     if cols is not None:
         idx = torch.as_tensor(cols, dtype=torch.long)
         xf = xf[:, idx]
-        dyf = dy2[:, idx].float()
-    else:
-        dyf = dy2.float()
-    return (dyf * xf * r).sum(0)
+        dy2 = dy2[:, idx]
+    return _column_sums32(dy2.float() * (xf * r))
 
 
 def reference_backward_autograd(dy, x, weight, eps=DEFAULT_EPS, offset=False):
@@ -86,7 +103,6 @@ def reference_backward_autograd(dy, x, weight, eps=DEFAULT_EPS, offset=False):
     xf = x2.float().requires_grad_(True)
     w = weight.detach().to("cpu").float().reshape(-1).requires_grad_(True)
     g = 1.0 + w if offset else w
-    r = torch.rsqrt(xf.square().mean(-1, keepdim=True) + eps)
-    y = xf * r * g
+    y = (xf * _row_rstd32(xf, eps)) * g
     dx, dw = torch.autograd.grad(y, (xf, w), dy2.float())
     return dx.to(x.dtype), dw
