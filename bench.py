@@ -18,6 +18,15 @@ device copy as an achievable-bandwidth reference, and the CPU oracle's
 throughput on the same workload as ``cpu_baseline`` (the float64 golden on
 one thread, with the float32 torch CPU reference timed beside it).
 
+Three timing scopes are reported.  ``value`` comes from the K timed steps,
+back to back on one set of buffers (W untimed steps first).  ``cold_cache``
+is the per-call protocol: 50 samples per pass, each call preceded by an
+untimed 1 GiB read that evicts L2 and the Infinity Cache, median reported
+(with p10/p90).  ``rotating_warm`` times back-to-back steps that cycle over
+three independent buffer sets, so no step finds its inputs in the 256 MB
+Infinity Cache from the step before.  The cold-cache and rotating legs run
+before the warmup, so the timed steps start on a GPU that is already busy.
+
 ``--op layernorm`` measures the LayerNorm path of the same library instead
 (layernorm_fwd, layernorm_bwd_rows, layernorm_bwd_reduce) on the LayerNorm
 inputs of the workload (the same x, gamma and dy draws plus a bias and
@@ -100,6 +109,26 @@ def alg_bytes(M, N, s, op="rmsnorm"):
     return fwd, bwd_rows, bwd_reduce
 
 
+OP_NAMES = {"rmsnorm": "RMSNorm", "layernorm": "LayerNorm",
+            "add_rmsnorm": "residual add + RMSNorm", "rmsnorm_cast": "RMSNorm + output cast"}
+DTYPE_NAMES = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
+
+
+def metric_label(op, dtype, M, N):
+    """The metric named after the op and the workload's own dtype and shape."""
+    return (f"{OP_NAMES[op]} fwd/bwd achieved HBM GB/s and % of peak, "
+            f"{DTYPE_NAMES[dtype]} M={M} N={N}")
+
+
+def metric_for(op, workload):
+    """The metric line of ``--op op --workload workload``: the cast path reads
+    float32 x, the others the workload's own dtype."""
+    from backward_rmsnorm_fwd_amd import workloads
+    wl = workloads.WORKLOADS[workload]
+    dtype = torch.float32 if op == "rmsnorm_cast" else wl.dtype
+    return metric_label(op, dtype, wl.M, wl.N)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +139,10 @@ def parse():
     ap.add_argument("--workload", default="c2", help="workload name (c2..c5)")
     ap.add_argument("--op", choices=("rmsnorm", "layernorm", "add_rmsnorm", "rmsnorm_cast"),
                     default="rmsnorm")
-    ap.add_argument("--cold-samples", type=int, default=30)
+    ap.add_argument("--cold-samples", type=int, default=50)
+    ap.add_argument("--rotating-sets", type=int, default=3,
+                    help="independent buffer sets the rotating-warm leg cycles over")
+    ap.add_argument("--rotating-steps", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1 << 62,
                     help="rows of the workload the CPU oracle is timed on")
@@ -156,64 +188,151 @@ def main():
     inp = make(args.workload)
     M, N, T, off, eps = inp["M"], inp["N"], inp["dtype"], inp["offset"], inp["eps"]
     s = torch.tensor([], dtype=T).element_size()
-    x, w, dy = (inp[k].to(dev) for k in ("x", "w", "dy"))
-    y = torch.empty_like(x, dtype=cast_to) if cast else torch.empty_like(x)
-    rstd = torch.empty(M, device=dev, dtype=torch.float32)
-    dx = torch.empty_like(x)
-    dgamma = torch.empty(N, device=dev, dtype=torch.float32)
     if ln:
-        bias = inp["b"].to(dev)
-        mean = torch.empty(M, device=dev, dtype=torch.float32)
-        dbeta = torch.empty(N, device=dev, dtype=torch.float32)
         nbytes = rn.layernorm_bwd_workspace_bytes(M, N, T)
     elif fused:
-        res, dh = inp["res"].to(dev), inp["dh"].to(dev)
-        h = torch.empty_like(x)
         nbytes = rn.rmsnorm_add_bwd_workspace_bytes(M, N, T, off)
     elif cast:
         nbytes = rn.rmsnorm_cast_bwd_workspace_bytes(M, N, cast_to, off)
     else:
         nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, T, off)
-    ws = torch.empty(max(4, nbytes) // 4, device=dev, dtype=torch.float32)
+
+    def alloc_set(src=None):
+        """Device buffers of one step: inputs copied from `src` (another set)
+        or from the host draws, outputs and workspace fresh."""
+        b = {}
+        for k in ("x", "w", "dy") + (("b",) if ln else ()) + (("res", "dh") if fused else ()):
+            b[k] = src[k].clone() if src is not None else inp[k].to(dev)
+        x = b["x"]
+        b["y"] = torch.empty_like(x, dtype=cast_to) if cast else torch.empty_like(x)
+        b["rstd"] = torch.empty(M, device=dev, dtype=torch.float32)
+        b["dx"] = torch.empty_like(x)
+        b["dgamma"] = torch.empty(N, device=dev, dtype=torch.float32)
+        if ln:
+            b["mean"] = torch.empty(M, device=dev, dtype=torch.float32)
+            b["dbeta"] = torch.empty(N, device=dev, dtype=torch.float32)
+        if fused:
+            b["h"] = torch.empty_like(x)
+        b["ws"] = torch.empty(max(4, nbytes) // 4, device=dev, dtype=torch.float32)
+        return b
+
+    def stages_for(b):
+        x, w, dy, y, rstd, dx, dgamma, ws = (b[k] for k in ("x", "w", "dy", "y", "rstd", "dx",
+                                                             "dgamma", "ws"))
+        if fused:
+            res, dh, h = b["res"], b["dh"], b["h"]
+
+            def fwd():
+                rn.rmsnorm_add_fwd(x, res, w, eps, y, h, rstd, off)
+
+            def bwd_rows():
+                rn.rmsnorm_add_bwd_rows(dy, dh, h, w, rstd, dx, ws, off)
+
+            def bwd_reduce():
+                rn.rmsnorm_add_bwd_reduce(ws, M, N, T, dgamma, off)
+        elif cast:
+            def fwd():
+                rn.rmsnorm_cast_fwd(x, w, eps, y, rstd, off)
+
+            def bwd_rows():
+                rn.rmsnorm_cast_bwd_rows(dy, x, w, rstd, dx, ws, off)
+
+            def bwd_reduce():
+                rn.rmsnorm_cast_bwd_reduce(ws, M, N, cast_to, dgamma, off)
+        elif ln:
+            bias, mean, dbeta = b["b"], b["mean"], b["dbeta"]
+
+            def fwd():
+                rn.layernorm_fwd(x, w, bias, eps, y, mean, rstd)
+
+            def bwd_rows():
+                rn.layernorm_bwd_rows(dy, x, w, mean, rstd, dx, ws)
+
+            def bwd_reduce():
+                rn.layernorm_bwd_reduce(ws, M, N, T, dgamma, dbeta)
+        else:
+            def fwd():
+                rn.rmsnorm_fwd(x, w, eps, y, rstd, off)
+
+            def bwd_rows():
+                rn.rmsnorm_bwd_rows(dy, x, w, rstd, dx, ws, off)
+
+            def bwd_reduce():
+                rn.rmsnorm_bwd_reduce(ws, M, N, T, dgamma, off)
+        return fwd, bwd_rows, bwd_reduce
+
+    main_set = alloc_set()
+    x, w, dy = main_set["x"], main_set["w"], main_set["dy"]
+    if fused:
+        res, dh = main_set["res"], main_set["dh"]
+    fwd, bwd_rows, bwd_reduce = stages_for(main_set)
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    fb, rb, db = alg_bytes(M, N, s, args.op)
+    step_bytes = fb + rb + db
 
-    if fused:
-        def fwd():
-            rn.rmsnorm_add_fwd(x, res, w, eps, y, h, rstd, off)
+    # ---- cold-cache per-call samples (the primary per-call protocol) ----
+    # Before each sample a 1 GiB buffer is read (not written), so L2 and the
+    # 256 MB Infinity Cache hold only clean, unrelated lines.
+    flush = torch.ones(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
+    for _ in range(3):
+        for f in (fwd, bwd_rows, bwd_reduce):
+            f()
+    cold = {}
+    for name, calls in (("fwd", [fwd]), ("bwd", [bwd_rows, bwd_reduce])):
+        if args.cold_samples <= 0:
+            break
+        samples = []
+        for _ in range(args.cold_samples):
+            flush.sum()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for f in calls:
+                f()
+            b.record()
+            b.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3)
+        samples.sort()
+        med = statistics.median(samples)
+        nb = fb if name == "fwd" else rb + db
+        cold[name] = {"median_us": round(med, 2),
+                      "p10_us": round(samples[len(samples) // 10], 2),
+                      "p90_us": round(samples[(9 * len(samples)) // 10], 2),
+                      "GBps": round(nb / (med * 1e-6) / 1e9, 1),
+                      "pct_of_8TBps": round(100 * nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    if cold:
+        step_cold = cold["fwd"]["median_us"] + cold["bwd"]["median_us"]
+        cold["samples_per_pass"] = args.cold_samples
+        cold["flush_bytes"] = flush.numel() * 4
+        cold["step_us"] = round(step_cold, 2)
+        cold["GBps"] = round(step_bytes / (step_cold * 1e-6) / 1e9, 1)
+        cold["pct_of_8TBps"] = round(100 * cold["GBps"] / HBM_PEAK_GBS, 1)
+    del flush
 
-        def bwd_rows():
-            rn.rmsnorm_add_bwd_rows(dy, dh, h, w, rstd, dx, ws, off)
-
-        def bwd_reduce():
-            rn.rmsnorm_add_bwd_reduce(ws, M, N, T, dgamma, off)
-    elif cast:
-        def fwd():
-            rn.rmsnorm_cast_fwd(x, w, eps, y, rstd, off)
-
-        def bwd_rows():
-            rn.rmsnorm_cast_bwd_rows(dy, x, w, rstd, dx, ws, off)
-
-        def bwd_reduce():
-            rn.rmsnorm_cast_bwd_reduce(ws, M, N, cast_to, dgamma, off)
-    elif ln:
-        def fwd():
-            rn.layernorm_fwd(x, w, bias, eps, y, mean, rstd)
-
-        def bwd_rows():
-            rn.layernorm_bwd_rows(dy, x, w, mean, rstd, dx, ws)
-
-        def bwd_reduce():
-            rn.layernorm_bwd_reduce(ws, M, N, T, dgamma, dbeta)
-    else:
-        def fwd():
-            rn.rmsnorm_fwd(x, w, eps, y, rstd, off)
-
-        def bwd_rows():
-            rn.rmsnorm_bwd_rows(dy, x, w, rstd, dx, ws, off)
-
-        def bwd_reduce():
-            rn.rmsnorm_bwd_reduce(ws, M, N, T, dgamma, off)
+    # ---- rotating warm: back-to-back steps over independent buffer sets ----
+    rotating = None
+    if args.rotating_sets > 1 and args.rotating_steps > 0:
+        sets = [main_set] + [alloc_set(main_set) for _ in range(args.rotating_sets - 1)]
+        rot_stages = [stages_for(b) for b in sets]
+        for i in range(2 * len(sets)):
+            for f in rot_stages[i % len(sets)]:
+                f()
+        torch.cuda.synchronize()
+        t_rot = time.perf_counter()
+        for i in range(args.rotating_steps):
+            for f in rot_stages[i % len(sets)]:
+                f()
+        torch.cuda.synchronize()
+        rot_us = (time.perf_counter() - t_rot) * 1e6 / args.rotating_steps
+        per_set = sum(t.numel() * t.element_size() for t in sets[1].values())
+        rotating = {"sets": len(sets), "steps": args.rotating_steps,
+                    "bytes_per_set": per_set, "step_us": round(rot_us, 2),
+                    "GBps": round(step_bytes / (rot_us * 1e-6) / 1e9, 1),
+                    "pct_of_8TBps": round(100 * step_bytes / (rot_us * 1e-6) / 1e9
+                                          / HBM_PEAK_GBS, 1)}
+        del sets, rot_stages
+        torch.cuda.synchronize()
 
     stages = [("fwd", fwd), ("bwd_rows", bwd_rows), ("bwd_reduce", bwd_reduce)]
     for _ in range(args.warmup):
@@ -263,8 +382,6 @@ def main():
         torch.cuda.synchronize()
         per_kernel_us[k] = statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
 
-    fb, rb, db = alg_bytes(M, N, s, args.op)
-    step_bytes = fb + rb + db
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = rb / (dominant_us * 1e-6) / 1e9
 
@@ -316,35 +433,6 @@ def main():
         torch.cuda.synchronize()
         unfused_us = (time.perf_counter() - t) * 1e6 / n_unf
         del y32, y2, dy32, dx2, ws2
-
-    # ---- cold-cache per-call samples ----
-    # Before each sample a 1 GiB buffer is read (not written), so L2 and the
-    # 256 MB Infinity Cache hold only clean, unrelated lines.
-    flush = torch.ones(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
-    cold = {}
-    for name, calls in (("fwd", [fwd]), ("bwd", [bwd_rows, bwd_reduce])):
-        if args.cold_samples <= 0:
-            break
-        samples = []
-        for _ in range(args.cold_samples):
-            flush.sum()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for f in calls:
-                f()
-            b.record()
-            b.synchronize()
-            samples.append(a.elapsed_time(b) * 1e3)
-        samples.sort()
-        med = statistics.median(samples)
-        nbytes = fb if name == "fwd" else rb + db
-        cold[name] = {"median_us": round(med, 2),
-                      "p10_us": round(samples[len(samples) // 10], 2),
-                      "p90_us": round(samples[(9 * len(samples)) // 10], 2),
-                      "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                      "pct_of_8TBps": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-    del flush
 
     # ---- plain device copy of 1 GiB, for an achievable-bandwidth reference ----
     src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
@@ -425,9 +513,7 @@ def main():
                                       f"median of 3 runs of {ref_s:.2f} s"}}
 
     result = {
-        "metric": ("LayerNorm" if ln else "residual add + RMSNorm" if fused
-                   else "RMSNorm + output cast" if cast else "RMSNorm")
-        + " fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096",
+        "metric": metric_for(args.op, args.workload),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -455,6 +541,7 @@ def main():
                 "GBps": round((rb + db) / ((per_kernel_us["bwd_rows"]
                                             + per_kernel_us["bwd_reduce"]) * 1e-6) / 1e9, 1)},
         "cold_cache": cold,
+        "rotating_warm": rotating,
         "device_copy_GBps": round(copy_gbs, 1),
         "unfused_step_us": None if unfused_us is None else round(unfused_us, 2),
         "roofline": {"kernel": ("ln_bwd_rows" if ln else "add_bwd_rows" if fused

@@ -102,3 +102,16 @@ def test_unsupported_workloads_are_refused_before_any_gpu_work(argv, needle):
     assert res.returncode == 2
     assert needle in res.stderr
     assert res.stdout == ""
+
+
+@pytest.mark.parametrize("op,workload,label", [
+    ("rmsnorm", "c2", "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, bf16 M=32768 N=4096"),
+    ("rmsnorm", "c3", "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, fp16 M=262144 N=1024"),
+    ("rmsnorm", "c4", "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, bf16 M=2048 N=65536"),
+    ("rmsnorm", "c5", "RMSNorm fwd/bwd achieved HBM GB/s and % of peak, bf16 M=65536 N=5120"),
+    ("layernorm", "c3", "LayerNorm fwd/bwd achieved HBM GB/s and % of peak, fp16 M=262144 N=1024"),
+    ("rmsnorm_cast", "c2",
+     "RMSNorm + output cast fwd/bwd achieved HBM GB/s and % of peak, fp32 M=32768 N=4096"),
+])
+def test_metric_names_the_workload(op, workload, label):
+    assert bench.metric_for(op, workload) == label
