@@ -153,60 +153,124 @@ class GateRow:
         return d
 
 
+class TensorGate:
+    """The gate of one output tensor, fed in row chunks.
+
+    ``add(target, reference, golden)`` takes one chunk of rows (the golden
+    float64 NumPy); ``finish()`` returns the GateRow.  Every quantity of the
+    gate is a maximum (reference and target error, rounding floor, golden
+    scale) or a sum (the rounding-bias numerator and denominator), so a tensor
+    fed in chunks gets the row it would get whole: full-size tensors can be
+    gated on every element without holding them in float64 at once."""
+
+    def __init__(self, name, out_dtype, shape, condition=None, fudge=FUDGE_FACTOR,
+                 project_atol=PROJECT_ATOL, max_ref_rel=MAX_REFERENCE_RELATIVE_ERROR):
+        self.out_dtype = out_dtype
+        self.want = str(_as_torch_dtype(out_dtype)).replace("torch.", "")
+        self.row = GateRow(tensor=name, dtype=self.want, shape=tuple(shape), condition=condition)
+        self.fudge, self.project_atol, self.max_ref_rel = fudge, project_atol, max_ref_rel
+        self.failed = None      # structure failure of the target
+        self.ref_failed = None  # structure failure of the reference
+        self.ref_err = self.tgt_err = self.floor = self.scale = 0.0
+        self.bias = {"t": [0.0, 0.0, 0], "r": [0.0, 0.0, 0]}  # sum(e*s), sum|e|, count
+        self.any_finite = False
+
+    @staticmethod
+    def _bias_terms(a, g, acc):
+        mask = np.isfinite(g) & np.isfinite(a)
+        e = a[mask] - g[mask]
+        sg = np.sign(g[mask])
+        keep = (e != 0) & (sg != 0)
+        e, sg = e[keep], sg[keep]
+        acc[0] += float(np.sum(e * sg))
+        acc[1] += float(np.sum(np.abs(e)))
+        acc[2] += int(e.size)
+
+    def add(self, target, reference, golden):
+        golden = np.asarray(golden, dtype=np.float64)
+        if self.failed is not None:
+            return
+        why = structure_mismatch(target, golden, self.out_dtype)
+        if why is not None:
+            self.failed = why
+            return
+        if self.ref_failed is None:
+            why = structure_mismatch(reference, golden, self.out_dtype)
+            if why is not None:
+                self.ref_failed = why
+                return
+        t = _to_f64(target)
+        r = _to_f64(reference)
+        self.ref_err = max(self.ref_err, _max_abs_err(r, golden))
+        self.tgt_err = max(self.tgt_err, _max_abs_err(t, golden))
+        self.floor = max(self.floor, rounding_floor(golden, self.out_dtype))
+        fin = np.isfinite(golden)
+        if fin.any():
+            self.any_finite = True
+            self.scale = max(self.scale, float(np.max(np.abs(golden[fin]))))
+        if self.want in ("bfloat16", "float16"):
+            self._bias_terms(t.ravel(), golden.ravel(), self.bias["t"])
+            self._bias_terms(r.ravel(), golden.ravel(), self.bias["r"])
+
+    @staticmethod
+    def _bias(acc):
+        if acc[2] < ROUNDING_BIAS_MIN_ELEMENTS:
+            return None
+        return acc[0] / acc[1]
+
+    def finish(self):
+        row = self.row
+        if self.failed is not None:
+            row.verdict = "FAIL"
+            row.note = "structure: " + self.failed
+            return row
+        if self.ref_failed is not None:
+            row.verdict = "INCONCLUSIVE"
+            row.note = "reference structure: " + self.ref_failed
+            return row
+        row.reference_error = self.ref_err
+        row.target_error = self.tgt_err
+        row.rounding_floor = self.floor
+        row.absolute_floor = max(self.project_atol, row.rounding_floor)
+        row.threshold = self.fudge * row.reference_error + row.absolute_floor
+        row.golden_scale = self.scale if self.any_finite else 0.0
+        denom = max(row.golden_scale, row.absolute_floor)
+        if denom > 0:
+            row.reference_relative_error = row.reference_error / denom
+        else:
+            row.reference_relative_error = 0.0 if row.reference_error == 0 else float("inf")
+        row.gate_valid = row.reference_relative_error <= self.max_ref_rel
+        if not row.gate_valid:
+            row.verdict = "INCONCLUSIVE"
+            row.note = "reference is too inaccurate to gate the target"
+            return row
+        ok = row.target_error <= row.threshold
+        notes = []
+        if self.want in ("bfloat16", "float16"):
+            row.bias_target = self._bias(self.bias["t"])
+            row.bias_reference = self._bias(self.bias["r"])
+            if row.bias_target is not None:
+                lim = ROUNDING_BIAS_MAX
+                if row.bias_reference is not None:
+                    lim = max(lim, 2.0 * abs(row.bias_reference))
+                if abs(row.bias_target) > lim:
+                    ok = False
+                    notes.append(f"rounding bias {row.bias_target:+.3f} beyond {lim:.3f}")
+        if row.target_error > row.threshold:
+            notes.append("target_error above threshold")
+        row.verdict = "PASS" if ok else "FAIL"
+        row.note = "; ".join(notes)
+        return row
+
+
 def gate_tensor(name, target, reference, golden, out_dtype, condition=None,
                 fudge=FUDGE_FACTOR, project_atol=PROJECT_ATOL,
                 max_ref_rel=MAX_REFERENCE_RELATIVE_ERROR):
     """Gate one output tensor.  ``golden`` is float64 NumPy."""
     golden = np.asarray(golden, dtype=np.float64)
-    want = str(_as_torch_dtype(out_dtype)).replace("torch.", "")
-    row = GateRow(tensor=name, dtype=want, shape=tuple(golden.shape),
-                  condition=condition)
-    why = structure_mismatch(target, golden, out_dtype)
-    if why is not None:
-        row.verdict = "FAIL"
-        row.note = "structure: " + why
-        return row
-    why = structure_mismatch(reference, golden, out_dtype)
-    if why is not None:
-        row.verdict = "INCONCLUSIVE"
-        row.note = "reference structure: " + why
-        return row
-    t = _to_f64(target)
-    r = _to_f64(reference)
-    row.reference_error = _max_abs_err(r, golden)
-    row.target_error = _max_abs_err(t, golden)
-    row.rounding_floor = rounding_floor(golden, out_dtype)
-    row.absolute_floor = max(project_atol, row.rounding_floor)
-    row.threshold = fudge * row.reference_error + row.absolute_floor
-    fin = np.isfinite(golden)
-    row.golden_scale = float(np.max(np.abs(golden[fin]))) if fin.any() else 0.0
-    denom = max(row.golden_scale, row.absolute_floor)
-    if denom > 0:
-        row.reference_relative_error = row.reference_error / denom
-    else:
-        row.reference_relative_error = 0.0 if row.reference_error == 0 else float("inf")
-    row.gate_valid = row.reference_relative_error <= max_ref_rel
-    if not row.gate_valid:
-        row.verdict = "INCONCLUSIVE"
-        row.note = "reference is too inaccurate to gate the target"
-        return row
-    ok = row.target_error <= row.threshold
-    notes = []
-    if want in ("bfloat16", "float16"):
-        row.bias_target = rounding_bias(t, golden)
-        row.bias_reference = rounding_bias(r, golden)
-        if row.bias_target is not None:
-            lim = ROUNDING_BIAS_MAX
-            if row.bias_reference is not None:
-                lim = max(lim, 2.0 * abs(row.bias_reference))
-            if abs(row.bias_target) > lim:
-                ok = False
-                notes.append(f"rounding bias {row.bias_target:+.3f} beyond {lim:.3f}")
-    if row.target_error > row.threshold:
-        notes.append("target_error above threshold")
-    row.verdict = "PASS" if ok else "FAIL"
-    row.note = "; ".join(notes)
-    return row
+    g = TensorGate(name, out_dtype, golden.shape, condition, fudge, project_atol, max_ref_rel)
+    g.add(target, reference, golden)
+    return g.finish()
 
 
 def gate_rstd(target_rstd, golden_r, reference_rstd=None,

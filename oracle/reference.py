@@ -16,7 +16,8 @@ inputs are promoted (section "Why convert before reducing?"):
 * ``ss = sum_j x_j^2``, ``r = 1/sqrt(ss/N + eps)``, ``xhat = x*r``,
   ``y = xhat*g``;
 * ``u = dy*g``, ``c = sum_j u_j*x_j / N``, ``dx = r*(u - x*r^2*c)``;
-* ``dgamma_j = sum_i dy_ij*xhat_ij``.
+* ``dgamma_j = sum_i dy_ij*x_ij*r_i``, products taken left to right as the
+  formula is written.
 
 Offset mode forms ``g = 1 + w`` after promotion to float32, as the torchtitan
 page's offset reference does.  rstd and dgamma are float32.
@@ -77,15 +78,15 @@ def reference_backward(dy, x, weight, eps=DEFAULT_EPS, offset=False):
     u = dyf * g
     c = (u * xf).sum(-1, keepdim=True) / n
     dx = r * (u - xf * (r * r) * c)
-    dgamma = _column_sums32(dyf * (xf * r))
+    dgamma = _column_sums32(dyf * xf * r)
     return dx.to(x.dtype), dgamma
 
 
 def reference_dgamma(dy, x, eps=DEFAULT_EPS, cols=None):
     """dgamma of ``reference_backward`` restricted to some columns.
 
-    Same float32 arithmetic: r from whole rows, then dy*(x*r) summed over
-    rows for the selected columns only."""
+    Same float32 arithmetic: r from whole rows, then dy*x*r (left to right)
+    summed over rows for the selected columns only."""
     xf = _rows2d(x.detach().to("cpu")).float()
     dy2 = _rows2d(dy.detach().to("cpu"))
     r = _row_rstd32(xf, eps)
@@ -93,7 +94,7 @@ def reference_dgamma(dy, x, eps=DEFAULT_EPS, cols=None):
         idx = torch.as_tensor(cols, dtype=torch.long)
         xf = xf[:, idx]
         dy2 = dy2[:, idx]
-    return _column_sums32(dy2.float() * (xf * r))
+    return _column_sums32(dy2.float() * xf * r)
 
 
 def reference_backward_autograd(dy, x, weight, eps=DEFAULT_EPS, offset=False):

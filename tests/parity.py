@@ -50,6 +50,39 @@ def gate_full(inp, out):
     ]
 
 
+def gate_full_chunked(inp, out, chunk_rows=8192):
+    """Gate every element of a full-size run, a block of rows at a time.
+
+    y and dx are gated through gate.TensorGate, fed one row block at a time
+    (golden and reference computed for that block only, the target's block
+    copied from the device), so no tensor is held in float64 whole; rstd and
+    dgamma are gated whole (dgamma's golden and reference are column sums
+    over all rows, themselves accumulated in row blocks)."""
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    off, eps, T = inp["offset"], inp["eps"], inp["x"].dtype
+    M, n = x.shape[0], x.shape[-1]
+    gy = gate.TensorGate("y", T, (M, n))
+    gdx = gate.TensorGate("dx", T, (M, n))
+    r_g = np.empty(M)
+    r_r = torch.empty(M, dtype=torch.float32)
+    for a in range(0, M, chunk_rows):
+        b = min(M, a + chunk_rows)
+        xs, dys = x[a:b], dy[a:b]
+        y_r, r_r[a:b] = reference.reference_forward(xs, w, eps, off)
+        dx_r, _ = reference.reference_backward(dys, xs, w, eps, off)
+        y_g, r_g[a:b] = golden.golden_forward(xs, w, eps, off)
+        dx_g = golden.golden_dx(dys, xs, w, eps, off)
+        gy.add(out["y"][a:b].cpu(), y_r, y_g)
+        gdx.add(out["dx"][a:b].cpu(), dx_r, dx_g)
+    dg_g = golden.golden_dgamma(dy, x, eps)
+    dg_r = reference.reference_dgamma(dy, x, eps)
+    dg_t = out["dgamma"].cpu()
+    worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
+    cond = golden.dgamma_condition(dy, x, eps, worst)
+    return [gy.finish(), gate.gate_rstd(out["rstd"].cpu(), r_g, r_r), gdx.finish(),
+            gate.gate_tensor("dgamma", dg_t, dg_r, dg_g, torch.float32, condition=cond)]
+
+
 def sample_rows(inp, count, seed=1234):
     """Random rows plus the first/last rows and any special rows of the recipe."""
     M = inp["x"].shape[0]

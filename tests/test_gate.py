@@ -209,3 +209,30 @@ def test_gate_mean_bounds():
     bad[2] = 2.0 ** -38
     assert gate.gate_mean(bad, g, absmax).verdict == "PASS"
     assert gate.gate_mean(t.double(), g, absmax).verdict == "FAIL"  # must be float32
+
+
+@pytest.mark.parametrize("mutation", [None, "truncate", "r_squared", "unwritten"])
+def test_chunked_gate_equals_whole_gate(mutation):
+    """TensorGate fed in row chunks gives the row gate_tensor gives on the
+    whole tensor (same errors, floor, threshold, bias within float64 sum
+    order, verdict), so full-size tensors can be gated chunk by chunk."""
+    inp = workloads.make_inputs("c2", M=96, N=256)
+    x, w, dy = inp["x"], inp["w"], inp["dy"]
+    y_t, _, dx_t, _ = stand_in(x, w, dy, EPS, False, mutation)
+    y_r, _ = reference.reference_forward(x, w, EPS)
+    dx_r, _ = reference.reference_backward(dy, x, w, EPS)
+    y_g, _ = golden.golden_forward(x, w, EPS)
+    dx_g = golden.golden_dx(dy, x, w, EPS)
+    for name, t, r, g in (("y", y_t, y_r, y_g), ("dx", dx_t, dx_r, dx_g)):
+        whole = gate.gate_tensor(name, t, r, g, torch.bfloat16)
+        acc = gate.TensorGate(name, torch.bfloat16, g.shape)
+        for a in range(0, 96, 40):
+            acc.add(t[a:a + 40], r[a:a + 40], g[a:a + 40])
+        part = acc.finish()
+        assert part.verdict == whole.verdict, (name, mutation)
+        for k in ("reference_error", "target_error", "rounding_floor", "threshold",
+                  "golden_scale", "gate_valid", "note"):
+            a_, b_ = getattr(part, k), getattr(whole, k)
+            assert a_ == b_ or (a_ != a_ and b_ != b_), (k, a_, b_)
+        if whole.bias_target is not None:
+            assert abs(part.bias_target - whole.bias_target) < 1e-12

@@ -15,7 +15,8 @@ import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from backward_rmsnorm_fwd_amd import workloads
-from parity import assert_pass, gate_full, gate_sampled, log, run_target, sample_cols, sample_rows
+from parity import (assert_pass, gate_full, gate_full_chunked, gate_sampled, log, run_target,
+                    sample_cols, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +95,20 @@ def test_full_size_every_element(cuda, name):
     out = run_target(inp, cuda)
     log(f"case {name} device run done")
     assert_pass(gate_full(inp, out), f"{name} full size, every element")
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_full_size_every_element_chunked(cuda, name):
+    """fp16 262144 x 1024 (special rows included) and bf16 offset 65536 x
+    5120, default plan (the one bench.py times, the pipelined backward with
+    its explicit waits): every element of y, rstd, dx and dgamma gated, the
+    oracle evaluated one block of rows at a time and the blocks' errors
+    combined into one gate row per tensor."""
+    inp = workloads.make_inputs(name)
+    log(f"case {name} full size M={inp['M']} N={inp['N']} generated")
+    out = run_target(inp, cuda)
+    log(f"case {name} device run done")
+    assert_pass(gate_full_chunked(inp, out), f"{name} full size, every element")
 
 
 @pytest.mark.parametrize("name", ["c3", "c5"])

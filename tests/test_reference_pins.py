@@ -117,20 +117,20 @@ def _mut_no_r(dy, x, eps, cols):
 def _mut_mean(dy, x, eps, cols):
     xf, dyf = x.float(), dy.float()
     r = torch.rsqrt((xf * xf).sum(-1, keepdim=True) / xf.shape[-1] + eps)
-    return (dyf * (xf * r)).mean(0)[cols]
+    return (dyf * xf * r).mean(0)[cols]
 
 
 def _mut_cols_shifted(dy, x, eps, cols):
     xf, dyf = x.float(), dy.float()
     r = torch.rsqrt((xf * xf).sum(-1, keepdim=True) / xf.shape[-1] + eps)
     shifted = [(c + 1) % xf.shape[-1] for c in cols]
-    return (dyf * (xf * r)).sum(0)[shifted]
+    return (dyf * xf * r).sum(0)[shifted]
 
 
 def _mut_r_from_selected_cols(dy, x, eps, cols):
     xf, dyf = x.float()[:, cols], dy.float()[:, cols]
     r = torch.rsqrt((xf * xf).sum(-1, keepdim=True) / xf.shape[-1] + eps)
-    return (dyf * (xf * r)).sum(0)
+    return (dyf * xf * r).sum(0)
 
 
 def _golden_pin(impl, M=257, N=96):
