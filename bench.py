@@ -344,11 +344,12 @@ def main():
     # Events bracket only the dominant kernel (backward stage 1) on the stream
     # it is launched on; the step time comes from the host clock around K
     # steps bracketed by device synchronization.
-    # An event pair costs a few microseconds of queue time, so only every
-    # `every`-th step carries one (about ten samples per run).
-    every = max(1, args.steps // 10)
+    # An event pair costs a few microseconds of queue time, so only a few
+    # steps carry one: one pair per ten steps, between 2 and 10 pairs.
+    n_ev = max(2, min(10, args.steps // 10))
+    every = max(1, args.steps // n_ev)
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for i in range(0, args.steps, every)}
+          for i in list(range(0, args.steps, every))[:n_ev]}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
