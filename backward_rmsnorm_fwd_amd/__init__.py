@@ -25,7 +25,8 @@ __all__ = [
     "RmsnormError", "library_path", "load_library", "rmsnorm_status_string",
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_query_plan", "rmsnorm_fwd_strided",
-    "rmsnorm_bwd_strided", "row_layout", "fwd", "bwd", "EXPORTED_SYMBOLS",
+    "rmsnorm_bwd_strided", "rmsnorm_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "row_layout", "fwd",
+    "bwd", "EXPORTED_SYMBOLS",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
     "layernorm_bwd_rows", "layernorm_bwd_reduce", "ln_fwd", "ln_bwd", "LAYERNORM_MAX_N",
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
@@ -49,11 +50,12 @@ LAYERNORM_MAX_N = 16384
 RMSNORM_ADD_MAX_N = 16384
 RMSNORM_CAST_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RMSNORM_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",
     "rmsnorm_bwd_workspace_bytes", "rmsnorm_status_string", "rmsnorm_query_plan",
-    "rmsnorm_fwd_strided", "rmsnorm_bwd_strided",
+    "rmsnorm_fwd_strided", "rmsnorm_bwd_strided", "rmsnorm_bwd_noalloc",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
     "layernorm_bwd_rows", "layernorm_bwd_reduce",
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
@@ -110,6 +112,8 @@ def load_library():
     lib.rmsnorm_fwd.restype = i32
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, u32, vp, vp, vp, sz, vp]
     lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, u32, vp, vp, vp]
+    lib.rmsnorm_bwd_noalloc.restype = i32
     lib.rmsnorm_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, u32, vp, vp, sz, vp]
     lib.rmsnorm_bwd_rows.restype = i32
     lib.rmsnorm_bwd_reduce.argtypes = [vp, sz, i64, i64, i32, u32, vp, vp]
@@ -325,6 +329,17 @@ def rmsnorm_bwd(dy, x, gamma, rstd, dx, dgamma, workspace, offset=False, stream=
         _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
         _flags(offset, in_dtype), _ptr(dx), _ptr(dgamma), _ptr(workspace), ws_bytes,
         _stream(x.device, stream)))
+
+
+def rmsnorm_bwd_noalloc(dy, x, gamma, rstd, dx, dgamma, offset=False, stream=None):
+    """rmsnorm_bwd with the dgamma partial sums in the library's own device
+    buffer (RMSNORM_NOALLOC_SCRATCH_BYTES per device) instead of a workspace."""
+    m, n = _rows(x)
+    in_dtype = dgamma.dtype != torch.float32
+    _require(not in_dtype or dgamma.dtype == x.dtype, "dgamma must be float32 or x's dtype")
+    _check("rmsnorm_bwd_noalloc", load_library().rmsnorm_bwd_noalloc(
+        _ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), m, n, _dtype_code(x),
+        _flags(offset, in_dtype), _ptr(dx), _ptr(dgamma), _stream(x.device, stream)))
 
 
 # ---- allocating front ends ----------------------------------------------------

@@ -12,10 +12,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/layernorm.h"
 #include "../../include/rmsnorm.h"
@@ -745,7 +747,7 @@ int check_fwd_args(const void* x, int64_t ldx, const void* gamma, float eps, int
 int check_bwd_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                         const void* gamma, const float* rstd, int64_t M, int64_t N, int dtype,
                         uint32_t flags, const void* dx, int64_t lddx, const void* workspace,
-                        size_t workspace_bytes) {
+                        size_t workspace_bytes, bool library_scratch = false) {
   int st = check_common(M, N, dtype, flags);
   if (st != RMSNORM_OK) return st;
   if (bad_stride(lddy, N) || bad_stride(ldx, N) || bad_stride(lddx, N)) return RMSNORM_ERR_STRIDE;
@@ -756,8 +758,15 @@ int check_bwd_rows_args(const void* dy, int64_t lddy, const void* x, int64_t ldx
       misaligned(dx, es) || misaligned(rstd, 4))
     return RMSNORM_ERR_ALIGNMENT;
   const size_t need = rmsnorm_bwd_workspace_bytes(M, N, static_cast<rmsnorm_dtype_t>(dtype), flags);
-  if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
-  if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  // The library's own scratch is a separate device allocation, sized and
+  // aligned by the library: only the caller's buffers are checked here.
+  if (library_scratch) {
+    if (need > RMSNORM_NOALLOC_SCRATCH_BYTES) return RMSNORM_ERR_WORKSPACE;
+    workspace = nullptr;
+  } else {
+    if (workspace_bytes < need || (need > 0 && !workspace)) return RMSNORM_ERR_WORKSPACE;
+    if (misaligned(workspace, 16)) return RMSNORM_ERR_ALIGNMENT;
+  }
   if (const int sp = span_status({matrix(dx, M, lddx * es, N * es), vec(workspace, static_cast<int64_t>(need))},
                   {matrix(dy, M, lddy * es, N * es), matrix(x, M, ldx * es, N * es),
                    vec(gamma, N * es), vec(rstd, M * 4)}))
@@ -1367,6 +1376,45 @@ void fill_cast_plan(int64_t M, int64_t N, int pass, int align, rmsnorm_plan_t* o
 
 }  // namespace
 
+// ---- the allocation-free backward's scratch --------------------------------
+//
+// rmsnorm_bwd_noalloc keeps its dgamma partial sums in this file-scope device
+// array instead of a caller workspace.  Every device the library runs on
+// holds its own copy, reserved when this file's code object is loaded there
+// and held until the process ends.  Stage 1 writes every partial that stage 2
+// reads, so nothing in it has to start at zero.
+static __device__ __align__(256) float scratch[RMSNORM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of each device's copy is looked up once, with that device
+// current, and only that address is passed to kernels.
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMSNORM_ERR_LAUNCH;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+        return RMSNORM_ERR_LAUNCH;
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RMSNORM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rmsnorm_status_string(int status) {
@@ -1381,7 +1429,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_EPS: return "eps must be finite and positive";
     case RMSNORM_ERR_FLAGS: return "unknown flag bits";
     case RMSNORM_ERR_WORKSPACE:
-      return "workspace missing or smaller than the matching *_bwd_workspace_bytes()";
+      return "workspace missing or smaller than the matching *_bwd_workspace_bytes(), or (for "
+             "rmsnorm_bwd_noalloc) a need above RMSNORM_NOALLOC_SCRATCH_BYTES";
     case RMSNORM_ERR_ALIGNMENT: return "pointer not aligned to its element size (workspace: 16 bytes)";
     case RMSNORM_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
     case RMSNORM_ERR_LAUNCH: return "kernel launch failed";
@@ -1454,6 +1503,31 @@ int rmsnorm_bwd(const void* dy, const void* x, const void* gamma, const float* r
                 void* dgamma, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_impl(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, dgamma, workspace,
                   workspace_bytes, stream);
+}
+
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* gamma, const float* rstd,
+                        int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
+                        void* dgamma, hipStream_t stream) {
+  // Every caller argument is checked before the scratch is looked up.
+  int st = check_bwd_rows_args(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, nullptr, 0,
+                               /*library_scratch=*/true);
+  if (st != RMSNORM_OK) return st;
+  st = check_dgamma_args(dgamma, N, dtype, flags);
+  if (st != RMSNORM_OK) return st;
+  const int es = elem_bytes(dtype);
+  if (const int sp = span_status({vec(dgamma, N * dgamma_elem_bytes(dtype, flags)),
+                                  matrix(dx, M, N * es, N * es)},
+                                 {matrix(dy, M, N * es, N * es), matrix(x, M, N * es, N * es),
+                                  vec(gamma, N * es), vec(rstd, M * 4)}))
+    return sp;
+  float* part = nullptr;
+  if (rmsnorm_bwd_workspace_bytes(M, N, dtype, flags) > 0) {
+    st = scratch_on_current_device(&part);
+    if (st != RMSNORM_OK) return st;
+  }
+  st = bwd_rows_launch(dy, N, x, N, gamma, rstd, M, N, dtype, flags, dx, N, part, stream);
+  if (st != RMSNORM_OK) return st;
+  return bwd_reduce_launch(part, M, N, dtype, flags, dgamma, stream);
 }
 
 int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x, int64_t ldx,

@@ -37,7 +37,9 @@
  *  - The caller owns and allocates every buffer.  The library allocates
  *    nothing, keeps no state between calls and never synchronizes the host:
  *    kernels are enqueued on `stream` and the call returns.  Calls on
- *    different streams are independent.
+ *    different streams are independent.  The one exception is
+ *    rmsnorm_bwd_noalloc, which uses a fixed device buffer of the library's
+ *    own (see there).
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns a negative status and writes nothing.  There is no
  *    fallback path: an unsupported input is an error.
@@ -205,6 +207,34 @@ int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x,
                         uint32_t flags, void* dx, int64_t lddx, void* dgamma,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * Backward with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Arguments, results and errors are those
+ * of rmsnorm_bwd, whose kernels and plan it uses (dx and dgamma are bitwise
+ * identical to rmsnorm_bwd's), except that the dgamma partial sums go to a
+ * buffer the library holds in device memory: RMSNORM_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) on each device the library runs on, reserved when the library's
+ * code is loaded on that device and held until the process ends.  The call
+ * allocates nothing; the first call with a device current looks up that
+ * device's buffer.
+ *   - Shapes needing more than RMSNORM_NOALLOC_SCRATCH_BYTES of partial sums
+ *     (rmsnorm_bwd_workspace_bytes gives the need) are rejected with
+ *     WORKSPACE before anything is enqueued.
+ *   - All calls on one device share its buffer, which keeps the last call's
+ *     partial sums (nothing in it needs to start at zero).  Calls on one
+ *     stream are ordered and safe; calls that may overlap in time on one
+ *     device (other streams, other threads without ordering) race and give
+ *     wrong dgamma.
+ * Errors: as rmsnorm_bwd (WORKSPACE as above), and LAUNCH when the buffer's
+ * device address cannot be obtained.
+ */
+#define RMSNORM_NOALLOC_SCRATCH_BYTES (((size_t)64) << 20)
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* gamma,
+                        const float* rstd, int64_t M, int64_t N,
+                        rmsnorm_dtype_t dtype, uint32_t flags, void* dx,
+                        void* dgamma, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* rmsnorm_status_string(int status);

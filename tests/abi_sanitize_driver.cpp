@@ -125,6 +125,29 @@ void plain_rejections() {
                            at(A), 256, fat(A), nullptr),
            RMSNORM_ERR_STRIDE);
   }
+  {
+    // The allocation-free backward: the need above its fixed buffer, and
+    // caller arguments, are refused before the buffer is looked up.
+    const uint64_t big = uint64_t(8) << 26;
+    expect("bwd_noalloc beyond its buffer",
+           rmsnorm_bwd_noalloc(at(A), at(A + big), at(A + 2 * big), fat(A + 3 * big), 8,
+                               RMSNORM_MAX_N, RMSNORM_F32, 0, at(A + 4 * big), at(A + 5 * big),
+                               nullptr),
+           RMSNORM_ERR_WORKSPACE);
+    expect("bwd_noalloc null dy",
+           rmsnorm_bwd_noalloc(nullptr, at(A), at(A), fat(A), 4, 256, RMSNORM_BF16, 0, at(A),
+                               at(A), nullptr),
+           RMSNORM_ERR_NULL_POINTER);
+    expect("bwd_noalloc dx overlaps x",
+           rmsnorm_bwd_noalloc(at(A), at(A + (1u << 24)), at(A + (2u << 24)),
+                               fat(A + (3u << 24)), 4, 256, RMSNORM_BF16, 0,
+                               at(A + (1u << 24) + 64), at(A + (5u << 24)), nullptr),
+           RMSNORM_ERR_OVERLAP);
+    expect("bwd_noalloc huge M*N",
+           rmsnorm_bwd_noalloc(at(A), at(A), at(A), fat(A), RMSNORM_MAX_M, 4096, RMSNORM_BF16, 0,
+                               at(A), at(A), nullptr),
+           RMSNORM_ERR_SHAPE);
+  }
   expect("cast same dtype",
          rmsnorm_cast_fwd(at(A), 256, at(A + 4096), 1e-6f, 4, 256, RMSNORM_F32, RMSNORM_F32, 0,
                           at(A + 8192), 256, fat(A + 16384), nullptr),

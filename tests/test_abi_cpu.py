@@ -213,6 +213,29 @@ def test_overlap_found_at_large_pitches():
     assert fwd_strided_call(x=A, ldx=ld, y=A + 2 * ld, ldy=ld, M=1 << 14, N=8) == EOVL
 
 
+def test_bwd_noalloc_rejects():
+    """The allocation-free backward checks every caller argument, and the need
+    against its fixed buffer, before it looks the buffer up on a device."""
+    L = lib()
+    S = 1 << 24
+
+    def call(dy=A, x=A + S, g=A + 2 * S, r=A + 3 * S, M=4, N=256, dtype=2, flags=0,
+             dx=A + 4 * S, dg=A + 5 * S):
+        return L.rmsnorm_bwd_noalloc(dy, x, g, r, M, N, dtype, flags, dx, dg, None)
+    # 8 rows of 2^24 float32 need 64 MiB + the split plan's row sums: too big
+    assert L.rmsnorm_bwd_workspace_bytes(8, 1 << 24, 0, 0) > rn.NOALLOC_SCRATCH_BYTES
+    big = 8 << 26
+    assert call(dy=A, x=A + big, g=A + 2 * big, r=A + 3 * big, M=8, N=1 << 24, dtype=0,
+                dx=A + 4 * big, dg=A + 5 * big) == EWS
+    assert call(dtype=5) == EDTYPE and call(flags=8) == EFLAGS and call(N=0) == ESHAPE
+    assert call(dy=None) == ENULL and call(dg=None) == ENULL and call(r=None) == ENULL
+    assert call(x=A + S + 1) == EALIGN and call(dg=A + 5 * S + 2) == EALIGN
+    assert call(dx=A + S + 64) == EOVL        # dx overlaps x
+    assert call(dg=A + 2 * S + 4) == EOVL     # dgamma overlaps gamma
+    assert call(dg=A + 4 * S + 8) == EOVL     # dgamma overlaps dx
+    assert "RMSNORM_NOALLOC_SCRATCH_BYTES" in rn.rmsnorm_status_string(EWS)
+
+
 def test_shape_status_string_names_each_family_limit():
     s = rn.rmsnorm_status_string(-3)
     assert "2^24" in s and "16384" in s and "layernorm_" in s
