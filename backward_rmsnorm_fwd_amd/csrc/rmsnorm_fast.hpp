@@ -138,6 +138,51 @@ __device__ __forceinline__ float group_sum(float v, float* slots, int& parity, i
   }
 }
 
+// Order in which a workgroup takes its rows.  Either way the rows of
+// workgroup w (of P) are a fixed function of (M, P, G), so every reduction
+// order is reproducible; row group `group` of the G in a workgroup takes row
+// base + it*stride + group.
+//   kRowsBlocked: the contiguous rows [w*M/P, (w+1)*M/P)
+//   kRowsCyclic:  row groups w, w+P, w+2P, ... counted from the first (all
+//                 workgroups sweep the tensor together, front to back)
+//   kRowsReverse: the same row groups counted from the last (the sweep runs
+//                 back to front)
+// A grid that sweeps the tensor together keeps the rows in flight within one
+// window of the matrix, which the HBM serves far better than P streams at
+// once when the data is not in cache.  Running the backward's sweep in the
+// direction opposite to the forward's starts it on the rows the forward
+// touched last.
+constexpr int kRowsBlocked = 0;
+constexpr int kRowsCyclic = 1;
+constexpr int kRowsReverse = 2;
+
+template <int ORD>
+struct RowSched {
+  int64_t base, stride, limit, iters;
+  __device__ __forceinline__ RowSched(int64_t w, int64_t M, int64_t P, int G) {
+    if constexpr (ORD == kRowsBlocked) {
+      const int64_t r0 = block_row_begin(w, M, P), r1 = block_row_begin(w + 1, M, P);
+      base = r0;
+      stride = G;
+      limit = r1;
+      iters = (r1 - r0 + G - 1) / G;
+    } else {
+      const int64_t groups = (M + G - 1) / G;
+      iters = w < groups ? (groups - w + P - 1) / P : 0;
+      limit = M;
+      if constexpr (ORD == kRowsCyclic) {
+        base = w * G;
+        stride = P * G;
+      } else {
+        // Row group groups-1-w first; the partial group (if any) is the
+        // last one, so only workgroup 0's first step can reach past M.
+        base = (groups - 1 - w) * G;
+        stride = -P * G;
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Forward.  Workgroup b handles rows b*G + g, then strides by gridDim.x*G.
 // GREG keeps the weight in registers across rows (else it is re-read from
@@ -228,9 +273,9 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward stage 1.  Workgroup w owns rows [w*M/P, (w+1)*M/P); its G row
-// groups take them in turn (row = r0 + it*G + g), all groups running the same
-// number of iterations.  Per row: dot = sum(dy*g*x) over the row, then one
+// Backward stage 1.  Workgroup w takes the rows RowSched<ORD> gives it; its G
+// row groups take them in turn (row = base + it*stride + g), all groups
+// running the same number of iterations.  Per row: dot = sum(dy*g*x) over the row, then one
 // sweep computes dx = r*u - x*(r^3*dot/N) and acc_j += (dy_j*x_j)*r.  Then the
 // G accumulators are added in group order, one chunk-wide slice at a time
 // through LDS, and the workgroup writes its partial row part[w, :].
@@ -239,7 +284,8 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
 // in flight) and is read back for both sweeps.
 // GREG: the weight lives in registers; otherwise it is re-read from cache.
 // ---------------------------------------------------------------------------
-template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool XLDS, bool NT, int MINW = 1>
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool XLDS, bool NT, int ORD,
+          int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
@@ -261,9 +307,8 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
   const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
   int parity = 0;
   const int64_t w = blockIdx.x;
-  const int64_t r0 = block_row_begin(w, M, P);
-  const int64_t r1 = block_row_begin(w + 1, M, P);
-  const int64_t iters = (r1 - r0 + G - 1) / G;
+  const RowSched<ORD> rs(w, M, P, G);
+  const int64_t iters = rs.iters;
   const float n_f = static_cast<float>(N);
   char* xrow = dyn + static_cast<int64_t>(group) * row_bytes;
   const GRow gbuf(gamma);
@@ -283,8 +328,8 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_fast_kernel(
     for (int k = 0; k < VEC; ++k) acc[c][k] = 0.f;
 
   for (int64_t it = 0; it < iters; ++it) {
-    const int64_t row = r0 + it * G + group;
-    const bool active = row < r1;
+    const int64_t row = rs.base + it * rs.stride + group;
+    const bool active = row < rs.limit;
     if constexpr (GREG) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) g[c].opaque();
@@ -459,33 +504,6 @@ __device__ __forceinline__ float group_sum_lds(float v, float* slots, int& parit
   }
 }
 
-// Rows of workgroup w (of P) for the pipelined kernels, in processing order;
-// row group `group` of the G in a workgroup takes row base + it*stride + group.
-//   blocked (CYC = false): the contiguous rows [w*M/P, (w+1)*M/P)
-//   cyclic  (CYC = true):  row groups w, w+P, w+2P, ... (all workgroups sweep
-//                          the tensor together, front to back)
-// Either way the rows of a workgroup are a fixed function of (M, P), and
-// rows only grow with `it`, so a row beyond `limit` is followed by no row.
-template <bool CYC>
-struct RowSched {
-  int64_t base, stride, limit, iters;
-  __device__ __forceinline__ RowSched(int64_t w, int64_t M, int64_t P, int G) {
-    if constexpr (CYC) {
-      const int64_t groups = (M + G - 1) / G;
-      base = w * G;
-      stride = P * G;
-      limit = M;
-      iters = w < groups ? (groups - w + P - 1) / P : 0;
-    } else {
-      const int64_t r0 = block_row_begin(w, M, P), r1 = block_row_begin(w + 1, M, P);
-      base = r0;
-      stride = G;
-      limit = r1;
-      iters = (r1 - r0 + G - 1) / G;
-    }
-  }
-};
-
 // 16 bytes from LDS, complete on return.  Written as one asm statement (read
 // and wait together) so the compiler neither sees an LDS read it would guard
 // with a wait for every DMA in flight, nor can touch the destination
@@ -497,13 +515,13 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) {
   return v;
 }
 
-// Forward, pipelined.  Workgroup w owns the contiguous rows
-// [block_row_begin(w), block_row_begin(w+1)) of a P = gridDim.x split; its G
-// row groups take rows r0 + it*G + group.  The weight stays in registers for
-// the whole launch.  x is prefetched one row ahead either into LDS by DMA (XL,
-// two stage buffers of [G][N] elements, read back with lds_read16 after an
-// explicit wait) or into the second of two register sets.
-template <int DT, int CH, int WPR, int BLOCK, bool NT, bool XL, bool CYC, int MINW = 1>
+// Forward, pipelined.  Workgroup w of P = gridDim.x takes the rows
+// RowSched<ORD> gives it; its G row groups take rows base + it*stride + group.
+// The weight stays in registers for the whole launch.  x is prefetched one
+// row ahead either into LDS by DMA (XL, two stage buffers of [G][N] elements,
+// read back with lds_read16 after an explicit wait) or into the second of two
+// register sets.
+template <int DT, int CH, int WPR, int BLOCK, bool NT, bool XL, int ORD, int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
     float* __restrict__ rstd, int64_t M, int N, float eps, int offset, int64_t x_pitch,
@@ -522,7 +540,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_pipe_kernel(
   const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
   int parity = 0;
   const float n_f = static_cast<float>(N);
-  const RowSched<CYC> rs(blockIdx.x, M, gridDim.x, G);
+  const RowSched<ORD> rs(blockIdx.x, M, gridDim.x, G);
   const int64_t iters = rs.iters;
   char* const xstage = dyn + static_cast<int64_t>(group) * row_bytes;
   const int64_t stage_stride = static_cast<int64_t>(G) * row_bytes;
@@ -643,14 +661,14 @@ inline int64_t fwd_pipe_lds_bytes(int N) {
   return XL ? 2 * static_cast<int64_t>(Geo::G) * N * ElemBytes<DT>::value : 0;
 }
 
-// Backward stage 1, pipelined.  Rows split as in bwd_fast_kernel (P = gridDim.x
-// workgroups, fixed row blocks, one fp32 dgamma partial row each).  x (and,
+// Backward stage 1, pipelined.  Rows taken as in bwd_fast_kernel (P = gridDim.x
+// workgroups, RowSched<ORD>, one fp32 dgamma partial row each).  x (and,
 // with DLDS, dy) reaches LDS by DMA into one of two stage buffers
 // ([2][DLDS ? 2 : 1][G][N] elements); without DLDS dy is loaded into one of
 // two register sets.  Each wavefront reads back exactly the bytes its own DMA
 // wrote, so the staging needs no barrier; the wait for row it's data is an
 // explicit count (see `step`).
-template <int DT, int CH, int WPR, int BLOCK, bool NT, bool DLDS, bool CYC, int MINW = 1>
+template <int DT, int CH, int WPR, int BLOCK, bool NT, bool DLDS, int ORD, int MINW = 1>
 __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
@@ -671,7 +689,7 @@ __global__ __launch_bounds__(BLOCK, MINW) void bwd_pipe_kernel(
   const uint32_t row_bytes = static_cast<uint32_t>(N) * ElemBytes<DT>::value;
   int parity = 0;
   const int64_t w = blockIdx.x;
-  const RowSched<CYC> rs(w, M, P, G);
+  const RowSched<ORD> rs(w, M, P, G);
   const int64_t iters = rs.iters;
   const float n_f = static_cast<float>(N);
   // Stage buffer b: x row of this group at xstage + b*stage_stride, dy row
@@ -925,7 +943,7 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
   const uint32_t dma_off = wave * kWave * 16;
   int parity = 0;
   const int64_t w = blockIdx.x;
-  const RowSched<true> rs(w, M, P, 1);
+  const RowSched<kRowsCyclic> rs(w, M, P, 1);
   const float n_f = static_cast<float>(N);
   const URow gbuf(gamma);
 

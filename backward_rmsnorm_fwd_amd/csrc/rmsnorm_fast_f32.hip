@@ -23,7 +23,7 @@ hipError_t fast_bwd_launch<kF32>(int wpr, int ch, int block, int greg, int xlds,
                                  const FastBwdArgs& a, hipStream_t s) {
 #define RMSNORM_X(W, C, B, GR, XL)                                                          \
   if (wpr == W && ch == C && block == B && greg == GR && xlds == XL)                        \
-    return launch(bwd_fast_kernel<kF32, C, W, B, GR != 0, XL != 0, true>, a.P, B,             \
+    return launch(bwd_fast_kernel<kF32, C, W, B, GR != 0, XL != 0, true, kRowsReverse>, a.P, B,             \
                   static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
                   a.M, a.N, a.offset, a.P, a.dy_pitch, a.x_pitch, a.dx_pitch);
   RMSNORM_BWD_FAST_LIST(RMSNORM_X)
@@ -36,7 +36,7 @@ hipError_t pipe_fwd_launch<kF32>(int wpr, int ch, int block, int xl, int64_t gri
                                 const FastFwdArgs& a, hipStream_t s) {
 #define RMSNORM_X(W, C, B, XL)                                                              \
   if (wpr == W && ch == C && block == B && xl == XL)                                        \
-    return launch(fwd_pipe_kernel<kF32, C, W, B, true, XL != 0, true>, grid, B,              \
+    return launch(fwd_pipe_kernel<kF32, C, W, B, true, XL != 0, kRowsCyclic>, grid, B,              \
                   static_cast<size_t>(lds), s, a.x, a.gamma, a.y, a.rstd, a.M, a.N, a.eps,  \
                   a.offset, a.x_pitch, a.y_pitch);
   RMSNORM_FWD_PIPE_LIST(RMSNORM_X)
@@ -49,7 +49,7 @@ hipError_t pipe_bwd_launch<kF32>(int wpr, int ch, int block, int dlds, int64_t l
                                 const FastBwdArgs& a, hipStream_t s) {
 #define RMSNORM_X(W, C, B, DL)                                                              \
   if (wpr == W && ch == C && block == B && dlds == DL)                                      \
-    return launch(bwd_pipe_kernel<kF32, C, W, B, true, DL != 0, true>, a.P, B,               \
+    return launch(bwd_pipe_kernel<kF32, C, W, B, true, DL != 0, kRowsCyclic>, a.P, B,               \
                   static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.rstd, a.dx, a.part,    \
                   a.M, a.N, a.offset, a.P, a.dy_pitch, a.x_pitch, a.dx_pitch);
   RMSNORM_BWD_PIPE_LIST(RMSNORM_X)
