@@ -53,6 +53,14 @@ ROUNDING_BIAS_MAX = 0.25
 ROUNDING_BIAS_MIN_ELEMENTS = 4096
 # ------------------------------------------------------------------------------
 
+# The page "Check an AI model calculation before accelerating it" (section
+# "Three distinct numerical comparisons") declares allclose tolerances for the
+# kernel against its same-dtype reference: |target - reference| <= atol +
+# rtol*|reference| elementwise, atol 1e-5 and rtol 1e-4 in float32, atol =
+# rtol = 3e-3 in float16.  They are logged beside each gate row as
+# information only (the gate decides); the page declares none for bfloat16.
+PAGE_ALLCLOSE = {"float32": (1e-5, 1e-4), "float16": (3e-3, 3e-3)}
+
 _TORCH_DTYPES = {
     "float32": torch.float32, "fp32": torch.float32, torch.float32: torch.float32,
     "float16": torch.float16, "fp16": torch.float16, torch.float16: torch.float16,
@@ -174,6 +182,8 @@ class TensorGate:
         self.ref_err = self.tgt_err = self.floor = self.scale = 0.0
         self.bias = {"t": [0.0, 0.0, 0], "r": [0.0, 0.0, 0]}  # sum(e*s), sum|e|, count
         self.any_finite = False
+        self.allclose_bad = 0   # elements outside the page's allclose rule
+        self.allclose_n = 0
 
     @staticmethod
     def _bias_terms(a, g, acc):
@@ -211,6 +221,12 @@ class TensorGate:
         if self.want in ("bfloat16", "float16"):
             self._bias_terms(t.ravel(), golden.ravel(), self.bias["t"])
             self._bias_terms(r.ravel(), golden.ravel(), self.bias["r"])
+        if self.want in PAGE_ALLCLOSE:
+            atol, rtol = PAGE_ALLCLOSE[self.want]
+            both = np.isfinite(t) & np.isfinite(r)
+            bad = np.abs(t[both] - r[both]) > atol + rtol * np.abs(r[both])
+            self.allclose_bad += int(np.count_nonzero(bad))
+            self.allclose_n += int(np.count_nonzero(both))
 
     @staticmethod
     def _bias(acc):
@@ -220,6 +236,11 @@ class TensorGate:
 
     def finish(self):
         row = self.row
+        if self.want in PAGE_ALLCLOSE and self.failed is None and self.ref_failed is None:
+            atol, rtol = PAGE_ALLCLOSE[self.want]
+            row.extra["allclose"] = {"atol": atol, "rtol": rtol, "outside": self.allclose_bad,
+                                     "elements": self.allclose_n,
+                                     "verdict": self.allclose_bad == 0}
         if self.failed is not None:
             row.verdict = "FAIL"
             row.note = "structure: " + self.failed
@@ -289,6 +310,10 @@ def gate_rstd(target_rstd, golden_r, reference_rstd=None,
     if reference_rstd is not None and g.size:
         rr = _to_f64(reference_rstd).ravel()
         row.reference_error = float(np.max(np.abs(rr - g) / g))
+        atol, rtol = PAGE_ALLCLOSE["float32"]
+        bad = int(np.count_nonzero(np.abs(t - rr) > atol + rtol * np.abs(rr)))
+        row.extra["allclose"] = {"atol": atol, "rtol": rtol, "outside": bad,
+                                 "elements": int(g.size), "verdict": bad == 0}
     row.threshold = max_rel
     row.absolute_floor = 0.0
     row.golden_scale = float(np.max(np.abs(g))) if g.size else 0.0
@@ -333,11 +358,16 @@ def gate_mean(target_mean, golden_mean, row_absmax):
 
 
 def overall_verdict(rows):
+    """One verdict for the report (torchtitan page, report section): FAIL if
+    any row fails, else INCONCLUSIVE if any row is, else PASS WITH
+    LIMITATIONS if any row is, else PASS."""
     verdicts = [r.verdict for r in rows]
     if any(v == "FAIL" for v in verdicts):
         return "FAIL"
     if any(v == "INCONCLUSIVE" for v in verdicts):
         return "INCONCLUSIVE"
+    if any(v == "PASS WITH LIMITATIONS" for v in verdicts):
+        return "PASS WITH LIMITATIONS"
     return "PASS"
 
 
@@ -355,4 +385,12 @@ def report(rows, title=""):
             f"{r.target_error:.3e} | {r.threshold:.3e} | {r.gate_valid} | "
             f"{r.verdict}{' — ' + r.note if r.note else ''} |")
     lines.append(f"\nOverall: **{overall_verdict(rows)}**")
+    info = []
+    for r in rows:
+        a = r.extra.get("allclose") if r.extra else None
+        if a is not None:
+            info.append(f"{r.tensor} {a['verdict']} ({a['outside']} of {a['elements']} outside "
+                        f"atol {a['atol']:g}, rtol {a['rtol']:g})")
+    if info:
+        lines.append("Page allclose against the reference (information only): " + "; ".join(info))
     return "\n".join(lines)

@@ -209,3 +209,41 @@ def reference_ln_param_grads(dy, x, eps=DEFAULT_EPS, cols=None):
         idx = torch.as_tensor(cols, dtype=torch.long)
         xhat, dyf = xhat[:, idx], dyf[:, idx]
     return (dyf * xhat).sum(0), dyf.sum(0)
+
+
+# ---- inputs of the fallback analysis (oracle.fallback) for dx --------------
+
+def reference_ln_dx_reordered(dy, x, gamma, eps=DEFAULT_EPS):
+    """dx of ``reference_ln_backward`` in a second legal float32 order: every
+    row sum taken over the columns back to front, and r distributed over the
+    three terms (r*u - r*mean(u) - (r*xhat)*mean(u*xhat)).  Returns dx in x's
+    dtype."""
+    xf, dyf = _t32(x), _t32(dy)
+    g = gamma.detach().to("cpu").float().reshape(-1)
+    n = xf.shape[-1]
+
+    def rsum(t):
+        return torch.flip(t, dims=[-1]).sum(-1, keepdim=True)
+
+    mean = rsum(xf) / n
+    d = xf - mean
+    r = torch.rsqrt(rsum(d * d) / n + eps)
+    xhat = d * r
+    u = dyf * g
+    dx = r * u - r * (rsum(u) / n) - (r * xhat) * (rsum(u * xhat) / n)
+    return dx.to(x.dtype)
+
+
+def ln_dx_magnitude(dy, x, gamma, eps=DEFAULT_EPS):
+    """Per element, the magnitudes of the terms dx adds, in float64:
+    r*(|u_ij| + mean_j|u_ij| + |xhat_ij| * mean_j|u_ij*xhat_ij|) -- the
+    numerator of each element's condition number."""
+    xd = _f64(x)
+    xd = xd.reshape(-1, xd.shape[-1])
+    ud = _f64(dy).reshape(xd.shape) * _vec(gamma, xd.shape[-1], "gamma")
+    mu = xd.mean(-1, keepdims=True)
+    d = xd - mu
+    r = 1.0 / np.sqrt((d * d).mean(-1, keepdims=True) + eps)
+    xh = d * r
+    return r * (np.abs(ud) + np.abs(ud).mean(-1, keepdims=True)
+                + np.abs(xh) * np.abs(ud * xh).mean(-1, keepdims=True))

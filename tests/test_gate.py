@@ -236,3 +236,25 @@ def test_chunked_gate_equals_whole_gate(mutation):
             assert a_ == b_ or (a_ != a_ and b_ != b_), (k, a_, b_)
         if whole.bias_target is not None:
             assert abs(part.bias_target - whole.bias_target) < 1e-12
+
+
+def test_page_allclose_logged_as_information():
+    """The page's allclose rule (|t - ref| <= atol + rtol*|ref|, float32
+    1e-5/1e-4, float16 3e-3/3e-3) is reported beside the gate row and never
+    changes the verdict; bfloat16 has no declared tolerance."""
+    g = np.array([1.0, 100.0, -3.0])
+    ref = torch.tensor(g, dtype=torch.float32)
+    near = ref.clone()
+    near[0] += 1e-4                    # within 1e-5 + 1e-4*1
+    far = ref.clone()
+    far[1] += 0.02                     # beyond 1e-5 + 1e-4*100
+    a = gate.gate_tensor("t", near, ref, g, torch.float32).extra["allclose"]
+    assert a["verdict"] and a["outside"] == 0 and a["elements"] == 3
+    row = gate.gate_tensor("t", far, ref, g, torch.float32)
+    assert row.extra["allclose"]["outside"] == 1 and not row.extra["allclose"]["verdict"]
+    assert row.verdict == "FAIL"       # the gate, not allclose, decides
+    h = torch.tensor(g, dtype=torch.float16)
+    assert gate.gate_tensor("t", h, h, g, torch.float16).extra["allclose"]["atol"] == 3e-3
+    b = torch.tensor(g, dtype=torch.bfloat16)
+    assert "allclose" not in gate.gate_tensor("t", b, b, g, torch.bfloat16).extra
+    assert "Page allclose" in gate.report([row])
