@@ -180,6 +180,26 @@ def analyse(cases):
     return FallbackResult(rows, ts, rs, bias_t, bias_r, verdict, reasons)
 
 
+def legal_column_sums(terms, k=8, seed=0):
+    """``k`` legal float32 evaluations of the column sums of ``terms`` (an
+    [M, N] float32 tensor of per-row contributions): plain sequential
+    accumulations over the rows, the first back to front, the others in
+    random row orders drawn from ``seed``.  Step 1 of the analysis uses them
+    to test whether the gate can decide a column sum at all: a gate that
+    rejects one of them rejects correct float32 arithmetic, and cannot tell a
+    bug from rounding order (the gate is then invalid for that tensor)."""
+    t = terms.detach().to("cpu").float()
+    rng = np.random.default_rng(seed)
+    orders = [np.arange(t.shape[0])[::-1]] + [rng.permutation(t.shape[0]) for _ in range(k - 1)]
+    out = []
+    for order in orders:
+        acc = torch.zeros(t.shape[1], dtype=torch.float32)
+        for i in order:
+            acc = acc + t[int(i)]
+        out.append(acc)
+    return out
+
+
 def report(res, title=""):
     """Markdown table of the sweep and the verdict."""
     lines = [f"### {title}"] if title else []

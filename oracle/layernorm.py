@@ -247,3 +247,13 @@ def ln_dx_magnitude(dy, x, gamma, eps=DEFAULT_EPS):
     xh = d * r
     return r * (np.abs(ud) + np.abs(ud).mean(-1, keepdims=True)
                 + np.abs(xh) * np.abs(ud * xh).mean(-1, keepdims=True))
+
+
+def reference_ln_param_terms(dy, x, eps=DEFAULT_EPS):
+    """The float32 per-row contributions the parameter gradients sum over the
+    rows: ``(dy*xhat, dy)``, each [M, N], with the reference's xhat."""
+    xf, dyf = _t32(x), _t32(dy)
+    mean = xf.mean(-1, keepdim=True)
+    d = xf - mean
+    r = torch.rsqrt(d.square().mean(-1, keepdim=True) + eps)
+    return dyf * (d * r), dyf

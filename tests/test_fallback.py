@@ -102,3 +102,33 @@ def test_error_growing_with_T_never_passes_in_bf16():
 def test_wide_noise_is_inconclusive():
     res = fallback.analyse(_cases(torch.float32, "noise"))
     assert res.verdict == "INCONCLUSIVE"
+
+
+def test_legal_column_sums_are_float32_sums_in_other_orders():
+    g = np.random.default_rng(5)
+    terms = torch.from_numpy(g.standard_normal((64, 7)).astype(np.float32))
+    sums = fallback.legal_column_sums(terms, k=4, seed=3)
+    exact = terms.double().sum(0).numpy()
+    bound = 63 * fallback.U32 * terms.double().abs().sum(0).numpy()
+    seq = torch.zeros(7)
+    for i in range(63, -1, -1):
+        seq = seq + terms[i]
+    assert torch.equal(sums[0], seq)                      # back to front
+    for s_ in sums:
+        assert np.all(np.abs(s_.double().numpy() - exact) <= bound)
+    assert len({tuple(s_.tolist()) for s_ in sums}) > 1    # orders differ
+
+
+def test_the_gate_rejects_legal_orders_of_small_column_sums():
+    """What step 1 measures, shown on the CPU: for 64-row column sums of 2
+    columns, the gate (2x the float32 reference's error) rejects some plain
+    float32 sums taken in other row orders -- it cannot decide there."""
+    from oracle import gate
+    inp = workloads.make_layernorm_tile_case((64, 2), torch.bfloat16, 100)
+    x, w, dy, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
+    dg_g, _ = lnref.golden_ln_param_grads(dy, x, eps)
+    dg_r = lnref.reference_ln_backward(dy, x, w, eps)[1]
+    terms, _ = lnref.reference_ln_param_terms(dy, x, eps)
+    verdicts = [gate.gate_tensor("dgamma", c, dg_r, dg_g, torch.float32).verdict
+                for c in fallback.legal_column_sums(terms, k=16, seed=1)]
+    assert "FAIL" in verdicts
