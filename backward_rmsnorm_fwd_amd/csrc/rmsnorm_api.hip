@@ -83,13 +83,23 @@ int pointer_alignment(std::initializer_list<const void*> ptrs) {
 //            most rows' loads in flight: 4 wavefronts x 2 chunks at N=4096,
 //            1 x 2 at N=1024 (fp16), 4 x 3 at N=5120.
 //  backward  x arrives in LDS by DMA (no VGPRs while in flight), 1-2 chunks
-//            per thread, 1024-thread workgroups, P = 512 row blocks:
-//            4 x 2 at N=4096 (step 225.1 us vs 230.2 us for 1 wavefront x 8
-//            chunks), 2 x 1 at N=1024 fp16 (441.8 us vs 465.3 us), 8 x 2 at
+//            per thread, P = 512 workgroups: 4 x 2 at N=4096 (1024-thread
+//            workgroups: step 225.1 us vs 230.2 us for 1 wavefront x 8
+//            chunks; now 512 threads, below), 2 x 1 at N=1024 fp16 (441.8 us vs 465.3 us), 8 x 2 at
 //            N=5120 (592.8 us vs 616.6 us).  Staging dy in LDS as well was
 //            slower everywhere.  Rows needing more than 3 chunks at 16
 //            wavefronts keep only the dgamma accumulators in registers (x in
 //            LDS, weight re-read from cache).
+//  shapes at 4-8 KiB rows, measured in the same three scopes: the
+//            pipelined forward with 4 wavefronts x 2 chunks per row (4 rows
+//            per 1024-thread workgroup, 512 workgroups) and bwd_fast with
+//            512-thread workgroups (2 rows each, P = 512): 201.0 / 210.7 /
+//            230.7 us per bf16 32768 x 4096 step against 207.2 / 220.8 /
+//            245.4 us for 2 wavefronts x 4 chunks and 1024 threads (same GPU,
+//            same session).  Each half helps alone (forward: rotating and
+//            cold -5 us; backward: -2 to -4 us in all three); 256
+//            forward workgroups, 8-wavefront rows, P = 256 or 1024, and
+//            256-thread backward workgroups all measured slower.
 //  row order of bwd_fast_kernel: reverse cyclic (the grid sweeps the matrix
 //            back to front, against the forward's sweep).  bf16 32768 x 4096,
 //            three timing scopes (step over one buffer set / steps over three
@@ -143,7 +153,7 @@ Cfg plan_fast_fwd(int64_t nvec) {
 }
 
 Cfg plan_fast_bwd(int64_t nvec) {
-  Cfg c{true, 1, 1, 1024, 1, 1};
+  Cfg c{true, 1, 1, 512, 1, 1};
   if (nvec < 256) {
     c.wpr = pow2_at_least(ceil_div(nvec, 64));
   } else {
@@ -175,7 +185,8 @@ int64_t fast_bwd_lds(const Cfg& c, int64_t N, int es) {
 //  forward   rows of 4-8 KiB: x staged in LDS by DMA one row ahead, rows
 //            interleaved across 512 workgroups of 1024 threads, 2 wavefronts
 //            x 4 chunks per row: 207.8 us per bf16 32768x4096 step against
-//            238.4 us with fwd_fast 4 x 2 (the backward unchanged).  Shorter
+//            238.4 us with fwd_fast 4 x 2 (the backward unchanged); since
+//            4 wavefronts x 2 chunks (see the full-width notes above).  Shorter
 //            and longer rows (fp16 N=1024, bf16 N=5120) measured slower
 //            pipelined than fwd_fast and keep it.
 //  backward  rows up to 4 KiB: one chunk per thread, dy prefetched into
@@ -206,9 +217,9 @@ constexpr int64_t kPipeFwdWorkgroups = 512;
 constexpr int64_t kPipeBwdWorkgroups = 256;
 
 PipeCfg plan_pipe_fwd(int64_t nvec) {
-  PipeCfg c{false, 2, 1, 1024, 1};
+  PipeCfg c{false, 4, 1, 1024, 1};
   if (nvec <= 256 || nvec > 512) return c;
-  c.ch = static_cast<int>(ceil_div(nvec, 128));
+  c.ch = static_cast<int>(ceil_div(nvec, 64 * c.wpr));
   c.ok = listed_pipe_fwd(c);
   return c;
 }

@@ -27,9 +27,9 @@
   X(16, 9, 1024, 0) X(16, 10, 1024, 0) X(16, 11, 1024, 0) X(16, 12, 1024, 0)      \
   X(16, 13, 1024, 0) X(16, 14, 1024, 0) X(16, 15, 1024, 0) X(16, 16, 1024, 0)
 
-#define RMSNORM_BWD_FAST_LIST(X) X(4, 2, 1024, 1, 1)
+#define RMSNORM_BWD_FAST_LIST(X) X(4, 2, 512, 1, 1)
 
-#define RMSNORM_FWD_PIPE_LIST(X) X(2, 3, 1024, 1) X(2, 4, 1024, 1)
+#define RMSNORM_FWD_PIPE_LIST(X) X(4, 2, 1024, 1)
 
 #define RMSNORM_BWD_PIPE_LIST(X) \
   X(1, 1, 1024, 0) X(2, 1, 1024, 0) X(4, 1, 1024, 0) X(16, 1, 1024, 1) X(10, 1, 640, 1)

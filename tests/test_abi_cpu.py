@@ -264,11 +264,12 @@ def test_plans_for_the_workloads():
     """The full-width kernels serve the five workloads (aligned pointers)."""
     c2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_FWD)
     assert c2["kernel_name"] == "fwd_pipe" and c2["vec"] == 8 and c2["x_in_lds"] == 1
-    assert (c2["threads_per_row"], c2["chunks"], c2["block_threads"]) == (128, 4, 1024)
-    assert c2["grid"] == 512 and c2["lds_bytes"] == 2 * 8 * 4096 * 2
+    assert (c2["threads_per_row"], c2["chunks"], c2["block_threads"]) == (256, 2, 1024)
+    assert c2["grid"] == 512 and c2["lds_bytes"] == 2 * 4 * 4096 * 2
     b2 = rn.rmsnorm_query_plan(32768, 4096, 2, which=rn.PASS_BWD_ROWS)
     assert b2["kernel_name"] == "bwd_rows" and b2["x_in_lds"] == 1
     assert (b2["threads_per_row"], b2["chunks"], b2["partials"]) == (256, 2, 512)
+    assert b2["block_threads"] == 512 and b2["lds_bytes"] == 2 * 4096 * 2
     b3 = rn.rmsnorm_query_plan(262144, 1024, 1, which=rn.PASS_BWD_ROWS)
     assert b3["kernel_name"] == "bwd_pipe" and b3["dy_in_lds"] == 0
     assert (b3["threads_per_row"], b3["chunks"], b3["partials"]) == (128, 1, 256)
