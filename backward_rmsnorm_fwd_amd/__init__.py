@@ -29,6 +29,7 @@ __all__ = [
     "bwd", "EXPORTED_SYMBOLS",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_bytes", "layernorm_query_plan",
     "layernorm_bwd_rows", "layernorm_bwd_reduce", "ln_fwd", "ln_bwd", "LAYERNORM_MAX_N",
+    "LAYERNORM_RESIDENT_MAX_N",
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
     "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce", "add_fwd",
     "add_bwd", "RMSNORM_ADD_MAX_N",
@@ -45,8 +46,10 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 5: "bwd_reduce", 6: "fwd_rows", 7: "bwd_rows", 8: "bwd_reduce16",
                 9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
                 13: "bwd_split", 14: "bwd_reduce_wide", 15: "ln_fwd",
-                16: "ln_bwd", 17: "add_fwd", 18: "add_bwd", 19: "cast_fwd", 20: "cast_bwd"}
-LAYERNORM_MAX_N = 16384
+                16: "ln_bwd", 17: "add_fwd", 18: "add_bwd", 19: "cast_fwd", 20: "cast_bwd",
+                21: "ln_fwd_split", 22: "ln_bwd_split"}
+LAYERNORM_MAX_N = 1 << 24
+LAYERNORM_RESIDENT_MAX_N = 16384
 RMSNORM_ADD_MAX_N = 16384
 RMSNORM_CAST_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "rmsnorm_api.hip", "rmsnorm_fast_f32.hip", "rmsnorm_fast_f16.hip",
-    "rmsnorm_fast_bf16.hip", "rmsnorm_split.hip", "layernorm.hip", "fused_add.hip",
-    "fused_cast.hip")]
+    "rmsnorm_fast_bf16.hip", "rmsnorm_split.hip", "layernorm.hip", "layernorm_split.hip",
+    "fused_add.hip", "fused_cast.hip")]
 LIB = os.path.join(HERE, "librmsnorm.so")
 ARCH = "gfx950"
 

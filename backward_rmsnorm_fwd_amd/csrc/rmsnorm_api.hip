@@ -986,8 +986,28 @@ LnPlan ln_plan(int64_t M, int64_t N, int es, bool backward, int align, int matri
   return p;
 }
 
+// LayerNorm rows longer than the row-resident kernels hold take the
+// split-row plan (layernorm_split.hip) on RMSNorm's segments and row blocks:
+// split_partials gives P, and the backward's workspace adds the per-(row,
+// segment) sums and the per-row coefficients after the two [P, N] blocks.
+bool ln_split_rows(int64_t N) { return N > LAYERNORM_RESIDENT_MAX_N; }
+
 int64_t ln_partials(int64_t M, int64_t N, int es) {
-  return M > 0 ? ln_plan(M, N, es, true, 16).grid : 0;
+  if (M <= 0) return 0;
+  if (ln_split_rows(N)) return split_partials(M, N, es, true);
+  return ln_plan(M, N, es, true, 16).grid;
+}
+
+struct LnSplitWorkspace {
+  int64_t sums_offset, coef_offset, total_floats;  // in floats
+};
+
+LnSplitWorkspace ln_split_workspace(int64_t M, int64_t N, int es) {
+  LnSplitWorkspace w;
+  w.sums_offset = ceil_div(2 * split_partials(M, N, es, true) * N, 4) * 4;
+  w.coef_offset = w.sums_offset + ceil_div(3 * M * split_nseg(N, es), 4) * 4;
+  w.total_floats = w.coef_offset + ceil_div(3 * M, 4) * 4;
+  return w;
 }
 
 int check_ln_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
@@ -995,6 +1015,7 @@ int check_ln_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
     return RMSNORM_ERR_DTYPE;
   if (flags & ~RMSNORM_FLAG_DGAMMA_IN_DTYPE) return RMSNORM_ERR_FLAGS;
   if (N < 1 || N > LAYERNORM_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  if (M > RMSNORM_MAX_ELEMENTS / N) return RMSNORM_ERR_SHAPE;
   return RMSNORM_OK;
 }
 
@@ -1015,15 +1036,23 @@ int ln_fwd_impl(const void* x, int64_t ldx, const void* gamma, const void* beta,
                   {matrix(x, M, ldx * es, N * es), vec(gamma, N * es),
                    vec(beta, beta ? N * es : 0)}))
     return sp;
-  const LnPlan p = ln_plan(M, N, es, false,
-                           layout_alignment({x, gamma, beta, y}, {ldx * es, ldy * es}));
+  const int align = layout_alignment({x, gamma, beta, y}, {ldx * es, ldy * es});
   const LnFwdArgs a{x, gamma, beta, y, mean, rstd, M, static_cast<int>(N), eps, ldx * es,
                     ldy * es};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
+                       split_partials(M, N, es, false)};
+    return status_of(ln_split_fwd_launch(dtype, sp, a, stream));
+  }
+  const LnPlan p = ln_plan(M, N, es, false, align);
   return status_of(ln_fwd_launch(dtype, p, a, stream));
 }
 
 size_t ln_workspace_bytes(int64_t M, int64_t N, int dtype) {
-  return static_cast<size_t>(2 * ln_partials(M, N, elem_bytes(dtype)) * N * 4);
+  if (M <= 0) return 0;
+  const int es = elem_bytes(dtype);
+  if (ln_split_rows(N)) return static_cast<size_t>(ln_split_workspace(M, N, es).total_floats * 4);
+  return static_cast<size_t>(2 * ln_partials(M, N, es) * N * 4);
 }
 
 // Stage-1 argument checks (dy, x, gamma, mean, rstd, dx, workspace).
@@ -1056,10 +1085,18 @@ int ln_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, con
                    hipStream_t stream) {
   if (M == 0) return RMSNORM_OK;
   const int es = elem_bytes(dtype);
-  const LnPlan p = ln_plan(M, N, es, true,
-                           layout_alignment({dy, x, gamma, dx}, {lddy * es, ldx * es, lddx * es}));
-  const LnBwdArgs a{dy, x, gamma, mean, rstd, dx, static_cast<float*>(workspace), M,
-                    static_cast<int>(N), lddy * es, ldx * es, lddx * es};
+  const int align = layout_alignment({dy, x, gamma, dx}, {lddy * es, ldx * es, lddx * es});
+  float* part = static_cast<float*>(workspace);
+  const LnBwdArgs a{dy, x, gamma, mean, rstd, dx, part, M, static_cast<int>(N), lddy * es,
+                    ldx * es, lddx * es};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
+                       split_partials(M, N, es, true)};
+    const LnSplitWorkspace w = ln_split_workspace(M, N, es);
+    return status_of(ln_split_bwd_launch(dtype, sp, a, part + w.sums_offset,
+                                         part + w.coef_offset, stream));
+  }
+  const LnPlan p = ln_plan(M, N, es, true, align);
   return status_of(ln_bwd_launch(dtype, p, a, stream));
 }
 
@@ -1120,6 +1157,21 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
     return;
   }
   const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+  if (ln_split_rows(N)) {
+    const int64_t nseg = split_nseg(N, es);
+    const int vec = pick_vec(N, es, align);
+    const int64_t P = split_partials(M, N, es, bwd);
+    out->kernel = bwd ? LAYERNORM_KERNEL_BWD_SPLIT : LAYERNORM_KERNEL_FWD_SPLIT;
+    out->vec = vec;
+    out->segments = static_cast<int32_t>(nseg);
+    out->threads_per_row = static_cast<int32_t>(256 * nseg);
+    out->chunks = split_chunks(vec, es);
+    out->block_threads = 256;
+    out->weight_in_regs = 1;
+    out->partials = bwd ? P : 0;
+    out->grid = P * nseg;
+    return;
+  }
   const LnPlan p = ln_plan(M, N, es, bwd, align, matrices);
   out->kernel = bwd ? LAYERNORM_KERNEL_BWD : LAYERNORM_KERNEL_FWD;
   out->vec = p.vec;

@@ -140,6 +140,16 @@ struct LnBwdArgs {
 
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
 
+// LayerNorm split-row plan (layernorm_split.hip, rows over 16384 elements),
+// on the RMSNorm split geometry.  Forward: stats, finish, apply and head
+// kernels (y rows hold the segment statistics, then the mean's remainder,
+// between them).  Backward stage 1: stats (sums[M, nseg, 3]), finish
+// (coef[M, 3]) and apply (dx and part[2, P, N]).
+hipError_t ln_split_fwd_launch(int dtype, const SplitPlan& sp, const LnFwdArgs& a,
+                               hipStream_t s);
+hipError_t ln_split_bwd_launch(int dtype, const SplitPlan& sp, const LnBwdArgs& a, float* sums,
+                               float* coef, hipStream_t s);
+
 // RMSNorm with the residual add fused before it (fused_add.hip), on the
 // row-resident plan of LayerNorm.
 struct AddFwdArgs {

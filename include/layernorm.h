@@ -17,18 +17,22 @@
  *             dx_ij   = r_i * (u_ij - mean_j(u_ij) - xhat_ij * mean_j(u_ij * xhat_ij))
  *             dgamma_j = sum_i dy_ij * xhat_ij,   dbeta_j = sum_i dy_ij
  *
- * Arithmetic: inputs widened to float32 on load; the variance is the mean of
- * the squared deviations from the row mean (computed from the row held in
- * registers); the column sums add per-workgroup float32 partials in float64
- * in a fixed order and round once.  Outputs of type T round to nearest even.
+ * Arithmetic: inputs widened to float32 on load; the row sum is taken in
+ * float64; the variance is the mean of the squared deviations from the row
+ * mean (from the row held in registers, or, for split rows, from per-segment
+ * float64 statistics merged in segment order); the column sums add
+ * per-workgroup float32 partials in float64 in a fixed order and round once.
+ * Outputs of type T round to nearest even.
  *
  * Conventions are those of rmsnorm.h (device pointers on the current device,
  * caller-owned buffers, work enqueued on `stream`, host-side validation
  * before anything is enqueued, no fallback, no overlapping outputs, bitwise
  * reproducible for equal inputs, shape and alignment), with these
  * differences:
- *  - 1 <= N <= LAYERNORM_MAX_N: a row is held in registers across up to 16
- *    wavefronts of one workgroup;
+ *  - 1 <= N <= LAYERNORM_MAX_N (2^24) and M * N <= RMSNORM_MAX_ELEMENTS.
+ *    Rows of up to LAYERNORM_RESIDENT_MAX_N elements are held in registers
+ *    across up to 16 wavefronts of one workgroup; longer rows take the
+ *    split-row plan (LAYERNORM_KERNEL_FWD_SPLIT / BWD_SPLIT);
  *  - flags: only RMSNORM_FLAG_DGAMMA_IN_DTYPE (it applies to dgamma and
  *    dbeta); RMSNORM_FLAG_OFFSET is RMSNORM_ERR_FLAGS;
  *  - beta may be NULL in the forward (no bias), dbeta may be NULL in the
@@ -44,11 +48,23 @@
 extern "C" {
 #endif
 
-#define LAYERNORM_MAX_N 16384
+#define LAYERNORM_MAX_N (((int64_t)1) << 24)
+#define LAYERNORM_RESIDENT_MAX_N 16384
 
 /* Kernels (rmsnorm_plan_t.kernel). */
 #define LAYERNORM_KERNEL_FWD 15 /* forward, rows resident in registers */
 #define LAYERNORM_KERNEL_BWD 16 /* backward stage 1, same geometry */
+/* Split-row plan for N > LAYERNORM_RESIDENT_MAX_N, on the segments of the
+ * RMSNorm split plan (16 KiB, one 256-thread workgroup per (row block,
+ * segment)).  Forward: a stats kernel writes each segment's float64 sum and
+ * sum of squared deviations into the first bytes of the row of y, a finish
+ * kernel merges them per row (segment order) into mean and rstd and leaves
+ * the mean's float32 rounding remainder in the row's first 4 bytes, an apply
+ * kernel writes y except those bytes, and a head kernel writes them.
+ * Backward stage 1: stats, finish and apply kernels with the per-row sums in
+ * the workspace. */
+#define LAYERNORM_KERNEL_FWD_SPLIT 21 /* forward, four kernels */
+#define LAYERNORM_KERNEL_BWD_SPLIT 22 /* backward stage 1, three kernels */
 
 /*
  * Forward.
@@ -60,7 +76,8 @@ extern "C" {
  *   mean   [M] float32, written (mu_i)
  *   rstd   [M] float32, written (r_i)
  * Errors: NULL_POINTER (x, gamma, y, mean or rstd NULL with M > 0), DTYPE,
- * SHAPE (N outside [1, LAYERNORM_MAX_N], M outside [0, RMSNORM_MAX_M]), EPS,
+ * SHAPE (N outside [1, LAYERNORM_MAX_N], M outside [0, RMSNORM_MAX_M],
+ * M * N above RMSNORM_MAX_ELEMENTS), EPS,
  * FLAGS, STRIDE, ALIGNMENT (a pointer not aligned to its element size),
  * OVERLAP (an output overlaps an input or another output), LAUNCH.
  */
@@ -71,8 +88,10 @@ int layernorm_fwd(const void* x, int64_t ldx, const void* gamma, const void* bet
 
 /*
  * Bytes of device workspace layernorm_bwd needs: two float32 partial blocks
- * [P, N] (dgamma, then dbeta), P a fixed function of (M, N, dtype).
- * Returns 0 for M = 0 and for invalid arguments.
+ * [P, N] (dgamma, then dbeta), P a fixed function of (M, N, dtype); split
+ * rows add three float32 sums per (row, segment) and three coefficients per
+ * row, each part starting on a 16-byte boundary.  Returns 0 for M = 0 and
+ * for invalid arguments.
  */
 size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                      uint32_t flags);

@@ -117,8 +117,12 @@ void plain_rejections() {
            rmsnorm_bwd_reduce(at(A), 4, 1 << 20, 4096, dt, 0, at(A + (1u << 26)), nullptr),
            RMSNORM_ERR_WORKSPACE);
     expect("layernorm N too large",
-           layernorm_fwd(at(A), 32768, at(A), at(A), 1e-5f, 4, 32768, dt, 0, at(A), 32768,
-                         fat(A), fat(A), nullptr),
+           layernorm_fwd(at(A), LAYERNORM_MAX_N + 1, at(A), at(A), 1e-5f, 4, LAYERNORM_MAX_N + 1,
+                         dt, 0, at(A), LAYERNORM_MAX_N + 1, fat(A), fat(A), nullptr),
+           RMSNORM_ERR_SHAPE);
+    expect("layernorm M*N too large",
+           layernorm_fwd(at(A), 65537, at(A), at(A), 1e-5f, RMSNORM_MAX_M, 65537, dt, 0, at(A),
+                         65537, fat(A), fat(A), nullptr),
            RMSNORM_ERR_SHAPE);
     expect("add stride below N",
            rmsnorm_add_fwd(at(A), 100, at(A), 256, at(A), 1e-6f, 4, 256, dt, 0, at(A), 256,
@@ -175,14 +179,13 @@ void queries() {
           for (int pass = 0; pass < 3; ++pass)
             for (int align : {2, 4, 8, 16}) (void)rmsnorm_query_plan(M, N, dt, flags, pass, align, &plan);
         }
-        if (N <= LAYERNORM_MAX_N) {
-          (void)layernorm_bwd_workspace_bytes(M, N, dt, 0);
+        (void)layernorm_bwd_workspace_bytes(M, N, dt, 0);
+        for (int pass = 0; pass < 3; ++pass)
+          for (int align : {2, 4, 8, 16}) (void)layernorm_query_plan(M, N, dt, 0, pass, align, &plan);
+        if (N <= RMSNORM_ADD_MAX_N) {
           (void)rmsnorm_add_bwd_workspace_bytes(M, N, dt, 0);
           for (int pass = 0; pass < 3; ++pass)
-            for (int align : {2, 4, 8, 16}) {
-              (void)layernorm_query_plan(M, N, dt, 0, pass, align, &plan);
-              (void)rmsnorm_add_query_plan(M, N, dt, 0, pass, align, &plan);
-            }
+            for (int align : {2, 4, 8, 16}) (void)rmsnorm_add_query_plan(M, N, dt, 0, pass, align, &plan);
         }
       }
     }

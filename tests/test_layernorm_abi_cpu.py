@@ -29,7 +29,8 @@ def fwd_call(x=A, ldx=None, g=A + S, b=A + 2 * S, eps=1e-5, M=4, N=256, dtype=2,
 
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": 3}, EDTYPE), ({"flags": 1}, EFLAGS), ({"flags": 4}, EFLAGS),
-    ({"N": 0}, ESHAPE), ({"N": 16385}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"N": 0}, ESHAPE), ({"N": (1 << 24) + 1}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"M": 1 << 40, "N": 65537}, ESHAPE),                 # M * N above 2^46
     ({"eps": 0.0}, EEPS), ({"eps": float("nan")}, EEPS),
     ({"ldx": 255}, ESTRIDE), ({"ldy": 100}, ESTRIDE),
     ({"x": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL),
@@ -66,7 +67,7 @@ def bwd_call(dy=A, x=A + S, g=A + 2 * S, mean=A + 3 * S, rstd=A + 4 * S, M=4, N=
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": 5}, EDTYPE), ({"flags": 1}, EFLAGS), ({"N": 20000}, ESHAPE),
+    ({"dtype": 5}, EDTYPE), ({"flags": 1}, EFLAGS), ({"N": (1 << 24) + 1}, ESHAPE),
     ({"lddx": 3}, ESTRIDE),
     ({"dy": None}, ENULL), ({"x": None}, ENULL), ({"g": None}, ENULL), ({"mean": None}, ENULL),
     ({"rstd": None}, ENULL), ({"dx": None}, ENULL), ({"dg": None}, ENULL),
@@ -132,10 +133,11 @@ def test_query_plan_rejects():
     p = rn.Plan()
     assert L.layernorm_query_plan(4, 256, 2, 0, 7, 16, ctypes.byref(p)) == EARG
     assert L.layernorm_query_plan(4, 256, 2, 1, 0, 16, ctypes.byref(p)) == EFLAGS
-    assert L.layernorm_query_plan(4, 16385, 2, 0, 0, 16, ctypes.byref(p)) == ESHAPE
+    assert L.layernorm_query_plan(4, (1 << 24) + 1, 2, 0, 0, 16, ctypes.byref(p)) == ESHAPE
     assert L.layernorm_query_plan(4, 256, 2, 0, 0, 16, None) == ENULL
     assert rn.layernorm_bwd_workspace_bytes(0, 256, 2) == 0
-    assert rn.layernorm_bwd_workspace_bytes(4, 16385, 2) == 0
+    assert rn.layernorm_bwd_workspace_bytes(4, (1 << 24) + 1, 2) == 0
+    assert rn.layernorm_bwd_workspace_bytes(0, 1 << 20, 2) == 0
 
 
 @pytest.mark.parametrize("dt,n,tpr,ch", [(2, 5120, 320, 2), (1, 5120, 320, 2), (0, 5120, 320, 4),
@@ -151,3 +153,60 @@ def test_backward_exact_fit(dt, n, tpr, ch):
     assert (a["threads_per_row"], a["chunks"]) == (tpr, ch)
     f = rn.layernorm_query_plan(65536, 5120, 2, which=rn.PASS_FWD)
     assert (f["threads_per_row"], f["chunks"], f["block_threads"]) == (256, 3, 256)
+
+
+@pytest.mark.parametrize("M,N,dt", [(33, 16385, 2), (5, 16386, 1), (7, 16388, 0),
+                                    (2, 1 << 24, 2), (261, 98304, 2), (100000, 20000, 1),
+                                    (1, 1 << 24, 0), (4096, 65537, 0), (8, 32768, 2)])
+def test_split_plan(M, N, dt):
+    """Rows longer than the row-resident limit: the RMSNorm split geometry
+    (16 KiB segments, one 256-thread workgroup per (row block, segment), the
+    same P); the workspace holds the two [P, N] column blocks, three sums per
+    (row, segment) and three coefficients per row, each from a 16-byte
+    boundary."""
+    es = 4 if dt == 0 else 2
+    nseg = _ceil(N * es, 16384)
+    f = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_FWD)
+    b = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
+    assert f["kernel_name"] == "ln_fwd_split" and b["kernel_name"] == "ln_bwd_split"
+    rf = rn.rmsnorm_query_plan(M, max(N, 65537), dt, which=rn.PASS_FWD)
+    for p in (f, b):
+        assert p["segments"] == nseg and p["block_threads"] == 256
+        assert p["threads_per_row"] == 256 * nseg
+        assert p["grid"] % nseg == 0 and p["grid"] < 1 << 24
+        assert p["chunks"] * p["vec"] * es == 64
+        assert 1 <= p["grid"] // nseg <= M
+    P = b["partials"]
+    assert b["grid"] == P * nseg
+    assert P == max(1, min(M, max(_ceil(M, 16), _ceil(1024, nseg)), ((1 << 24) - 1) // nseg))
+    assert f["partials"] == 0
+    assert f["grid"] // nseg == max(1, min(M, _ceil(2048, nseg), ((1 << 24) - 1) // nseg))
+    if N > 65536:
+        assert (f["grid"], f["segments"]) == (rf["grid"], rf["segments"])
+    r4 = lambda v: _ceil(v, 4) * 4  # noqa: E731
+    assert rn.layernorm_bwd_workspace_bytes(M, N, dt) == 4 * (r4(2 * P * N) + r4(3 * M * nseg)
+                                                             + r4(3 * M))
+    red = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_BWD_REDUCE)
+    assert red["partials"] == P
+
+
+def test_split_plan_boundary_and_row_room():
+    """16384 elements stay row-resident and 16385 split, in every dtype; a
+    row of y has room for the forward's 16 bytes per segment plus nothing
+    more (the mean's remainder reuses the first segment's slot)."""
+    for dt in (0, 1, 2):
+        es = 4 if dt == 0 else 2
+        assert rn.layernorm_query_plan(3, 16384, dt)["kernel_name"] == "ln_fwd"
+        assert rn.layernorm_query_plan(3, 16384, dt, which=rn.PASS_BWD_ROWS)["kernel_name"] \
+            == "ln_bwd"
+        for n in [16385, 16387, 16400, 24576, 65535, 65537, 131073, 999999, (1 << 24) - 1,
+                  1 << 24]:
+            for align in (16, 8, 4, 2):
+                if es == 4 and align < 4:
+                    continue
+                p = rn.layernorm_query_plan(3, n, dt, which=rn.PASS_FWD, align_bytes=align)
+                seg = 256 * p["chunks"] * p["vec"]
+                assert p["kernel_name"] == "ln_fwd_split"
+                assert seg * es == 16384 and n % p["vec"] == 0
+                assert p["segments"] * seg >= n > (p["segments"] - 1) * seg
+                assert 16 * p["segments"] <= n * es

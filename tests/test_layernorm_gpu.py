@@ -1,8 +1,9 @@
 """LayerNorm on the GPU through the C ABI (include/layernorm.h), gated
 against the LayerNorm oracle (oracle.layernorm): every element of y, mean,
 rstd, dx, dgamma and dbeta at reduced sizes of each recipe, tile-boundary
-and degenerate rows, misaligned and strided layouts, and the c2, c3 and c5
-shapes at full size on sampled rows and columns."""
+and degenerate rows, misaligned and strided layouts, rows longer than the
+row-resident limit (the split-row plan), and the c2, c3, c4 and c5 shapes at
+full size on sampled rows and columns."""
 import numpy as np
 import pytest
 import torch
@@ -145,18 +146,63 @@ def test_no_bias(cuda):
     assert_pass(gate_ln_full(inp, out, bias=False), "ln without bias")
 
 
-@pytest.mark.parametrize("name,M,N", [("c2", None, None), ("c3", None, None),
-                                      ("c5", None, None)])
-def test_full_size_sampled(cuda, name, M, N):
+@pytest.mark.parametrize("name,M,N,nrows", [("c2", None, None, 2048), ("c3", None, None, 2048),
+                                            ("c4", None, None, 256), ("c5", None, None, 2048)])
+def test_full_size_sampled(cuda, name, M, N, nrows):
     inp = workloads.make_layernorm_inputs(name, M=M, N=N)
     log(f"case ln {name} full size M={inp['M']} N={inp['N']} generated")
     out = run_ln_target(inp, cuda)
     log(f"case ln {name} device run done")
-    rows = sample_rows(inp, 2048)
+    rows = sample_rows(inp, nrows)
     cols = sample_cols(inp["N"], 64)
     assert_pass(gate_ln_sampled(inp, out, rows, cols), f"ln {name} full size, sampled")
     for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
         assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
+# Rows longer than the row-resident limit: 16 KiB segments (4096 float32 or
+# 8192 16-bit elements), a last segment of one access or a few elements,
+# odd N (2-byte accesses), row blocks of one to several rows, and the leading
+# elements of y that hold the mean's remainder during the forward.
+SPLIT = [((5, 16385), torch.bfloat16), ((4, 16386), torch.float16),
+         ((3, 16388), torch.float32), ((7, 24577), torch.float32),
+         ((9, 32768), torch.bfloat16), ((6, 65537), torch.float16),
+         ((3, 131072), torch.bfloat16), ((700, 16400), torch.bfloat16),
+         ((2, 3, 20000), torch.float32)]
+
+
+@pytest.mark.parametrize("shape,dtype", SPLIT)
+def test_split_rows(cuda, shape, dtype):
+    inp = workloads.make_layernorm_tile_case(shape, dtype, 57 + shape[-1] % 89)
+    log(f"case ln split {shape} {dtype}")
+    out = run_ln_target(inp, cuda)
+    assert_pass(gate_ln_full(inp, out), f"ln split {shape} {dtype}")
+
+
+@pytest.mark.parametrize("scale,shift,dtype", [(1e-3, 50.0, torch.float32),
+                                               (1e-2, 8.0, torch.float16),
+                                               (0.0, 3.0, torch.bfloat16)])
+def test_split_degenerate_rows(cuda, scale, shift, dtype):
+    """Split rows with a spread tiny against their mean, and constant rows
+    (zero variance: y = beta exactly)."""
+    inp = workloads.make_layernorm_tile_case((12, 40000), dtype, 43, scale=scale,
+                                             shift_std=shift)
+    log(f"case ln split degenerate scale={scale} shift={shift} {dtype}")
+    out = run_ln_target(inp, cuda)
+    assert_pass(gate_ln_full(inp, out), f"ln split degenerate {scale} {shift} {dtype}")
+    if scale == 0.0:
+        assert torch.equal(out["y"].cpu(), inp["b"].expand(12, 40000))
+
+
+def test_split_no_bias_and_reproducible(cuda):
+    inp = workloads.make_layernorm_inputs("c4", M=40, N=65536)
+    log("case ln split c4 recipe 40 x 65536, no bias, twice")
+    out = run_ln_target(inp, cuda, bias=False)
+    assert out["dbeta"] is None
+    assert_pass(gate_ln_full(inp, out, bias=False), "ln split without bias")
+    again = run_ln_target(inp, cuda, bias=False)
+    for k in ("y", "mean", "rstd", "dx", "dgamma"):
+        assert torch.equal(out[k], again[k]), k
 
 
 def test_reproducible_and_dgamma_in_dtype(cuda):
@@ -176,10 +222,11 @@ def test_reproducible_and_dgamma_in_dtype(cuda):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_misaligned_and_strided(cuda, dtype):
+@pytest.mark.parametrize("M,N", [(33, 4096), (9, 20000)])
+def test_misaligned_and_strided(cuda, dtype, M, N):
     """Buffers one element past an aligned address, and x/dy as column
-    slices of wider buffers (y/dx dense): same gate."""
-    M, N = 33, 4096
+    slices of wider buffers (y/dx dense): same gate, row-resident and split
+    rows."""
     inp = workloads.make_layernorm_inputs("c2", M=M, N=N, dtype=dtype)
 
     def shifted(t):
