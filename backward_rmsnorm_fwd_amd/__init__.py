@@ -32,10 +32,10 @@ __all__ = [
     "LAYERNORM_RESIDENT_MAX_N",
     "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_workspace_bytes",
     "rmsnorm_add_query_plan", "rmsnorm_add_bwd_rows", "rmsnorm_add_bwd_reduce", "add_fwd",
-    "add_bwd", "RMSNORM_ADD_MAX_N",
+    "add_bwd", "RMSNORM_ADD_MAX_N", "RMSNORM_ADD_RESIDENT_MAX_N",
     "rmsnorm_cast_fwd", "rmsnorm_cast_bwd", "rmsnorm_cast_bwd_workspace_bytes",
     "rmsnorm_cast_query_plan", "rmsnorm_cast_bwd_rows", "rmsnorm_cast_bwd_reduce", "cast_fwd",
-    "cast_bwd", "RMSNORM_CAST_MAX_N",
+    "cast_bwd", "RMSNORM_CAST_MAX_N", "RMSNORM_CAST_RESIDENT_MAX_N",
 ]
 
 RMSNORM_F32, RMSNORM_F16, RMSNORM_BF16 = 0, 1, 2
@@ -47,11 +47,14 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 9: "fwd_pipe", 10: "bwd_pipe", 11: "bwd_long", 12: "fwd_split",
                 13: "bwd_split", 14: "bwd_reduce_wide", 15: "ln_fwd",
                 16: "ln_bwd", 17: "add_fwd", 18: "add_bwd", 19: "cast_fwd", 20: "cast_bwd",
-                21: "ln_fwd_split", 22: "ln_bwd_split"}
+                21: "ln_fwd_split", 22: "ln_bwd_split", 23: "add_fwd_split",
+                24: "add_bwd_split", 25: "cast_fwd_split", 26: "cast_bwd_split"}
 LAYERNORM_MAX_N = 1 << 24
 LAYERNORM_RESIDENT_MAX_N = 16384
-RMSNORM_ADD_MAX_N = 16384
-RMSNORM_CAST_MAX_N = 16384
+RMSNORM_ADD_MAX_N = 1 << 24
+RMSNORM_ADD_RESIDENT_MAX_N = 16384
+RMSNORM_CAST_MAX_N = 1 << 24
+RMSNORM_CAST_RESIDENT_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
 NOALLOC_SCRATCH_BYTES = 64 << 20  # RMSNORM_NOALLOC_SCRATCH_BYTES
 

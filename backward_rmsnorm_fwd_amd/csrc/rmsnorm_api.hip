@@ -1196,11 +1196,17 @@ int check_add_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
     return RMSNORM_ERR_DTYPE;
   if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
   if (N < 1 || N > RMSNORM_ADD_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  if (M > RMSNORM_MAX_ELEMENTS / N) return RMSNORM_ERR_SHAPE;
   return RMSNORM_OK;
 }
 
+// Rows over 16384 elements take RMSNorm's split plan and its workspace
+// ([P, N] partials, per-(row, segment) sums, per-row coefficients).
 size_t add_workspace_bytes(int64_t M, int64_t N, int dtype) {
-  return static_cast<size_t>(ln_partials(M, N, elem_bytes(dtype)) * N * 4);
+  if (M <= 0) return 0;
+  const int es = elem_bytes(dtype);
+  if (ln_split_rows(N)) return static_cast<size_t>(split_workspace(M, N, es).total_floats * 4);
+  return static_cast<size_t>(ln_partials(M, N, es) * N * 4);
 }
 
 int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
@@ -1222,13 +1228,17 @@ int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const
                   {matrix(x, M, ldx * es, N * es), matrix(res, M, ldr * es, N * es),
                    vec(gamma, N * es)}))
     return sp;
-  const LnPlan p = ln_plan(M, N, es, false,
-                           layout_alignment({x, res, gamma, y, h},
-                                            {ldx * es, ldr * es, ldy * es, ldh * es}),
-                           kAddFwdMatrices);
+  const int align = layout_alignment({x, res, gamma, y, h},
+                                     {ldx * es, ldr * es, ldy * es, ldh * es});
   const AddFwdArgs a{x, res, gamma, y, h, rstd, M, static_cast<int>(N), eps,
                      (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * es, ldr * es, ldy * es,
                      ldh * es};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
+                       split_partials(M, N, es, false)};
+    return status_of(add_split_fwd_launch(dtype, sp, a, stream));
+  }
+  const LnPlan p = ln_plan(M, N, es, false, align, kAddFwdMatrices);
   return status_of(add_fwd_launch(dtype, p, a, stream));
 }
 
@@ -1263,13 +1273,20 @@ int add_rows_launch(const void* dy, int64_t lddy, const void* dh, int64_t lddh, 
                     void* workspace, hipStream_t stream) {
   if (M == 0) return RMSNORM_OK;
   const int es = elem_bytes(dtype);
-  const LnPlan p = ln_plan(M, N, es, true,
-                           layout_alignment({dy, dh, h, gamma, dx},
-                                            {lddy * es, dh ? lddh * es : 16, ldh * es,
-                                             lddx * es}));
-  const AddBwdArgs a{dy, dh, h, gamma, rstd, dx, static_cast<float*>(workspace), M,
-                     static_cast<int>(N), (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * es,
-                     lddh * es, ldh * es, lddx * es};
+  const int align = layout_alignment({dy, dh, h, gamma, dx},
+                                     {lddy * es, dh ? lddh * es : 16, ldh * es, lddx * es});
+  float* part = static_cast<float*>(workspace);
+  const AddBwdArgs a{dy, dh, h, gamma, rstd, dx, part, M, static_cast<int>(N),
+                     (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * es, lddh * es, ldh * es,
+                     lddx * es};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
+                       split_partials(M, N, es, true)};
+    const SplitWorkspace w = split_workspace(M, N, es);
+    return status_of(add_split_bwd_launch(dtype, sp, a, part + w.dotp_offset,
+                                          part + w.coef_offset, stream));
+  }
+  const LnPlan p = ln_plan(M, N, es, true, align);
   return status_of(add_bwd_launch(dtype, p, a, stream));
 }
 
@@ -1314,7 +1331,11 @@ int add_bwd_impl(const void* dy, int64_t lddy, const void* dh, int64_t lddh, con
 void fill_add_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* out) {
   fill_ln_plan(M, N, dtype, pass, align, out, kAddFwdMatrices);
   if (pass == RMSNORM_PASS_BWD_REDUCE) return;
-  out->kernel = pass == RMSNORM_PASS_BWD_ROWS ? RMSNORM_KERNEL_ADD_BWD : RMSNORM_KERNEL_ADD_FWD;
+  const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+  if (ln_split_rows(N))
+    out->kernel = bwd ? RMSNORM_KERNEL_ADD_BWD_SPLIT : RMSNORM_KERNEL_ADD_FWD_SPLIT;
+  else
+    out->kernel = bwd ? RMSNORM_KERNEL_ADD_BWD : RMSNORM_KERNEL_ADD_FWD;
 }
 
 // ---- RMSNorm with its output cast to a narrower dtype (fused_cast.hip) ------
@@ -1331,10 +1352,13 @@ int check_cast_common(int64_t M, int64_t N, int dtype, int out_dtype, uint32_t f
     return RMSNORM_ERR_DTYPE;
   if (flags & ~(RMSNORM_FLAG_OFFSET | RMSNORM_FLAG_DGAMMA_IN_DTYPE)) return RMSNORM_ERR_FLAGS;
   if (N < 1 || N > RMSNORM_CAST_MAX_N || M < 0 || M > RMSNORM_MAX_M) return RMSNORM_ERR_SHAPE;
+  if (M > RMSNORM_MAX_ELEMENTS / N) return RMSNORM_ERR_SHAPE;
   return RMSNORM_OK;
 }
 
 size_t cast_workspace_bytes(int64_t M, int64_t N) {
+  if (M <= 0) return 0;
+  if (ln_split_rows(N)) return static_cast<size_t>(split_workspace(M, N, kCastIn).total_floats * 4);
   return static_cast<size_t>(ln_partials(M, N, kCastIn) * N * 4);
 }
 
@@ -1354,10 +1378,15 @@ int cast_fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int6
   if (const int sp = span_status({matrix(y, M, ldy * eo, N * eo), vec(rstd, M * 4)},
                   {matrix(x, M, ldx * kCastIn, N * kCastIn), vec(gamma, N * kCastIn)}))
     return sp;
-  const LnPlan p = ln_plan(M, N, kCastIn, false,
-                           layout_alignment({x, gamma, y}, {ldx * kCastIn, ldy * eo}));
+  const int align = layout_alignment({x, gamma, y}, {ldx * kCastIn, ldy * eo});
   const CastFwdArgs a{x, gamma, y, rstd, M, static_cast<int>(N), eps,
                       (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * kCastIn, ldy * eo};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(split_nseg(N, kCastIn)),
+                       split_partials(M, N, kCastIn, false)};
+    return status_of(cast_split_fwd_launch(out_dtype, sp, a, stream));
+  }
+  const LnPlan p = ln_plan(M, N, kCastIn, false, align);
   return status_of(cast_fwd_launch(out_dtype, p, a, stream));
 }
 
@@ -1392,12 +1421,20 @@ int cast_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                      void* workspace, hipStream_t stream) {
   if (M == 0) return RMSNORM_OK;
   const int eo = elem_bytes(out_dtype);
-  const LnPlan p = ln_plan(M, N, kCastIn, true,
-                           layout_alignment({dy, x, gamma, dx},
-                                            {lddy * eo, ldx * kCastIn, lddx * kCastIn}));
-  const CastBwdArgs a{dy, x, gamma, rstd, dx, static_cast<float*>(workspace), M,
-                      static_cast<int>(N), (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * eo,
-                      ldx * kCastIn, lddx * kCastIn};
+  const int align = layout_alignment({dy, x, gamma, dx},
+                                     {lddy * eo, ldx * kCastIn, lddx * kCastIn});
+  float* part = static_cast<float*>(workspace);
+  const CastBwdArgs a{dy, x, gamma, rstd, dx, part, M, static_cast<int>(N),
+                      (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * eo, ldx * kCastIn,
+                      lddx * kCastIn};
+  if (ln_split_rows(N)) {
+    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(split_nseg(N, kCastIn)),
+                       split_partials(M, N, kCastIn, true)};
+    const SplitWorkspace w = split_workspace(M, N, kCastIn);
+    return status_of(cast_split_bwd_launch(out_dtype, sp, a, part + w.dotp_offset,
+                                           part + w.coef_offset, stream));
+  }
+  const LnPlan p = ln_plan(M, N, kCastIn, true, align);
   return status_of(cast_bwd_launch(out_dtype, p, a, stream));
 }
 
@@ -1442,7 +1479,11 @@ int cast_bwd_impl(const void* dy, int64_t lddy, const void* x, int64_t ldx, cons
 void fill_cast_plan(int64_t M, int64_t N, int pass, int align, rmsnorm_plan_t* out) {
   fill_ln_plan(M, N, RMSNORM_F32, pass, align, out);
   if (pass == RMSNORM_PASS_BWD_REDUCE) return;
-  out->kernel = pass == RMSNORM_PASS_BWD_ROWS ? RMSNORM_KERNEL_CAST_BWD : RMSNORM_KERNEL_CAST_FWD;
+  const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+  if (ln_split_rows(N))
+    out->kernel = bwd ? RMSNORM_KERNEL_CAST_BWD_SPLIT : RMSNORM_KERNEL_CAST_FWD_SPLIT;
+  else
+    out->kernel = bwd ? RMSNORM_KERNEL_CAST_BWD : RMSNORM_KERNEL_CAST_FWD;
 }
 
 }  // namespace

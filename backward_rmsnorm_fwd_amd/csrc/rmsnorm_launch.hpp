@@ -226,4 +226,17 @@ hipError_t cast_fwd_launch(int out_dtype, const LnPlan& p, const CastFwdArgs& a,
 hipError_t cast_bwd_launch(int out_dtype, const LnPlan& p, const CastBwdArgs& a,
                            hipStream_t s);
 
+// Split-row plans of the fused add and the fused cast (rmsnorm_split.hip,
+// rows over 16384 elements): RMSNorm's split kernels, the add forming and
+// writing h in the stats pass and adding dh in the backward apply, the cast
+// with float32 x and dx and 16-bit y and dy.  Segments are 16 KiB of x.
+hipError_t add_split_fwd_launch(int dtype, const SplitPlan& sp, const AddFwdArgs& a,
+                                hipStream_t s);
+hipError_t add_split_bwd_launch(int dtype, const SplitPlan& sp, const AddBwdArgs& a,
+                                float* dotp, float* coef, hipStream_t s);
+hipError_t cast_split_fwd_launch(int out_dtype, const SplitPlan& sp, const CastFwdArgs& a,
+                                 hipStream_t s);
+hipError_t cast_split_bwd_launch(int out_dtype, const SplitPlan& sp, const CastBwdArgs& a,
+                                 float* dotp, float* coef, hipStream_t s);
+
 }  // namespace rmsnorm_hip

@@ -166,7 +166,7 @@ def main():
     row_cap = {"layernorm": rn.LAYERNORM_MAX_N, "add_rmsnorm": rn.RMSNORM_ADD_MAX_N,
                "rmsnorm_cast": rn.RMSNORM_CAST_MAX_N}.get(args.op)
     if row_cap is not None and workloads.WORKLOADS[args.workload].N > row_cap:
-        print(f"bench.py: --op {args.op} holds rows in registers (N <= {row_cap}); workload "
+        print(f"bench.py: --op {args.op} takes rows of N <= {row_cap}; workload "
               f"{args.workload} has N = {workloads.WORKLOADS[args.workload].N}",
               file=sys.stderr, flush=True)
         sys.exit(2)

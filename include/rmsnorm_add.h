@@ -21,8 +21,10 @@
  *
  * Conventions are those of rmsnorm.h (device pointers on the current device,
  * caller-owned buffers, row pitches in elements >= N, host-side validation,
- * no fallback, no overlapping outputs, reproducible), with rows held in
- * registers: 1 <= N <= RMSNORM_ADD_MAX_N.  Flags: RMSNORM_FLAG_OFFSET and
+ * no fallback, no overlapping outputs, reproducible), with
+ * 1 <= N <= RMSNORM_ADD_MAX_N (2^24) and M * N <= RMSNORM_MAX_ELEMENTS: rows
+ * of up to RMSNORM_ADD_RESIDENT_MAX_N elements are held in registers, longer
+ * rows take the split-row plan.  Flags: RMSNORM_FLAG_OFFSET and
  * RMSNORM_FLAG_DGAMMA_IN_DTYPE as in rmsnorm.h.
  */
 #ifndef RMSNORM_ADD_H
@@ -34,10 +36,16 @@
 extern "C" {
 #endif
 
-#define RMSNORM_ADD_MAX_N 16384
+#define RMSNORM_ADD_MAX_N (((int64_t)1) << 24)
+#define RMSNORM_ADD_RESIDENT_MAX_N 16384
 
 #define RMSNORM_KERNEL_ADD_FWD 17 /* fused add + forward, rows in registers */
 #define RMSNORM_KERNEL_ADD_BWD 18 /* backward stage 1 plus dh, same geometry */
+/* Rows over RMSNORM_ADD_RESIDENT_MAX_N: RMSNorm's split-row plan (16 KiB
+ * segments); the forward's stats kernel forms and writes h, its apply
+ * kernel reads h back; the backward's apply kernel adds dh. */
+#define RMSNORM_KERNEL_ADD_FWD_SPLIT 23 /* forward, three kernels */
+#define RMSNORM_KERNEL_ADD_BWD_SPLIT 24 /* backward stage 1, three kernels */
 
 /*
  * Forward.
@@ -49,7 +57,8 @@ extern "C" {
  *   h      [M, N] T, written (row pitch ldh): x + res, kept for the residual
  *          stream and for the backward
  *   rstd   [M] float32, written
- * Errors: as rmsnorm_fwd_strided (SHAPE for N > RMSNORM_ADD_MAX_N).
+ * Errors: as rmsnorm_fwd_strided (SHAPE for N > RMSNORM_ADD_MAX_N or
+ * M * N above RMSNORM_MAX_ELEMENTS).
  */
 int rmsnorm_add_fwd(const void* x, int64_t ldx, const void* res, int64_t ldr,
                     const void* gamma, float eps, int64_t M, int64_t N,
@@ -57,7 +66,9 @@ int rmsnorm_add_fwd(const void* x, int64_t ldx, const void* res, int64_t ldr,
                     void* h, int64_t ldh, float* rstd, hipStream_t stream);
 
 /* Workspace bytes of rmsnorm_add_bwd: float32 partial column sums [P, N],
- * P a fixed function of (M, N, dtype); 0 for M = 0 or invalid arguments. */
+ * P a fixed function of (M, N, dtype); split rows add one float32 sum per
+ * (row, segment) and one coefficient per row, each part from a 16-byte
+ * boundary.  0 for M = 0 or invalid arguments. */
 size_t rmsnorm_add_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                        uint32_t flags);
 

@@ -25,8 +25,10 @@
  * Conventions are those of rmsnorm.h (device pointers on the current device,
  * caller-owned buffers, row pitches in elements >= N, work enqueued on
  * `stream`, host-side validation before anything is enqueued, no fallback,
- * no overlapping outputs, bitwise reproducible), with rows held in
- * registers: 1 <= N <= RMSNORM_CAST_MAX_N.  Flags: RMSNORM_FLAG_OFFSET;
+ * no overlapping outputs, bitwise reproducible), with
+ * 1 <= N <= RMSNORM_CAST_MAX_N (2^24) and M * N <= RMSNORM_MAX_ELEMENTS: rows
+ * of up to RMSNORM_CAST_RESIDENT_MAX_N elements are held in registers,
+ * longer rows take the split-row plan.  Flags: RMSNORM_FLAG_OFFSET;
  * RMSNORM_FLAG_DGAMMA_IN_DTYPE is accepted and changes nothing (the input
  * dtype is float32).
  */
@@ -39,10 +41,15 @@
 extern "C" {
 #endif
 
-#define RMSNORM_CAST_MAX_N 16384
+#define RMSNORM_CAST_MAX_N (((int64_t)1) << 24)
+#define RMSNORM_CAST_RESIDENT_MAX_N 16384
 
 #define RMSNORM_KERNEL_CAST_FWD 19 /* forward with the cast, rows in registers */
 #define RMSNORM_KERNEL_CAST_BWD 20 /* backward stage 1 from the narrow dy */
+/* Rows over RMSNORM_CAST_RESIDENT_MAX_N: RMSNorm's split-row plan on 16 KiB
+ * segments of the float32 x, the per-segment sums parked in the narrow y. */
+#define RMSNORM_KERNEL_CAST_FWD_SPLIT 25 /* forward, three kernels */
+#define RMSNORM_KERNEL_CAST_BWD_SPLIT 26 /* backward stage 1, three kernels */
 
 /*
  * Forward.
@@ -52,7 +59,8 @@ extern "C" {
  *   y      [M, N] out_dtype, written (row pitch ldy)
  *   rstd   [M] float32, written
  * Errors: NULL_POINTER, DTYPE (see above), SHAPE (N outside
- * [1, RMSNORM_CAST_MAX_N], M outside [0, RMSNORM_MAX_M]), EPS, FLAGS, STRIDE,
+ * [1, RMSNORM_CAST_MAX_N], M outside [0, RMSNORM_MAX_M], M * N above
+ * RMSNORM_MAX_ELEMENTS), EPS, FLAGS, STRIDE,
  * ALIGNMENT (a pointer not aligned to its element size), OVERLAP, LAUNCH.
  */
 int rmsnorm_cast_fwd(const void* x, int64_t ldx, const void* gamma, float eps,
@@ -61,7 +69,9 @@ int rmsnorm_cast_fwd(const void* x, int64_t ldx, const void* gamma, float eps,
                      float* rstd, hipStream_t stream);
 
 /* Workspace bytes of rmsnorm_cast_bwd: float32 partial column sums [P, N],
- * P a fixed function of (M, N); 0 for M = 0 or invalid arguments. */
+ * P a fixed function of (M, N); split rows add one float32 sum per (row,
+ * segment) and one coefficient per row, each part from a 16-byte boundary.
+ * 0 for M = 0 or invalid arguments. */
 size_t rmsnorm_cast_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                         rmsnorm_dtype_t out_dtype, uint32_t flags);
 

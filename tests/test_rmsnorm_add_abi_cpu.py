@@ -30,7 +30,7 @@ def fwd_call(x=A, res=A + S, g=A + 2 * S, eps=1e-6, M=4, N=256, dtype=2, flags=0
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": 3}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": 0}, ESHAPE), ({"N": 16385}, ESHAPE),
+    ({"dtype": 3}, EDTYPE), ({"flags": 4}, EFLAGS), ({"N": 0}, ESHAPE), ({"N": (1 << 24) + 1}, ESHAPE),
     ({"eps": -1.0}, EEPS), ({"ldr": 10}, ESTRIDE), ({"ldh": 255}, ESTRIDE),
     ({"x": None}, ENULL), ({"res": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL),
     ({"h": None}, ENULL), ({"rstd": None}, ENULL),
@@ -61,7 +61,7 @@ def bwd_call(dy=A, dh=A + S, h=A + 2 * S, g=A + 3 * S, rstd=A + 4 * S, M=4, N=25
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dtype": 7}, EDTYPE), ({"flags": 8}, EFLAGS), ({"N": 20000}, ESHAPE),
+    ({"dtype": 7}, EDTYPE), ({"flags": 8}, EFLAGS), ({"N": (1 << 24) + 1}, ESHAPE),
     ({"lddh": 3}, ESTRIDE),
     ({"dy": None}, ENULL), ({"h": None}, ENULL), ({"g": None}, ENULL), ({"rstd": None}, ENULL),
     ({"dx": None}, ENULL), ({"dg": None}, ENULL),
@@ -106,3 +106,33 @@ def test_plans_follow_the_row_resident_plan(dt):
                     assert a["kernel_name"] == want
             P = rn.rmsnorm_add_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)["partials"]
             assert rn.rmsnorm_add_bwd_workspace_bytes(m, n, dt) == P * n * 4
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("M,N,dt", [(33, 16385, 2), (5, 16386, 1), (7, 16388, 0),
+                                    (2, 1 << 24, 2), (2048, 65536, 2), (100000, 20000, 1),
+                                    (4096, 65537, 0)])
+def test_split_plan(M, N, dt):
+    """Rows over the row-resident limit take RMSNorm's split geometry (16 KiB
+    segments, the same P, a workspace of [P, N] partials, per-(row, segment)
+    sums and per-row coefficients)."""
+    es = 4 if dt == 0 else 2
+    nseg = _ceil(N * es, 16384)
+    f = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_FWD)
+    b = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
+    assert f["kernel_name"] == "add_fwd_split" and b["kernel_name"] == "add_bwd_split"
+    for p in (f, b):
+        assert p["segments"] == nseg and p["block_threads"] == 256
+        assert p["chunks"] * p["vec"] * es == 64 and p["grid"] % nseg == 0
+    P = b["partials"]
+    assert P == max(1, min(M, max(_ceil(M, 16), _ceil(1024, nseg)), ((1 << 24) - 1) // nseg))
+    assert f["grid"] // nseg == max(1, min(M, _ceil(2048, nseg), ((1 << 24) - 1) // nseg))
+    r4 = lambda v: _ceil(v, 4) * 4  # noqa: E731
+    assert rn.rmsnorm_add_bwd_workspace_bytes(M, N, dt) == 4 * (r4(P * N) + r4(M * nseg) + r4(M))
+    assert rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_BWD_REDUCE)["partials"] == P
+    if N > 65536:
+        r = rn.rmsnorm_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
+        assert (r["grid"], r["partials"]) == (b["grid"], P)

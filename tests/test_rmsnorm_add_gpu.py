@@ -2,8 +2,9 @@
 ABI (include/rmsnorm_add.h), against the fused oracle (oracle.fused): h
 bitwise equal to the dtype's add, y, rstd, dx (RMSNorm's gradient plus dh)
 and dgamma through the gate, at reduced sizes of each recipe, tile and edge
-shapes, misaligned and strided layouts, without dh, c2 at full size on
-every element and c3, c5 at full size on sampled rows and columns."""
+shapes, rows longer than the row-resident limit (the split-row plan),
+misaligned and strided layouts, without dh, c2 at full size on every
+element and c3, c4, c5 at full size on sampled rows and columns."""
 import pytest
 import torch
 
@@ -19,7 +20,9 @@ pytestmark = pytest.mark.gpu
                                       ("c2", 2051, 4096), ("c2", 517, 4104),
                                       ("c3", 3001, 1000), ("c3", 20011, 1024),
                                       ("c5", 1031, 5120), ("c5", 301, 5112),
-                                      ("c4", 37, 16384), ("c4", 9, 16376)])
+                                      ("c4", 37, 16384), ("c4", 9, 16376),
+                                      ("c4", 9, 65536), ("c5", 33, 20480),
+                                      ("c2", 700, 16400)])
 def test_recipes(cuda, name, M, N):
     inp = workloads.make_add_inputs(name, M=M, N=N)
     log(f"case add {name} M={inp['M']} N={inp['N']}")
@@ -30,17 +33,20 @@ def test_recipes(cuda, name, M, N):
                                      (torch.float16, 255), (torch.bfloat16, 257),
                                      (torch.float32, 4095), (torch.bfloat16, 4097),
                                      (torch.float16, 8193), (torch.float32, 16384),
-                                     (torch.bfloat16, 16383)])
+                                     (torch.bfloat16, 16383), (torch.bfloat16, 16385),
+                                     (torch.float16, 16386), (torch.float32, 16388),
+                                     (torch.float32, 24577), (torch.bfloat16, 131072)])
 def test_edge_shapes(cuda, dtype, N):
     inp = workloads.make_add_inputs("c1a", M=7, N=N, dtype=dtype)
     log(f"case add edge {dtype} N={N}")
     assert_pass(gate_add_full(inp, run_add_target(inp, cuda)), f"add edge {dtype} N={N}")
 
 
-def test_without_dh(cuda):
-    inp = workloads.make_add_inputs("c2", M=700, N=4096)
+@pytest.mark.parametrize("N", [4096, 40000])
+def test_without_dh(cuda, N):
+    inp = workloads.make_add_inputs("c2", M=700 if N == 4096 else 40, N=N)
     out = run_add_target(inp, cuda, with_dh=False)
-    assert_pass(gate_add_full(inp, out, with_dh=False), "add without dh")
+    assert_pass(gate_add_full(inp, out, with_dh=False), f"add without dh N={N}")
 
 
 def test_full_size_c2(cuda):
@@ -51,15 +57,16 @@ def test_full_size_c2(cuda):
     assert_pass(gate_add_full(inp, out), "add c2 full size, every element")
 
 
-@pytest.mark.parametrize("name", ["c3", "c5"])
-def test_full_size_sampled(cuda, name):
-    """The fp16 262144 x 1024 and offset bf16 65536 x 5120 shapes at full
-    size, default plan; sampled rows and dgamma columns against the oracle."""
+@pytest.mark.parametrize("name,nrows", [("c3", 1024), ("c4", 256), ("c5", 1024)])
+def test_full_size_sampled(cuda, name, nrows):
+    """The fp16 262144 x 1024, bf16 2048 x 65536 (split rows) and offset
+    bf16 65536 x 5120 shapes at full size, default plan; sampled rows and
+    dgamma columns against the oracle."""
     inp = workloads.make_add_inputs(name)
     log(f"case add {name} full size M={inp['M']} N={inp['N']} generated")
     out = run_add_target(inp, cuda)
     log(f"case add {name} device run done")
-    rows = sample_rows(inp, 1024)
+    rows = sample_rows(inp, nrows)
     cols = sample_cols(inp["N"], 64)
     assert_pass(gate_add_sampled(inp, out, rows, cols), f"add {name} full size, sampled")
     for k in ("y", "h", "dx", "rstd", "dgamma"):
@@ -81,8 +88,8 @@ def test_reproducible_offset_and_dgamma_in_dtype(cuda):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_misaligned_and_strided(cuda, dtype):
-    M, N = 33, 4096
+@pytest.mark.parametrize("M,N", [(33, 4096), (9, 20000)])
+def test_misaligned_and_strided(cuda, dtype, M, N):
     inp = workloads.make_add_inputs("c2", M=M, N=N, dtype=dtype)
 
     def shifted(t):

@@ -32,7 +32,7 @@ def fwd_call(x=A, g=A + S, eps=1e-6, M=4, N=256, dtype=F32, out=BF16, flags=0, y
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": BF16}, EDTYPE), ({"dtype": F16}, EDTYPE), ({"out": F32}, EDTYPE),
     ({"out": 3}, EDTYPE), ({"flags": 4}, EFLAGS),
-    ({"N": 0}, ESHAPE), ({"N": 16385}, ESHAPE), ({"M": -1}, ESHAPE),
+    ({"N": 0}, ESHAPE), ({"N": (1 << 24) + 1}, ESHAPE), ({"M": -1}, ESHAPE),
     ({"eps": 0.0}, EEPS), ({"eps": float("inf")}, EEPS),
     ({"ldx": 255}, ESTRIDE), ({"ldy": 100}, ESTRIDE),
     ({"x": None}, ENULL), ({"g": None}, ENULL), ({"y": None}, ENULL), ({"rstd": None}, ENULL),
@@ -68,7 +68,7 @@ def bwd_call(dy=A, x=A + S, g=A + 2 * S, rstd=A + 3 * S, M=4, N=256, dtype=F32, 
 
 @pytest.mark.parametrize("kw,code", [
     ({"dtype": F16}, EDTYPE), ({"out": F32}, EDTYPE), ({"flags": 8}, EFLAGS),
-    ({"N": 20000}, ESHAPE), ({"lddx": 3}, ESTRIDE), ({"lddy": 255}, ESTRIDE),
+    ({"N": (1 << 24) + 1}, ESHAPE), ({"lddx": 3}, ESTRIDE), ({"lddy": 255}, ESTRIDE),
     ({"dy": None}, ENULL), ({"x": None}, ENULL), ({"g": None}, ENULL), ({"rstd": None}, ENULL),
     ({"dx": None}, ENULL), ({"dg": None}, ENULL),
     ({"ws": None}, EWS), ({"ws_bytes": 16}, EWS), ({"ws": A + 6 * S + 8}, EALIGN),
@@ -126,7 +126,35 @@ def test_query_plan_rejects():
     assert L.rmsnorm_cast_query_plan(4, 256, F32, BF16, 0, 7, 16, ctypes.byref(p)) == EARG
     assert L.rmsnorm_cast_query_plan(4, 256, F32, BF16, 0, 0, 3, ctypes.byref(p)) == EARG
     assert L.rmsnorm_cast_query_plan(4, 256, BF16, BF16, 0, 0, 16, ctypes.byref(p)) == EDTYPE
-    assert L.rmsnorm_cast_query_plan(4, 16385, F32, F16, 0, 0, 16, ctypes.byref(p)) == ESHAPE
+    assert L.rmsnorm_cast_query_plan(4, (1 << 24) + 1, F32, F16, 0, 0, 16,
+                                     ctypes.byref(p)) == ESHAPE
     assert L.rmsnorm_cast_query_plan(4, 256, F32, F16, 0, 0, 16, None) == ENULL
     assert L.rmsnorm_cast_bwd_workspace_bytes(0, 256, F32, BF16, 0) == 0
     assert L.rmsnorm_cast_bwd_workspace_bytes(4, 256, F32, F32, 0) == 0
+
+
+@pytest.mark.parametrize("out", ["bfloat16", "float16"])
+@pytest.mark.parametrize("M,N", [(33, 16385), (7, 16388), (2048, 65536), (2, 1 << 24),
+                                 (100000, 20000)])
+def test_split_plan(out, M, N):
+    """Rows over the row-resident limit take RMSNorm's float32 split
+    geometry: 16 KiB segments of x (4096 elements), P and the workspace of a
+    float32 RMSNorm split; the access width keeps the narrow y and dy within
+    the layout's alignment."""
+    import torch
+    od = getattr(torch, out)
+    nseg = -(-N // 4096)
+    f = rn.rmsnorm_cast_query_plan(M, N, od, which=rn.PASS_FWD)
+    b = rn.rmsnorm_cast_query_plan(M, N, od, which=rn.PASS_BWD_ROWS)
+    assert f["kernel_name"] == "cast_fwd_split" and b["kernel_name"] == "cast_bwd_split"
+    for p in (f, b):
+        assert p["segments"] == nseg and p["chunks"] * p["vec"] * 4 == 64
+    ln = rn.layernorm_query_plan(M, N, torch.float32, which=rn.PASS_BWD_ROWS)
+    assert (b["grid"], b["partials"]) == (ln["grid"], ln["partials"])
+    P = b["partials"]
+    r4 = lambda v: -(-v // 4) * 4  # noqa: E731
+    assert rn.rmsnorm_cast_bwd_workspace_bytes(M, N, od) == 4 * (r4(P * N) + r4(M * nseg)
+                                                                + r4(M))
+    for align in (16, 8, 4):
+        p = rn.rmsnorm_cast_query_plan(M, N, od, which=rn.PASS_FWD, align_bytes=align)
+        assert p["vec"] * 4 <= align and N % p["vec"] == 0

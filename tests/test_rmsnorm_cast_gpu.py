@@ -2,10 +2,10 @@
 ABI (include/rmsnorm_cast.h), against the cast oracle (oracle.fused): y in
 bfloat16 or float16 (gated at that dtype's rounding floor), rstd, dx and
 dgamma (float32, from dy in the narrow dtype) through the gate, at reduced
-sizes of each recipe, edge shapes, misaligned and strided layouts, the
-offset weight, the c2, c3 and c5 shapes at full size on sampled rows and
-columns, and against the unfused pair (float32 RMSNorm, then PyTorch's
-cast)."""
+sizes of each recipe, edge shapes, rows longer than the row-resident limit
+(the split-row plan), misaligned and strided layouts, the offset weight,
+the c2, c3, c4 and c5 shapes at full size on sampled rows and columns, and
+against the unfused pair (float32 RMSNorm, then PyTorch's cast)."""
 import pytest
 import torch
 
@@ -24,7 +24,9 @@ OUT = [torch.bfloat16, torch.float16]
                                       ("c1c", None, None), ("c2", 2051, 4096),
                                       ("c2", 517, 4104), ("c3", 3001, 1000),
                                       ("c5", 1031, 5120), ("c5", 301, 5112),
-                                      ("c4", 37, 16384), ("c4", 9, 16376)])
+                                      ("c4", 37, 16384), ("c4", 9, 16376),
+                                      ("c4", 9, 65536), ("c5", 33, 20480),
+                                      ("c2", 700, 16400)])
 def test_recipes(cuda, name, M, N, out_dtype):
     inp = workloads.make_cast_inputs(name, M=M, N=N, out_dtype=out_dtype)
     log(f"case cast {name} M={inp['M']} N={inp['N']} -> {out_dtype}")
@@ -37,7 +39,9 @@ def test_recipes(cuda, name, M, N, out_dtype):
                                          (torch.bfloat16, 257), (torch.float16, 4095),
                                          (torch.bfloat16, 4097), (torch.float16, 8193),
                                          (torch.bfloat16, 12288), (torch.float16, 16383),
-                                         (torch.bfloat16, 16384)])
+                                         (torch.bfloat16, 16384), (torch.bfloat16, 16385),
+                                         (torch.float16, 16386), (torch.bfloat16, 16388),
+                                         (torch.float16, 24577), (torch.bfloat16, 131072)])
 def test_edge_shapes(cuda, out_dtype, N):
     inp = workloads.make_cast_inputs("c1a", M=7, N=N, out_dtype=out_dtype)
     log(f"case cast edge N={N} -> {out_dtype}")
@@ -56,7 +60,7 @@ def test_tiny_and_zero_rows(cuda, out_dtype):
 
 
 @pytest.mark.parametrize("name,out_dtype", [("c2", torch.bfloat16), ("c3", torch.float16),
-                                            ("c5", torch.bfloat16)])
+                                            ("c4", torch.bfloat16), ("c5", torch.bfloat16)])
 def test_full_size_shape_sampled(cuda, name, out_dtype):
     """Each benchmarked shape at full size (float32 x, y and dy in the
     shape's 16-bit dtype), default plan, sampled rows and dgamma columns."""
@@ -107,8 +111,8 @@ def test_matches_the_unfused_pair(cuda, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", OUT)
-def test_misaligned_and_strided(cuda, out_dtype):
-    M, N = 33, 4096
+@pytest.mark.parametrize("M,N", [(33, 4096), (9, 20000)])
+def test_misaligned_and_strided(cuda, out_dtype, M, N):
     inp = workloads.make_cast_inputs("c2", M=M, N=N, out_dtype=out_dtype)
 
     def shifted(t, dtype=None):
