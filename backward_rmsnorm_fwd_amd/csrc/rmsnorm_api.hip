@@ -348,13 +348,17 @@ struct SplitWorkspace {
   int64_t part_floats, dotp_offset, coef_offset, total_floats;
 };
 
-SplitWorkspace split_workspace(int64_t M, int64_t N, int es) {
+SplitWorkspace split_workspace_for(int64_t P, int64_t M, int64_t N, int es) {
   SplitWorkspace w;
-  w.part_floats = split_partials(M, N, es, true) * N;
+  w.part_floats = P * N;
   w.dotp_offset = ceil_div(w.part_floats, 4) * 4;
   w.coef_offset = w.dotp_offset + ceil_div(M * split_nseg(N, es), 4) * 4;
   w.total_floats = w.coef_offset + ceil_div(M, 4) * 4;
   return w;
+}
+
+SplitWorkspace split_workspace(int64_t M, int64_t N, int es) {
+  return split_workspace_for(split_partials(M, N, es, true), M, N, es);
 }
 
 // Backward workgroup count P: a function of (M, N, dtype) only, computed
@@ -1200,14 +1204,68 @@ int check_add_common(int64_t M, int64_t N, int dtype, uint32_t flags) {
   return RMSNORM_OK;
 }
 
-// Rows over 16384 elements take RMSNorm's split plan and its workspace
-// ([P, N] partials, per-(row, segment) sums, per-row coefficients).
+// Rows over 16384 elements: full-width rows of up to 128 KiB run on
+// RMSNorm's long-row kernels (the forward's fwd_fast_kernel with the add,
+// bwd_longrow_kernel on h with dh), one row per 512-thread workgroup at a
+// time; other layouts take RMSNorm's split plan.  The split
+// fused step at bf16 2048 x 65536 measured 568.8 us, slower than the
+// unfused pair (torch's add around the long-row RMSNorm, 541.0 us).
+// P is a function of (M, N, dtype): the long-row count wherever the
+// full-width layout can take the long-row backward, so a misaligned call
+// runs the split kernels on the same P, and the workspace always has the
+// split layout ([P, N] partials, per-(row, segment) sums, per-row
+// coefficients).
+int add_long_fwd_ch(int64_t N, int es, int align) {
+  if (!ln_split_rows(N)) return 0;
+  const int vec = pick_vec(N, es, align);
+  if (vec * es != 16) return 0;
+  const Cfg c = plan_fast_fwd(N / vec);
+  if (!c.ok || c.wpr != 8 || c.block != 512 || !c.greg || c.ch < 5 || c.ch > 16) return 0;
+  return c.ch;
+}
+
+int add_long_bwd_ch(int64_t N, int es, int align) {
+  if (!ln_split_rows(N)) return 0;
+  const int vec = pick_vec(N, es, align);
+  if (vec * es != 16) return 0;
+  const int ch = plan_long_bwd(N / vec);
+  return ch >= 5 ? ch : 0;
+}
+
+int64_t add_bwd_partials(int64_t M, int64_t N, int es) {
+  if (M <= 0) return 0;
+  if (!ln_split_rows(N)) return ln_partials(M, N, es);
+  if (add_long_bwd_ch(N, es, 16)) return std::min<int64_t>(M, kLongBwdWorkgroups);
+  return split_partials(M, N, es, true);
+}
+
 size_t add_workspace_bytes(int64_t M, int64_t N, int dtype) {
   if (M <= 0) return 0;
   const int es = elem_bytes(dtype);
-  if (ln_split_rows(N)) return static_cast<size_t>(split_workspace(M, N, es).total_floats * 4);
-  return static_cast<size_t>(ln_partials(M, N, es) * N * 4);
+  const int64_t P = add_bwd_partials(M, N, es);
+  if (ln_split_rows(N)) return static_cast<size_t>(split_workspace_for(P, M, N, es).total_floats * 4);
+  return static_cast<size_t>(P * N * 4);
 }
+
+hipError_t add_long_fwd(int dtype, int ch, int64_t grid, const AddFwdArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_F32: return add_long_fwd_launch<kF32>(ch, grid, a, s);
+    case RMSNORM_F16: return add_long_fwd_launch<kF16>(ch, grid, a, s);
+    default: return add_long_fwd_launch<kBF16>(ch, grid, a, s);
+  }
+}
+
+hipError_t add_long_bwd(int dtype, int ch, int64_t P, int64_t lds, const AddBwdArgs& a,
+                        hipStream_t s) {
+  switch (dtype) {
+    case RMSNORM_F32: return add_long_bwd_launch<kF32>(ch, P, lds, a, s);
+    case RMSNORM_F16: return add_long_bwd_launch<kF16>(ch, P, lds, a, s);
+    default: return add_long_bwd_launch<kBF16>(ch, P, lds, a, s);
+  }
+}
+
+// Forward grid of the long-row add: one row per workgroup at a time.
+int64_t add_long_fwd_grid(int64_t M) { return std::min<int64_t>(M, int64_t(1) << 20); }
 
 int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
                  float eps, int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags, void* y,
@@ -1233,6 +1291,8 @@ int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const
   const AddFwdArgs a{x, res, gamma, y, h, rstd, M, static_cast<int>(N), eps,
                      (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * es, ldr * es, ldy * es,
                      ldh * es};
+  if (const int ch = add_long_fwd_ch(N, es, align))
+    return status_of(add_long_fwd(dtype, ch, add_long_fwd_grid(M), a, stream));
   if (ln_split_rows(N)) {
     const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
                        split_partials(M, N, es, false)};
@@ -1279,10 +1339,12 @@ int add_rows_launch(const void* dy, int64_t lddy, const void* dh, int64_t lddh, 
   const AddBwdArgs a{dy, dh, h, gamma, rstd, dx, part, M, static_cast<int>(N),
                      (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * es, lddh * es, ldh * es,
                      lddx * es};
+  const int64_t P = add_bwd_partials(M, N, es);
+  if (const int ch = add_long_bwd_ch(N, es, align))
+    return status_of(add_long_bwd(dtype, ch, P, N * es, a, stream));
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
-                       split_partials(M, N, es, true)};
-    const SplitWorkspace w = split_workspace(M, N, es);
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)), P};
+    const SplitWorkspace w = split_workspace_for(P, M, N, es);
     return status_of(add_split_bwd_launch(dtype, sp, a, part + w.dotp_offset,
                                           part + w.coef_offset, stream));
   }
@@ -1324,18 +1386,41 @@ int add_bwd_impl(const void* dy, int64_t lddy, const void* dh, int64_t lddh, con
   st = add_rows_launch(dy, lddy, dh, lddh, h, ldh, gamma, rstd, M, N, dtype, flags, dx, lddx,
                        workspace, stream);
   if (st != RMSNORM_OK) return st;
-  return reduce_columns(static_cast<const float*>(workspace), ln_partials(M, N, es), N, dtype,
+  return reduce_columns(static_cast<const float*>(workspace), add_bwd_partials(M, N, es), N, dtype,
                         flags, dgamma, stream);
 }
 
 void fill_add_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_plan_t* out) {
+  const int es = elem_bytes(dtype);
+  if (pass == RMSNORM_PASS_BWD_REDUCE) {
+    std::memset(out, 0, sizeof(*out));
+    fill_reduce_plan(add_bwd_partials(M, N, es), N, out);
+    return;
+  }
   fill_ln_plan(M, N, dtype, pass, align, out, kAddFwdMatrices);
-  if (pass == RMSNORM_PASS_BWD_REDUCE) return;
   const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
-  if (ln_split_rows(N))
+  const int ch = bwd ? add_long_bwd_ch(N, es, align) : add_long_fwd_ch(N, es, align);
+  if (ch) {
+    std::memset(out, 0, sizeof(*out));
+    out->kernel = bwd ? RMSNORM_KERNEL_ADD_BWD_LONG : RMSNORM_KERNEL_ADD_FWD_LONG;
+    out->vec = 16 / es;
+    out->threads_per_row = 512;
+    out->chunks = ch;
+    out->block_threads = 512;
+    out->weight_in_regs = bwd ? 0 : 1;
+    out->x_in_lds = bwd ? 1 : 0;
+    out->partials = bwd ? add_bwd_partials(M, N, es) : 0;
+    out->grid = bwd ? out->partials : add_long_fwd_grid(M);
+    out->lds_bytes = bwd ? N * es : 0;
+  } else if (ln_split_rows(N)) {
     out->kernel = bwd ? RMSNORM_KERNEL_ADD_BWD_SPLIT : RMSNORM_KERNEL_ADD_FWD_SPLIT;
-  else
+    if (bwd) {
+      out->partials = add_bwd_partials(M, N, es);
+      out->grid = out->partials * out->segments;
+    }
+  } else {
     out->kernel = bwd ? RMSNORM_KERNEL_ADD_BWD : RMSNORM_KERNEL_ADD_FWD;
+  }
 }
 
 // ---- RMSNorm with its output cast to a narrower dtype (fused_cast.hip) ------
@@ -1744,7 +1829,8 @@ int rmsnorm_add_bwd_reduce(const void* workspace, size_t workspace_bytes, int64_
   const int st = check_add_reduce_args(workspace, workspace_bytes, M, N, dtype, flags, dgamma);
   if (st != RMSNORM_OK) return st;
   return reduce_columns(static_cast<const float*>(workspace),
-                        ln_partials(M, N, elem_bytes(dtype)), N, dtype, flags, dgamma, stream);
+                        add_bwd_partials(M, N, elem_bytes(dtype)), N, dtype, flags, dgamma,
+                        stream);
 }
 
 int rmsnorm_add_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,

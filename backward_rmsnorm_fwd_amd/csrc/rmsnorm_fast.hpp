@@ -187,12 +187,16 @@ struct RowSched {
 // Forward.  Workgroup b handles rows b*G + g, then strides by gridDim.x*G.
 // GREG keeps the weight in registers across rows (else it is re-read from
 // cache each row); NT marks x loads and y stores as streaming.
+// ADD (the residual add fused before the norm): the row is h = T(x + res),
+// formed from the two loaded rows, written to h and then normalised; res, h
+// and their pitches are unused otherwise.
 // ---------------------------------------------------------------------------
-template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool NT, int MINW = 1>
+template <int DT, int CH, int WPR, int BLOCK, bool GREG, bool NT, int MINW = 1, bool ADD = false>
 __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, void* __restrict__ y,
     float* __restrict__ rstd, int64_t M, int N, float eps, int offset, int64_t x_pitch,
-    int64_t y_pitch) {
+    int64_t y_pitch, const void* __restrict__ res, void* __restrict__ h, int64_t res_pitch,
+    int64_t h_pitch) {
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR, G = Geo::G;
   constexpr uint32_t kChunk = TPR * 16;  // bytes per chunk sweep
@@ -232,6 +236,27 @@ __global__ __launch_bounds__(BLOCK, MINW) void fwd_fast_kernel(
       for (int c = 0; c < CH; ++c) {
         if (c < CH - 1 || voff + c * kChunk < row_bytes) xv[c].raw = xb.template load<NT>(voff, c * kChunk);
         else xv[c].zero();
+      }
+      if constexpr (ADD) {
+        // h = T(x + res): the float32 sum rounded once on packing; the
+        // norm below reads the rounded h.  Every chunk of res is in flight
+        // before the first sum.
+        const GRow rb(static_cast<const char*>(res) + row * res_pitch);
+        const GRow hb(static_cast<char*>(h) + row * h_pitch);
+        PK rv[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          if (c < CH - 1 || voff + c * kChunk < row_bytes) rv[c].raw = rb.template load<NT>(voff, c * kChunk);
+          else rv[c].zero();
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          float sum[VEC];
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) sum[k] = xv[c].get(k) + rv[c].get(k);
+          xv[c].set(sum);
+          if (c < CH - 1 || voff + c * kChunk < row_bytes) hb.template store<NT>(xv[c].raw, voff, c * kChunk);
+        }
       }
     } else {
 #pragma unroll
@@ -922,12 +947,15 @@ __device__ __forceinline__ u32x4 lds_read16_after(const void* p, const u32x4& de
   return v;
 }
 
-template <int DT, int CH, bool NT>
+// DH (the residual add fused before the norm, x being h): dx also adds the
+// gradient dh arriving on h, read like the weight one chunk ahead of its use.
+template <int DT, int CH, bool NT, bool DH = false>
 __global__ __launch_bounds__(512) void bwd_longrow_kernel(
     const void* __restrict__ dy, const void* __restrict__ x,
     const void* __restrict__ gamma, const float* __restrict__ rstd,
     void* __restrict__ dx, float* __restrict__ part, int64_t M, int N, int offset,
-    int64_t P, int64_t dy_pitch, int64_t x_pitch, int64_t dx_pitch) {
+    int64_t P, int64_t dy_pitch, int64_t x_pitch, int64_t dx_pitch,
+    const void* __restrict__ dh, int64_t dh_pitch) {
   constexpr int WPR = 8, BLOCK = 512;
   using Geo = Geometry<DT, CH, WPR, BLOCK>;
   constexpr int VEC = Geo::VEC, TPR = Geo::TPR;
@@ -1007,10 +1035,18 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
 
     // pass B
     const URow ob(static_cast<char*>(dx) + row * dx_pitch);
+    const URow hb(static_cast<const char*>(dh) + (DH ? row * dh_pitch : 0));
+    auto load_dh = [&](int c) __attribute__((always_inline)) {
+      PK e;
+      if (DH && in_row(c)) e.raw = hb.template load<NT>(voff, c * kChunk);
+      else e.zero();
+      return e;
+    };
     gc = load_g(0);
+    PK ec = load_dh(0);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      PK gn;
+      PK gn, en;
       if (c + 1 < CH) gn = load_g(c + 1);
       dv[c].opaque();  // re-widen here rather than keep pass A's floats
       if (in_row(c)) {
@@ -1023,10 +1059,19 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
           const float dyf = dv[c].get(k);
           const float u = dyf * weight_of(gc.get(k), offset);
           o[k] = fmaf(-xf, r3c, r * u);
+          if constexpr (DH) o[k] = o[k] + ec.get(k);
           acc[c][k] = fmaf(dyf * xf, r, acc[c][k]);
         }
         PK out;
         out.set(o);
+        // dh of the next chunk: issued once this chunk's dh is consumed
+        // (one set live) and before this chunk's store, so its wait does
+        // not cover the store.  (Only the last chunk can lie outside the
+        // row, and it has no next chunk.)
+        if constexpr (DH) {
+          order_fence();
+          if (c + 1 < CH) en = load_dh(c + 1);
+        }
         ob.template store<NT>(out.raw, voff, c * kChunk);
       }
 #pragma unroll
@@ -1034,7 +1079,10 @@ __global__ __launch_bounds__(512) void bwd_longrow_kernel(
       order_fence();
       if (has_next) issue_chunk(row + rs.stride, c);
       order_fence();
-      if (c + 1 < CH) gc = gn;
+      if (c + 1 < CH) {
+        gc = gn;
+        ec = en;
+      }
     }
   }
 

@@ -12,7 +12,8 @@ hipError_t fast_fwd_launch<kF32>(int wpr, int ch, int block, int greg, int64_t g
 #define RMSNORM_X(W, C, B, GR)                                                              \
   if (wpr == W && ch == C && block == B && greg == GR)                                      \
     return launch(fwd_fast_kernel<kF32, C, W, B, GR != 0, true>, grid, B, 0, s, a.x, a.gamma, \
-                  a.y, a.rstd, a.M, a.N, a.eps, a.offset, a.x_pitch, a.y_pitch);
+                  a.y, a.rstd, a.M, a.N, a.eps, a.offset, a.x_pitch, a.y_pitch, \
+                  nullptr, nullptr, int64_t(0), int64_t(0));
   RMSNORM_FWD_FAST_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
@@ -63,8 +64,39 @@ hipError_t long_bwd_launch<kF32>(int ch, int64_t lds, const FastBwdArgs& a, hipS
   if (ch == C)                                                                              \
     return launch(bwd_longrow_kernel<kF32, C, true>, a.P, 512, static_cast<size_t>(lds), s,   \
                   a.dy, a.x, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, a.P,        \
-                  a.dy_pitch, a.x_pitch, a.dx_pitch);
+                  a.dy_pitch, a.x_pitch, a.dx_pitch, nullptr, \
+                  int64_t(0));
   RMSNORM_BWD_LONG_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t add_long_fwd_launch<kF32>(int ch, int64_t grid, const AddFwdArgs& a, hipStream_t s) {
+#define RMSNORM_X(C)                                                                        \
+  if (ch == C)                                                                              \
+    return launch(fwd_fast_kernel<kF32, C, 8, 512, true, true, 1, true>, grid, 512, 0, s, a.x,  \
+                  a.gamma, a.y, a.rstd, a.M, a.N, a.eps, a.offset, a.x_pitch, a.y_pitch,    \
+                  a.res, a.h, a.res_pitch, a.h_pitch);
+  RMSNORM_ADD_LONG_LIST(RMSNORM_X)
+#undef RMSNORM_X
+  return hipErrorInvalidValue;
+}
+
+template <>
+hipError_t add_long_bwd_launch<kF32>(int ch, int64_t P, int64_t lds, const AddBwdArgs& a,
+                                    hipStream_t s) {
+#define RMSNORM_X(C)                                                                        \
+  if (ch == C) {                                                                            \
+    if (a.dh)                                                                               \
+      return launch(bwd_longrow_kernel<kF32, C, true, true>, P, 512, static_cast<size_t>(lds), \
+                    s, a.dy, a.h, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, P,     \
+                    a.dy_pitch, a.h_pitch, a.dx_pitch, a.dh, a.dh_pitch);                   \
+    return launch(bwd_longrow_kernel<kF32, C, true, false>, P, 512, static_cast<size_t>(lds),  \
+                  s, a.dy, a.h, a.gamma, a.rstd, a.dx, a.part, a.M, a.N, a.offset, P,       \
+                  a.dy_pitch, a.h_pitch, a.dx_pitch, nullptr, int64_t(0));                  \
+  }
+  RMSNORM_ADD_LONG_LIST(RMSNORM_X)
 #undef RMSNORM_X
   return hipErrorInvalidValue;
 }

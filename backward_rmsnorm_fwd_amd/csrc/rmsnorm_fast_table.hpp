@@ -7,6 +7,9 @@
 // Pipelined forward entries:  X(WPR, CH, BLOCK, XL)
 // Pipelined backward entries: X(WPR, CH, BLOCK, DLDS)
 // Long-row backward entries: X(CH), 512 threads per row
+// Fused-add long-row entries: X(CH), 8 wavefronts of a 512-thread workgroup
+//   per row in both directions (the forward with the weight in registers),
+//   for rows of 16 KiB to 128 KiB
 //   WPR  wavefronts per row, CH 16-byte chunks per thread and row,
 //   BLOCK threads per workgroup, GREG weight held in registers across rows,
 //   XLDS / XL x staged in LDS by DMA, DLDS dy staged in LDS too.  The
@@ -36,3 +39,6 @@
 
 #define RMSNORM_BWD_LONG_LIST(X) \
   X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+
+#define RMSNORM_ADD_LONG_LIST(X) \
+  X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)

@@ -188,6 +188,17 @@ struct AddBwdArgs {
 
 hipError_t add_fwd_launch(int dtype, const LnPlan& p, const AddFwdArgs& a, hipStream_t s);
 hipError_t add_bwd_launch(int dtype, const LnPlan& p, const AddBwdArgs& a, hipStream_t s);
+
+// The fused add on RMSNorm's long-row kernels (rmsnorm_fast.hpp, listed in
+// RMSNORM_ADD_LONG_LIST), for full-width rows of 16 KiB to 128 KiB: the
+// forward fwd_fast_kernel with ADD (grid workgroups of 512 threads, one row
+// each at a time), the backward bwd_longrow_kernel on h with dh (P
+// workgroups, `lds` bytes for a row of h).
+template <int DT>
+hipError_t add_long_fwd_launch(int ch, int64_t grid, const AddFwdArgs& a, hipStream_t s);
+template <int DT>
+hipError_t add_long_bwd_launch(int ch, int64_t P, int64_t lds, const AddBwdArgs& a,
+                               hipStream_t s);
 hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
 
 // RMSNorm with its output cast to a narrower dtype (fused_cast.hip): float32

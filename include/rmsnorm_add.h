@@ -46,6 +46,11 @@ extern "C" {
  * kernel reads h back; the backward's apply kernel adds dh. */
 #define RMSNORM_KERNEL_ADD_FWD_SPLIT 23 /* forward, three kernels */
 #define RMSNORM_KERNEL_ADD_BWD_SPLIT 24 /* backward stage 1, three kernels */
+/* Full-width rows of 16 to 128 KiB over RMSNORM_ADD_RESIDENT_MAX_N: one
+ * 512-thread workgroup per row at a time, as RMSNorm's long rows; the
+ * backward keeps a row of h in LDS. */
+#define RMSNORM_KERNEL_ADD_FWD_LONG 27 /* forward, the row in registers */
+#define RMSNORM_KERNEL_ADD_BWD_LONG 28 /* backward stage 1, h in LDS, dy in registers */
 
 /*
  * Forward.

@@ -112,27 +112,53 @@ def _ceil(a, b):
     return -(-a // b)
 
 
+def _long(N, es, align=16):
+    """Full-width rows of 16 to 128 KiB over 16384 elements (RMSNorm's
+    long-row range: 5 to 16 chunks of 8 KiB per 512-thread row)."""
+    vec = 16 // es
+    return N > 16384 and align >= 16 and N % vec == 0 and 5 <= _ceil(N // vec, 512) <= 16
+
+
 @pytest.mark.parametrize("M,N,dt", [(33, 16385, 2), (5, 16386, 1), (7, 16388, 0),
                                     (2, 1 << 24, 2), (2048, 65536, 2), (100000, 20000, 1),
-                                    (4096, 65537, 0)])
-def test_split_plan(M, N, dt):
-    """Rows over the row-resident limit take RMSNorm's split geometry (16 KiB
-    segments, the same P, a workspace of [P, N] partials, per-(row, segment)
-    sums and per-row coefficients)."""
+                                    (4096, 65537, 0), (700, 16400, 2), (9, 32768, 0),
+                                    (9, 40000, 0)])
+def test_long_and_split_plans(M, N, dt):
+    """Rows over the row-resident limit: full-width rows of up to 128 KiB
+    take RMSNorm's long-row kernels (one 512-thread workgroup per row, P =
+    min(M, 256)); other rows, and those under a narrower alignment, take
+    RMSNorm's split geometry on the same P.  The workspace has the split
+    layout ([P, N] partials, per-(row, segment) sums, per-row
+    coefficients) either way."""
     es = 4 if dt == 0 else 2
     nseg = _ceil(N * es, 16384)
-    f = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_FWD)
-    b = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
-    assert f["kernel_name"] == "add_fwd_split" and b["kernel_name"] == "add_bwd_split"
-    for p in (f, b):
-        assert p["segments"] == nseg and p["block_threads"] == 256
-        assert p["chunks"] * p["vec"] * es == 64 and p["grid"] % nseg == 0
-    P = b["partials"]
-    assert P == max(1, min(M, max(_ceil(M, 16), _ceil(1024, nseg)), ((1 << 24) - 1) // nseg))
-    assert f["grid"] // nseg == max(1, min(M, _ceil(2048, nseg), ((1 << 24) - 1) // nseg))
+    long_rows = _long(N, es)
+    P = min(M, 256) if long_rows else \
+        max(1, min(M, max(_ceil(M, 16), _ceil(1024, nseg)), ((1 << 24) - 1) // nseg))
+    for align in (16, 8, 4, 2):
+        if es == 4 and align < 4:
+            continue
+        f = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_FWD, align_bytes=align)
+        b = rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS, align_bytes=align)
+        assert b["partials"] == P
+        if _long(N, es, align):
+            assert f["kernel_name"] == "add_fwd_long" and b["kernel_name"] == "add_bwd_long"
+            ch = _ceil(N // (16 // es), 512)
+            for p in (f, b):
+                assert (p["threads_per_row"], p["block_threads"], p["chunks"]) == (512, 512, ch)
+            assert b["grid"] == P and b["lds_bytes"] == N * es
+            assert f["grid"] == min(M, 1 << 20)
+        else:
+            assert f["kernel_name"] == "add_fwd_split" and b["kernel_name"] == "add_bwd_split"
+            for p in (f, b):
+                assert p["segments"] == nseg and p["block_threads"] == 256
+                assert p["chunks"] * p["vec"] * es == 64 and p["grid"] % nseg == 0
+            assert b["grid"] == P * nseg
+            assert f["grid"] // nseg == max(1, min(M, _ceil(2048, nseg),
+                                                   ((1 << 24) - 1) // nseg))
     r4 = lambda v: _ceil(v, 4) * 4  # noqa: E731
     assert rn.rmsnorm_add_bwd_workspace_bytes(M, N, dt) == 4 * (r4(P * N) + r4(M * nseg) + r4(M))
     assert rn.rmsnorm_add_query_plan(M, N, dt, which=rn.PASS_BWD_REDUCE)["partials"] == P
-    if N > 65536:
+    if long_rows and N <= 65536:
         r = rn.rmsnorm_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
-        assert (r["grid"], r["partials"]) == (b["grid"], P)
+        assert r["kernel_name"] == "bwd_long" and r["partials"] == P

@@ -2,7 +2,8 @@
 ABI (include/rmsnorm_add.h), against the fused oracle (oracle.fused): h
 bitwise equal to the dtype's add, y, rstd, dx (RMSNorm's gradient plus dh)
 and dgamma through the gate, at reduced sizes of each recipe, tile and edge
-shapes, rows longer than the row-resident limit (the split-row plan),
+shapes, rows longer than the row-resident limit (full-width rows of up to
+128 KiB on the long-row kernels, other layouts on the split-row plan),
 misaligned and strided layouts, without dh, c2 at full size on every
 element and c3, c4, c5 at full size on sampled rows and columns."""
 import pytest
