@@ -57,7 +57,7 @@ RMSNORM_ADD_RESIDENT_MAX_N = 16384
 RMSNORM_CAST_MAX_N = 1 << 24
 RMSNORM_CAST_RESIDENT_MAX_N = 16384
 MAX_N = 1 << 24  # RMSNORM_MAX_N: rows longer than 65536 take the split-row plan
-NOALLOC_SCRATCH_BYTES = 64 << 20  # RMSNORM_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 72 << 20  # RMSNORM_NOALLOC_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_reduce",

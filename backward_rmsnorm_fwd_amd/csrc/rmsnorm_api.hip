@@ -330,6 +330,17 @@ constexpr int64_t kMaxSplitGrid = (int64_t(1) << 24) - 1;
 
 bool split_rows(int64_t N) { return N > kMaxRowN; }
 
+// Rows the generic kernels would otherwise take (no full-width kernel at
+// this alignment: odd N, narrow alignment, or float32 rows over 128 KiB)
+// run the split plan too once they are longer than kGenericSplitMinN.
+// Measured per kernel on one MI355X (generic -> split, us): fp32
+// 2048 x 65536 backward 906 -> 516; fp32 4096 x 40000 backward 836 -> 595;
+// bf16 2048 x 65535 (2-byte accesses) forward 992 -> 416, backward
+// 2802 -> 1040; fp16 8192 x 20001 backward 10865 -> 1313.  Full-width rows
+// keep their kernels: bf16 2048 x 40000 forward 53 against 83, backward
+// 109 against 142 split.
+constexpr int64_t kGenericSplitMinN = 16384;
+
 int64_t split_nseg(int64_t N, int es) { return ceil_div(N, split_segment_elems(es)); }
 
 int64_t split_partials(int64_t M, int64_t N, int es, bool backward) {
@@ -361,9 +372,22 @@ SplitWorkspace split_workspace(int64_t M, int64_t N, int es) {
   return split_workspace_for(split_partials(M, N, es, true), M, N, es);
 }
 
+// Whether a full-width kernel takes rows of N at access width vec.
+bool full_width_plan(int64_t N, int es, int vec, bool backward) {
+  if (vec * es != 16 || N > kMaxRowN) return false;
+  const int64_t nvec = N / vec;
+  if (backward) return plan_pipe_bwd(nvec).ok || plan_long_bwd(nvec) || plan_fast_bwd(nvec).ok;
+  return plan_pipe_fwd(nvec).ok || plan_fast_fwd(nvec).ok;
+}
+
+bool use_split(int64_t N, int es, int vec, bool backward) {
+  return split_rows(N) || (N > kGenericSplitMinN && !full_width_plan(N, es, vec, backward));
+}
+
 // Backward workgroup count P: a function of (M, N, dtype) only, computed
 // with the vector width that N alone allows (pointer alignment can only
-// change which kernel runs, never P).
+// change which kernel runs, never P; a layout narrower than that runs the
+// split or generic kernels on the same P).
 int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
   if (M <= 0) return 0;
   const int es = elem_bytes(dtype);
@@ -376,7 +400,16 @@ int64_t bwd_partials(int64_t M, int64_t N, int dtype) {
     const Cfg c = plan_fast_bwd(N / vec);
     if (c.ok) return fast_bwd_partials(M, c);
   }
+  if (N > kGenericSplitMinN) return split_partials(M, N, es, true);
   return generic_bwd_partials(M, N, vec);
+}
+
+// Backward workspace: [P, N] partials, and past kGenericSplitMinN (where a
+// layout may run the split kernels) the split plan's row sums after them.
+int64_t bwd_workspace_floats(int64_t M, int64_t N, int dtype) {
+  const int64_t P = bwd_partials(M, N, dtype);
+  if (N > kGenericSplitMinN) return split_workspace_for(P, M, N, elem_bytes(dtype)).total_floats;
+  return P * N;
 }
 
 // Stage 2 over a [P, N] block of partial column sums.
@@ -410,7 +443,7 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
     return;
   }
   p->vec = vec;
-  if (split_rows(N)) {
+  if (use_split(N, es, vec, pass == RMSNORM_PASS_BWD_ROWS)) {
     const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
     const int64_t nseg = split_nseg(N, es);
     p->kernel = bwd ? RMSNORM_KERNEL_BWD_SPLIT : RMSNORM_KERNEL_FWD_SPLIT;
@@ -419,7 +452,7 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
     p->chunks = split_chunks(vec, es);
     p->block_threads = 256;
     p->weight_in_regs = 1;
-    const int64_t P = split_partials(M, N, es, bwd);
+    const int64_t P = bwd ? bwd_partials(M, N, dtype) : split_partials(M, N, es, false);
     p->partials = bwd ? P : 0;
     p->grid = P * nseg;
     return;
@@ -858,7 +891,7 @@ int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, co
     const FastBwdArgs a{dy, x, gamma, rstd, dx, part, M, n, off, p.partials,
                         lddy * es, ldx * es, lddx * es};
     const SplitPlan sp{p.vec, p.segments, p.partials};
-    const SplitWorkspace w = split_workspace(M, N, es);
+    const SplitWorkspace w = split_workspace_for(p.partials, M, N, es);
     return status_of(split_bwd_launch(dtype, sp, a, part + w.dotp_offset, part + w.coef_offset,
                                       stream));
   }
@@ -1620,9 +1653,9 @@ const char* rmsnorm_status_string(int status) {
     case RMSNORM_ERR_NULL_POINTER: return "a required pointer is NULL";
     case RMSNORM_ERR_DTYPE: return "unsupported dtype (fp32, fp16 and bf16 are supported)";
     case RMSNORM_ERR_SHAPE:
-      return "unsupported shape (need 0 <= M <= 2^40 and, for rmsnorm_*, 1 <= N <= 2^24 with "
-             "M*N <= 2^46; for layernorm_*, rmsnorm_add_* and rmsnorm_cast_*, 1 <= N <= 16384), "
-             "or a buffer ending past byte address 2^57";
+      return "unsupported shape (need 0 <= M <= 2^40, 1 <= N <= 2^24 and M*N <= 2^46, for "
+             "rmsnorm_*, layernorm_*, rmsnorm_add_* and rmsnorm_cast_* alike), or a buffer "
+             "ending past byte address 2^57";
     case RMSNORM_ERR_EPS: return "eps must be finite and positive";
     case RMSNORM_ERR_FLAGS: return "unknown flag bits";
     case RMSNORM_ERR_WORKSPACE:
@@ -1654,8 +1687,7 @@ int rmsnorm_query_plan(int64_t M, int64_t N, rmsnorm_dtype_t dtype, uint32_t fla
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                                    uint32_t flags) {
   if (check_common(M, N, dtype, flags) != RMSNORM_OK || M == 0) return 0;
-  if (split_rows(N)) return static_cast<size_t>(split_workspace(M, N, elem_bytes(dtype)).total_floats * 4);
-  return static_cast<size_t>(bwd_partials(M, N, dtype) * N * 4);
+  return static_cast<size_t>(bwd_workspace_floats(M, N, dtype) * 4);
 }
 
 int rmsnorm_fwd(const void* x, const void* gamma, float eps, int64_t M, int64_t N,

@@ -215,7 +215,7 @@ int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x,
  * of rmsnorm_bwd, whose kernels and plan it uses (dx and dgamma are bitwise
  * identical to rmsnorm_bwd's), except that the dgamma partial sums go to a
  * buffer the library holds in device memory: RMSNORM_NOALLOC_SCRATCH_BYTES
- * (64 MiB) on each device the library runs on, reserved when the library's
+ * (72 MiB) on each device the library runs on, reserved when the library's
  * code is loaded on that device and held until the process ends.  The call
  * allocates nothing; the first call with a device current looks up that
  * device's buffer.
@@ -230,7 +230,7 @@ int rmsnorm_bwd_strided(const void* dy, int64_t lddy, const void* x,
  * Errors: as rmsnorm_bwd (WORKSPACE as above), and LAUNCH when the buffer's
  * device address cannot be obtained.
  */
-#define RMSNORM_NOALLOC_SCRATCH_BYTES (((size_t)64) << 20)
+#define RMSNORM_NOALLOC_SCRATCH_BYTES (((size_t)72) << 20)
 int rmsnorm_bwd_noalloc(const void* dy, const void* x, const void* gamma,
                         const float* rstd, int64_t M, int64_t N,
                         rmsnorm_dtype_t dtype, uint32_t flags, void* dx,

@@ -132,9 +132,9 @@ void plain_rejections() {
   {
     // The allocation-free backward: the need above its fixed buffer, and
     // caller arguments, are refused before the buffer is looked up.
-    const uint64_t big = uint64_t(8) << 26;
+    const uint64_t big = uint64_t(32) << 26;
     expect("bwd_noalloc beyond its buffer",
-           rmsnorm_bwd_noalloc(at(A), at(A + big), at(A + 2 * big), fat(A + 3 * big), 8,
+           rmsnorm_bwd_noalloc(at(A), at(A + big), at(A + 2 * big), fat(A + 3 * big), 32,
                                RMSNORM_MAX_N, RMSNORM_F32, 0, at(A + 4 * big), at(A + 5 * big),
                                nullptr),
            RMSNORM_ERR_WORKSPACE);

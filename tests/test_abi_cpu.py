@@ -222,10 +222,11 @@ def test_bwd_noalloc_rejects():
     def call(dy=A, x=A + S, g=A + 2 * S, r=A + 3 * S, M=4, N=256, dtype=2, flags=0,
              dx=A + 4 * S, dg=A + 5 * S):
         return L.rmsnorm_bwd_noalloc(dy, x, g, r, M, N, dtype, flags, dx, dg, None)
-    # 8 rows of 2^24 float32 need 64 MiB + the split plan's row sums: too big
-    assert L.rmsnorm_bwd_workspace_bytes(8, 1 << 24, 0, 0) > rn.NOALLOC_SCRATCH_BYTES
-    big = 8 << 26
-    assert call(dy=A, x=A + big, g=A + 2 * big, r=A + 3 * big, M=8, N=1 << 24, dtype=0,
+    # 32 rows of 2^24 float32 need two 64 MiB partial rows + the split
+    # plan's row sums: too big
+    assert L.rmsnorm_bwd_workspace_bytes(32, 1 << 24, 0, 0) > rn.NOALLOC_SCRATCH_BYTES
+    big = 32 << 26
+    assert call(dy=A, x=A + big, g=A + 2 * big, r=A + 3 * big, M=32, N=1 << 24, dtype=0,
                 dx=A + 4 * big, dg=A + 5 * big) == EWS
     assert call(dtype=5) == EDTYPE and call(flags=8) == EFLAGS and call(N=0) == ESHAPE
     assert call(dy=None) == ENULL and call(dg=None) == ENULL and call(r=None) == ENULL
@@ -238,7 +239,7 @@ def test_bwd_noalloc_rejects():
 
 def test_shape_status_string_names_each_family_limit():
     s = rn.rmsnorm_status_string(-3)
-    assert "2^24" in s and "16384" in s and "layernorm_" in s
+    assert "2^24" in s and "2^46" in s and "layernorm_" in s and "rmsnorm_cast_" in s
 
 
 def test_stride_status_string():
@@ -250,11 +251,20 @@ def test_workspace_bytes():
     assert L.rmsnorm_bwd_workspace_bytes(0, 4096, 2, 0) == 0
     assert L.rmsnorm_bwd_workspace_bytes(4, 0, 2, 0) == 0      # invalid -> 0
     assert L.rmsnorm_bwd_workspace_bytes(4, 4096, 9, 0) == 0   # invalid -> 0
+    r4 = lambda v: -(-v // 4) * 4  # noqa: E731
     for (m, n, dt) in [(32768, 4096, 2), (262144, 1024, 1), (2048, 65536, 2),
-                       (65536, 5120, 2), (65, 128, 0), (1, 2, 0)]:
+                       (65536, 5120, 2), (65, 128, 0), (1, 2, 0), (16, 16384, 0),
+                       (2048, 65535, 2), (4096, 20000, 0)]:
         p = rn.rmsnorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)
         ws = L.rmsnorm_bwd_workspace_bytes(m, n, dt, 0)
-        assert ws == p["partials"] * n * 4
+        if n <= 16384:
+            assert ws == p["partials"] * n * 4
+        else:
+            # past 16384 any layout may run the split kernels, so the
+            # workspace also holds their per-(row, segment) sums and
+            # per-row coefficients
+            nseg = -(-n * (4 if dt == 0 else 2) // 16384)
+            assert ws == 4 * (r4(p["partials"] * n) + r4(m * nseg) + r4(m))
         assert 1 <= p["partials"] <= m
         # the workspace is far below the page's M x N float32 partial array
         assert ws <= m * n * 4
@@ -308,7 +318,7 @@ def test_partials_do_not_depend_on_alignment():
 
 def test_full_width_plan_used_for_aligned_rows():
     """Every N whose rows are 16-byte multiples gets a listed full-width
-    kernel, except float32 rows beyond 32768 in the backward (generic)."""
+    kernel, except float32 rows beyond 32768 in the backward (split rows)."""
     for dt, es in ((0, 4), (1, 2), (2, 2)):
         vec = 16 // es
         for n in range(vec, 65537, vec * 7):
@@ -317,7 +327,7 @@ def test_full_width_plan_used_for_aligned_rows():
             assert (f["kernel_name"] == "fwd_pipe") == (4096 < n * es <= 8192), (dt, n)
             b = rn.rmsnorm_query_plan(5, n, dt, which=rn.PASS_BWD_ROWS)
             if dt == 0 and n > 32768:
-                assert b["kernel_name"] in ("bwd_wave", "bwd_block"), (dt, n)
+                assert b["kernel_name"] == "bwd_split", (dt, n)
             else:
                 assert b["kernel_name"] in ("bwd_rows", "bwd_pipe", "bwd_long"), (dt, n)
                 pipe = n * es <= 4096 or 8192 < n * es <= 16384
@@ -336,9 +346,14 @@ def test_plan_covers_every_n():
                     if dt == 0 and align < 4:
                         continue
                     p = rn.rmsnorm_query_plan(7, n, dt, which=which, align_bytes=align)
+                    assert n % p["vec"] == 0
+                    if p["kernel_name"].endswith("_split"):
+                        # rows over 16384 that no full-width kernel takes
+                        seg = 256 * p["chunks"] * p["vec"]
+                        assert n > 16384 and p["segments"] * seg >= n > (p["segments"] - 1) * seg
+                        continue
                     assert p["threads_per_row"] * p["chunks"] * p["vec"] >= n
                     assert p["threads_per_row"] * (p["chunks"] - 1) * p["vec"] < n
-                    assert n % p["vec"] == 0
                     assert p["chunks"] <= 64 and p["block_threads"] <= 1024
                     assert p["lds_bytes"] <= 160 * 1024
 
@@ -402,6 +417,16 @@ def test_split_plan_covers_rows_and_scratch():
                 assert p["segments"] * seg >= n > (p["segments"] - 1) * seg
                 assert p["segments"] * (4 // es) <= n
     assert rn.rmsnorm_query_plan(3, 65536, 2, which=rn.PASS_FWD)["kernel_name"] != "fwd_split"
+    # rows over 16384 that no full-width kernel takes run the split kernels
+    # too: odd N, narrow alignment, float32 backward rows over 128 KiB
+    for (n, dt, align, which) in [(65535, 2, 16, rn.PASS_FWD), (20001, 1, 16, rn.PASS_BWD_ROWS),
+                                  (40000, 2, 4, rn.PASS_FWD), (65536, 0, 16, rn.PASS_BWD_ROWS),
+                                  (40000, 0, 16, rn.PASS_BWD_ROWS)]:
+        p = rn.rmsnorm_query_plan(3, n, dt, which=which, align_bytes=align)
+        assert p["kernel_name"].endswith("_split"), (n, dt, align)
+    for (n, dt, align) in [(16383, 2, 16), (16384, 0, 4), (4097, 1, 16)]:
+        p = rn.rmsnorm_query_plan(3, n, dt, which=rn.PASS_BWD_ROWS, align_bytes=align)
+        assert p["kernel_name"] in ("bwd_wave", "bwd_block"), (n, dt, align)
     with pytest.raises(rn.RmsnormError):
         rn.rmsnorm_query_plan(3, (1 << 24) + 1, 2)
 

@@ -307,10 +307,43 @@ def test_m_zero(cuda):
     assert torch.equal(dg.cpu(), torch.zeros(64))
 
 
+# Rows over 16384 elements that no full-width kernel takes (odd N, narrow
+# alignment, float32 backward rows over 128 KiB) run the split kernels;
+# several rows per row block, P set by the natural vector width.
+GENERIC_SPLIT = [((300, 20001), torch.float16, "bwd_split", "fwd_split"),
+                 ((40, 40000), torch.float32, "bwd_split", "fwd_rows"),
+                 ((64, 65535), torch.bfloat16, "bwd_split", "fwd_split")]
+
+
+@pytest.mark.parametrize("shape,dtype,bwd_kernel,fwd_kernel", GENERIC_SPLIT)
+def test_generic_long_rows_take_split(cuda, shape, dtype, bwd_kernel, fwd_kernel):
+    M, N = shape
+    assert rn.rmsnorm_query_plan(M, N, dtype, which=rn.PASS_BWD_ROWS)["kernel_name"] == bwd_kernel
+    assert rn.rmsnorm_query_plan(M, N, dtype, which=rn.PASS_FWD)["kernel_name"] == fwd_kernel
+    inp = workloads.make_tile_case(shape, dtype, 19)
+    log(f"case generic long rows {shape} {dtype}")
+    assert_pass(gate_full(inp, run_target(inp, cuda)), f"generic long rows {shape} {dtype}")
+
+
+def test_full_size_sampled_fp32_long_rows(cuda):
+    """c4's recipe in float32 (2048 x 65536: 256 KiB rows, the split
+    backward), sampled rows and dgamma columns."""
+    inp = workloads.make_inputs("c4", dtype=torch.float32)
+    log("case c4 recipe in float32 full size generated")
+    out = run_target(inp, cuda)
+    log("case c4 float32 device run done")
+    rows = sample_rows(inp, 256)
+    cols = sample_cols(inp["N"], 64)
+    assert_pass(gate_sampled(inp, out, rows, cols), "c4 float32 full size, sampled")
+    for k in ("y", "dx", "rstd", "dgamma"):
+        assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_misaligned_pointers(cuda, dtype):
-    """Buffers starting one element past an aligned address: narrower vectors."""
-    M, N = 33, 4096
+@pytest.mark.parametrize("M,N", [(33, 4096), (9, 40000)])
+def test_misaligned_pointers(cuda, dtype, M, N):
+    """Buffers starting one element past an aligned address: narrower vectors
+    (generic kernels, or the split kernels for rows over 16384)."""
     inp = workloads.make_inputs("c2", M=M, N=N, dtype=dtype)
 
     def shifted(t):

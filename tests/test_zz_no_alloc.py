@@ -17,7 +17,8 @@ from parity import assert_pass, gate_full, log
 pytestmark = pytest.mark.gpu
 
 # (name, M, N, dtype, offset, seed): the first of each pair needs more partial
-# sums than the second.  2048 x 65536 bf16 fills the 64 MiB buffer exactly.
+# sums than the second.  2048 x 65536 bf16 needs 64 MiB of partial sums plus
+# the split plan's row sums (any layout of rows over 16384 may run them).
 PAIRS = [
     (("c4", 2048, 65536, torch.bfloat16, False, 1), ("c1a", None, None, None, None, None)),
     (("c2", 32768, 4096, torch.bfloat16, False, 2), ("tile", 513, 5120, torch.bfloat16, True, 3)),
@@ -69,9 +70,10 @@ def test_noalloc_matches_workspace_entry_point(cuda, big, small):
 
 
 def test_noalloc_rejects_shapes_beyond_its_buffer(cuda):
-    # 8 rows of 2^24 float32 need 64 MiB plus the split plan's row sums:
-    # more than the buffer, so the call is refused before anything runs.
-    M, N = 8, 1 << 24
+    # 32 rows of 2^24 float32 need two partial rows of 64 MiB plus the split
+    # plan's row sums: more than the buffer, so the call is refused before
+    # anything runs.
+    M, N = 32, 1 << 24
     assert rn.rmsnorm_bwd_workspace_bytes(M, N, torch.float32) > rn.NOALLOC_SCRATCH_BYTES
     x = torch.zeros((M, N), device=cuda)
     dy, dx = torch.zeros_like(x), torch.zeros_like(x)
