@@ -58,7 +58,10 @@ constexpr int kLnWaves = kRowWaves;
 
 // BLK: 256 for 256-thread workgroups (at least 3 wavefronts per SIMD, up to
 // 168 VGPRs), else 1024 (512- and 1024-thread workgroups, 128 VGPRs).
-template <int DT, int VEC, int MAXC, int BLK>
+// WREG keeps gamma and beta in registers across rows; without it (rows of
+// more than four 16-byte chunks per lane, up to 64 KiB of bf16 or 128 KiB
+// of float32) they are read from cache at each use.
+template <int DT, int VEC, int MAXC, int BLK, bool WREG = true>
 __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
     const void* __restrict__ x, const void* __restrict__ gamma, const void* __restrict__ beta,
     void* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd, int64_t M, int N,
@@ -70,15 +73,17 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
   const RowGeom rg = row_geom(wpr);
   const float n_f = static_cast<float>(N);
   int parity = 0;
-  PK g[MAXC], b[MAXC];
+  PK g[WREG ? MAXC : 1], b[WREG ? MAXC : 1];
+  if constexpr (WREG) {
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int e = (c * rg.tpr + rg.t) * VEC;
-    g[c].zero();
-    b[c].zero();
-    if (c < chunks && e < N) {
-      ld<DT, VEC, false>(g[c], static_cast<const char*>(gamma), e);
-      if (beta) ld<DT, VEC, false>(b[c], static_cast<const char*>(beta), e);
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = (c * rg.tpr + rg.t) * VEC;
+      g[c].zero();
+      b[c].zero();
+      if (c < chunks && e < N) {
+        ld<DT, VEC, false>(g[c], static_cast<const char*>(gamma), e);
+        if (beta) ld<DT, VEC, false>(b[c], static_cast<const char*>(beta), e);
+      }
     }
   }
   // ok[c]: this lane's vector of chunk c lies inside the row.
@@ -88,10 +93,12 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
   const int64_t step = static_cast<int64_t>(rg.G) * R;
   for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * step; row0 < M;
        row0 += static_cast<int64_t>(gridDim.x) * step) {
+    if constexpr (WREG) {
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      g[c].opaque();
-      b[c].opaque();
+      for (int c = 0; c < MAXC; ++c) {
+        g[c].opaque();
+        b[c].opaque();
+      }
     }
     // The loads carry no lane condition (a row past the matrix reads its
     // last row, a lane past the row reads the row's first vector); the
@@ -126,6 +133,13 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
 #pragma unroll
           for (int k = 0; k < h; ++k) v[k] += v[k + h];
         cs[c] = ok[c] ? v[0] : 0.0;
+        // Without the weights in registers the rows are long: widen one
+        // chunk at a time (no instruction crosses the fence) and from the
+        // packed registers again in each pass.
+        if constexpr (!WREG) {
+          xv[j][c].opaque();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #pragma unroll
       for (int h = MAXC / 2; h > 0; h /= 2)
@@ -150,6 +164,10 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
           qc = fmaf(d, d, qc);
         }
         q[j] += ok[c] ? qc : 0.f;
+        if constexpr (!WREG) {
+          xv[j][c].opaque();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     row_sums<0, R, R, R>(nullptr, q, slots64, slots, parity, wpr, rg);
@@ -169,12 +187,23 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void ln_fwd_kernel(
         if (!ok[c]) continue;
         const int e = (c * rg.tpr + rg.t) * VEC;
         float o[VEC];
+        if constexpr (WREG) {
 #pragma unroll
-        for (int k = 0; k < VEC; ++k)
-          o[k] = fmaf(fmaf(xv[j][c].get(k) - mu[j], r, ncr), g[c].get(k), b[c].get(k));
+          for (int k = 0; k < VEC; ++k)
+            o[k] = fmaf(fmaf(xv[j][c].get(k) - mu[j], r, ncr), g[c].get(k), b[c].get(k));
+        } else {
+          PK gv, bv;
+          ld<DT, VEC, false>(gv, static_cast<const char*>(gamma), e);
+          bv.zero();
+          if (beta) ld<DT, VEC, false>(bv, static_cast<const char*>(beta), e);
+#pragma unroll
+          for (int k = 0; k < VEC; ++k)
+            o[k] = fmaf(fmaf(xv[j][c].get(k) - mu[j], r, ncr), gv.get(k), bv.get(k));
+        }
         PK out;
         out.set(o);
         st<DT, VEC>(out, yr, e);
+        if constexpr (!WREG) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -426,6 +455,28 @@ hipError_t ln_bwd_dt(const LnPlan& p, const LnBwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Full-width rows of five to eight 16-byte chunks per lane over 16
+// wavefronts (bf16/fp16 N <= 65536, float32 N <= 32768): the weights are not
+// held in registers.
+template <int DT>
+hipError_t ln_fwd_long_dt(const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  constexpr int es = ElemBytes<DT>::value;
+  constexpr int VEC = 16 / es;
+  if (p.vec != VEC || p.block != 1024 || p.wpr != 16 || p.chunks > 8) return hipErrorInvalidValue;
+  return launch(ln_fwd_kernel<DT, VEC, 8, 1024, false>, p.grid, p.block, 0, s, a.x, a.gamma,
+                a.beta, a.y, a.mean, a.rstd, a.M, a.N, p.chunks, p.wpr, a.eps, a.x_pitch / es,
+                a.y_pitch / es);
+}
+
+hipError_t ln_fwd_long_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case kF32: return ln_fwd_long_dt<kF32>(p, a, s);
+    case kF16: return ln_fwd_long_dt<kF16>(p, a, s);
+    case kBF16: return ln_fwd_long_dt<kBF16>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s) {
   switch (dtype) {

@@ -139,6 +139,10 @@ struct LnBwdArgs {
 };
 
 hipError_t ln_fwd_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
+// The row-resident forward for full-width rows of up to 8 chunks per lane
+// over 16 wavefronts, the weights read from cache (rows past the 16384
+// elements of ln_fwd_launch's plans; bf16/fp16 N <= 65536, fp32 N <= 32768).
+hipError_t ln_fwd_long_launch(int dtype, const LnPlan& p, const LnFwdArgs& a, hipStream_t s);
 
 // LayerNorm split-row plan (layernorm_split.hip, rows over 16384 elements),
 // on the RMSNorm split geometry.  Forward: stats, finish, apply and head

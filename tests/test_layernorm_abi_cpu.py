@@ -155,6 +155,22 @@ def test_backward_exact_fit(dt, n, tpr, ch):
     assert (f["threads_per_row"], f["chunks"], f["block_threads"]) == (256, 3, 256)
 
 
+def _long_fwd(N, es, align=16):
+    """Full-width forward rows over 16384 of at most 8 chunks per lane over
+    16 wavefronts stay row-resident."""
+    vec = 16 // es
+    return N > 16384 and align >= 16 and N % vec == 0 and N // vec <= 8192
+
+
+def _check_long_fwd(f, M, N, es):
+    vec = 16 // es
+    ch = _ceil(N // vec, 1024)
+    assert f["kernel_name"] == "ln_fwd" and f["vec"] == vec
+    assert (f["threads_per_row"], f["block_threads"], f["chunks"]) == (1024, 1024, ch)
+    assert f["weight_in_regs"] == (1 if ch <= 4 else 0)
+    assert f["grid"] == min(M, 16384)
+
+
 @pytest.mark.parametrize("M,N,dt", [(33, 16385, 2), (5, 16386, 1), (7, 16388, 0),
                                     (2, 1 << 24, 2), (261, 98304, 2), (100000, 20000, 1),
                                     (1, 1 << 24, 0), (4096, 65537, 0), (8, 32768, 2)])
@@ -168,8 +184,12 @@ def test_split_plan(M, N, dt):
     nseg = _ceil(N * es, 16384)
     f = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_FWD)
     b = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_BWD_ROWS)
-    assert f["kernel_name"] == "ln_fwd_split" and b["kernel_name"] == "ln_bwd_split"
-    rf = rn.rmsnorm_query_plan(M, max(N, 65537), dt, which=rn.PASS_FWD)
+    assert b["kernel_name"] == "ln_bwd_split"
+    if _long_fwd(N, es):
+        _check_long_fwd(f, M, N, es)
+        f = rn.layernorm_query_plan(M, N, dt, which=rn.PASS_FWD, align_bytes=8)
+    assert f["kernel_name"] == "ln_fwd_split"
+    rf = rn.rmsnorm_query_plan(M, max(N, 65537), dt, which=rn.PASS_FWD, align_bytes=8)
     for p in (f, b):
         assert p["segments"] == nseg and p["block_threads"] == 256
         assert p["threads_per_row"] == 256 * nseg
@@ -205,6 +225,9 @@ def test_split_plan_boundary_and_row_room():
                 if es == 4 and align < 4:
                     continue
                 p = rn.layernorm_query_plan(3, n, dt, which=rn.PASS_FWD, align_bytes=align)
+                if _long_fwd(n, es, align):
+                    _check_long_fwd(p, 3, n, es)
+                    continue
                 seg = 256 * p["chunks"] * p["vec"]
                 assert p["kernel_name"] == "ln_fwd_split"
                 assert seg * es == 16384 and n % p["vec"] == 0
