@@ -547,8 +547,11 @@ hipError_t ln_split_bwd_vec(const SplitPlan& sp, const LnBwdArgs& a, float* sums
   constexpr int es = ElemBytes<DT>::value;
   const int64_t lddy = a.dy_pitch / es, ldx = a.x_pitch / es, lddx = a.dx_pitch / es;
   const int64_t grid = sp.P * sp.nseg;
-  hipError_t e = launch(ln_split_bwd_stats_kernel<DT, VEC>, grid, kSplitBlock, 0, s, a.dy, a.x,
-                        a.gamma, a.mean, sums, a.M, a.N, sp.nseg, sp.P, lddy, ldx);
+  // The stats pass keeps no column sums, so it may cut the rows finer than
+  // the apply pass (more workgroups in flight; its sums do not depend on it).
+  const int64_t Ps = sp.P_free > 0 ? sp.P_free : sp.P;
+  hipError_t e = launch(ln_split_bwd_stats_kernel<DT, VEC>, Ps * sp.nseg, kSplitBlock, 0, s, a.dy,
+                        a.x, a.gamma, a.mean, sums, a.M, a.N, sp.nseg, Ps, lddy, ldx);
   if (e != hipSuccess) return e;
   e = launch(ln_split_bwd_finish_kernel, (a.M + 255) / 256, 256, 0, s, sums, a.rstd, coef, a.M,
              a.N, sp.nseg);

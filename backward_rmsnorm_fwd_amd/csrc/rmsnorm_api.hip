@@ -352,6 +352,23 @@ int64_t split_partials(int64_t M, int64_t N, int es, bool backward) {
   return std::max<int64_t>(1, std::min(P, M));
 }
 
+// Row blocks of a split pass that keeps no column sums (every forward pass,
+// LayerNorm's backward stats pass, RMSNorm's backward apply pass): its
+// blocking is free, and one row per block keeps the most rows in flight.
+// Measured (us, blocks of the column-sum pass or of 2048 forward workgroups
+// -> one row per block): LayerNorm stage 1 bf16 2048 x 65536 251.6 -> 230.0,
+// bf16 1024 x 131072 261.0 -> 232.8, fp32 512 x 262144 494.0 -> 471.1;
+// RMSNorm stage 1 bf16 1024 x 131072 240.9 -> 230.6, fp32 512 x 262144
+// 516.2 -> 455.3, bf16 2048 x 65535 1050.6 -> 891.0; RMSNorm forward fp32
+// 512 x 262144 289.1 -> 260.1, bf16 2048 x 65535 417.7 -> 189.6, fp16
+// 8192 x 20001 579.4 -> 244.2.  Only with very few rows (fp16 8 x 2^24:
+// forward 289.7 -> 309.6, stage 1 385.3 -> 402.3) does the extra weight
+// traffic of the smaller blocks show.  LayerNorm's forward keeps its blocks
+// (bf16 1024 x 131072 145.1 against 193.5 us one row per block).
+int64_t split_free_partials(int64_t M, int64_t nseg) {
+  return std::max<int64_t>(1, std::min(M, kMaxSplitGrid / nseg));
+}
+
 // Backward workspace of the split plan: part[P, N], then the per-(row,
 // segment) dot partials [M, nseg], then the per-row coefficients [M], each
 // starting on a 16-byte boundary.
@@ -452,7 +469,7 @@ void fill_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_pla
     p->chunks = split_chunks(vec, es);
     p->block_threads = 256;
     p->weight_in_regs = 1;
-    const int64_t P = bwd ? bwd_partials(M, N, dtype) : split_partials(M, N, es, false);
+    const int64_t P = bwd ? bwd_partials(M, N, dtype) : split_free_partials(M, nseg);
     p->partials = bwd ? P : 0;
     p->grid = P * nseg;
     return;
@@ -890,7 +907,7 @@ int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, co
   if (p.kernel == RMSNORM_KERNEL_BWD_SPLIT) {
     const FastBwdArgs a{dy, x, gamma, rstd, dx, part, M, n, off, p.partials,
                         lddy * es, ldx * es, lddx * es};
-    const SplitPlan sp{p.vec, p.segments, p.partials};
+    const SplitPlan sp{p.vec, p.segments, p.partials, split_free_partials(M, p.segments)};
     const SplitWorkspace w = split_workspace_for(p.partials, M, N, es);
     return status_of(split_bwd_launch(dtype, sp, a, part + w.dotp_offset, part + w.coef_offset,
                                       stream));
@@ -1059,6 +1076,7 @@ LnPlan ln_long_fwd_plan(int64_t M, int64_t N, int vec) {
   return p;
 }
 
+
 LnSplitWorkspace ln_split_workspace(int64_t M, int64_t N, int es) {
   LnSplitWorkspace w;
   w.sums_offset = ceil_div(2 * split_partials(M, N, es, true) * N, 4) * 4;
@@ -1152,8 +1170,9 @@ int ln_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, con
   const LnBwdArgs a{dy, x, gamma, mean, rstd, dx, part, M, static_cast<int>(N), lddy * es,
                     ldx * es, lddx * es};
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
-                       split_partials(M, N, es, true)};
+    const int64_t nseg = split_nseg(N, es);
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(nseg),
+                       split_partials(M, N, es, true), split_free_partials(M, nseg)};
     const LnSplitWorkspace w = ln_split_workspace(M, N, es);
     return status_of(ln_split_bwd_launch(dtype, sp, a, part + w.sums_offset,
                                          part + w.coef_offset, stream));
@@ -1233,7 +1252,12 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
   if (ln_split_rows(N)) {
     const int64_t nseg = split_nseg(N, es);
     const int vec = pick_vec(N, es, align);
-    const int64_t P = split_partials(M, N, es, bwd);
+    // LayerNorm's forward passes keep their row blocks (its float64 stats
+    // pass measured slower one row per block); the RMSNorm kernels' forward
+    // takes one row per block.
+    const int64_t P = bwd ? split_partials(M, N, es, true)
+                          : (layernorm ? split_partials(M, N, es, false)
+                                       : split_free_partials(M, nseg));
     out->kernel = bwd ? LAYERNORM_KERNEL_BWD_SPLIT : LAYERNORM_KERNEL_FWD_SPLIT;
     out->vec = vec;
     out->segments = static_cast<int32_t>(nseg);
@@ -1363,8 +1387,8 @@ int add_fwd_impl(const void* x, int64_t ldx, const void* res, int64_t ldr, const
   if (const int ch = add_long_fwd_ch(N, es, align))
     return status_of(add_long_fwd(dtype, ch, add_long_fwd_grid(M), a, stream));
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)),
-                       split_partials(M, N, es, false)};
+    const int64_t nseg = split_nseg(N, es);
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(nseg), split_free_partials(M, nseg)};
     return status_of(add_split_fwd_launch(dtype, sp, a, stream));
   }
   const LnPlan p = ln_plan(M, N, es, false, align, kAddFwdMatrices);
@@ -1412,7 +1436,9 @@ int add_rows_launch(const void* dy, int64_t lddy, const void* dh, int64_t lddh, 
   if (const int ch = add_long_bwd_ch(N, es, align))
     return status_of(add_long_bwd(dtype, ch, P, N * es, a, stream));
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(split_nseg(N, es)), P};
+    const int64_t nseg = split_nseg(N, es);
+    const SplitPlan sp{pick_vec(N, es, align), static_cast<int>(nseg), P,
+                       split_free_partials(M, nseg)};
     const SplitWorkspace w = split_workspace_for(P, M, N, es);
     return status_of(add_split_bwd_launch(dtype, sp, a, part + w.dotp_offset,
                                           part + w.coef_offset, stream));
@@ -1536,8 +1562,9 @@ int cast_fwd_impl(const void* x, int64_t ldx, const void* gamma, float eps, int6
   const CastFwdArgs a{x, gamma, y, rstd, M, static_cast<int>(N), eps,
                       (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, ldx * kCastIn, ldy * eo};
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(split_nseg(N, kCastIn)),
-                       split_partials(M, N, kCastIn, false)};
+    const int64_t nseg = split_nseg(N, kCastIn);
+    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(nseg),
+                       split_free_partials(M, nseg)};
     return status_of(cast_split_fwd_launch(out_dtype, sp, a, stream));
   }
   const LnPlan p = ln_plan(M, N, kCastIn, false, align);
@@ -1582,8 +1609,9 @@ int cast_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                       (flags & RMSNORM_FLAG_OFFSET) ? 1 : 0, lddy * eo, ldx * kCastIn,
                       lddx * kCastIn};
   if (ln_split_rows(N)) {
-    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(split_nseg(N, kCastIn)),
-                       split_partials(M, N, kCastIn, true)};
+    const int64_t nseg = split_nseg(N, kCastIn);
+    const SplitPlan sp{pick_vec(N, kCastIn, align), static_cast<int>(nseg),
+                       split_partials(M, N, kCastIn, true), split_free_partials(M, nseg)};
     const SplitWorkspace w = split_workspace(M, N, kCastIn);
     return status_of(cast_split_bwd_launch(out_dtype, sp, a, part + w.dotp_offset,
                                            part + w.coef_offset, stream));

@@ -85,6 +85,9 @@ struct SplitPlan {
   int vec;
   int nseg;
   int64_t P;
+  // Row blocks of the backward pass that keeps no column sums (LayerNorm's
+  // stats pass, RMSNorm's apply pass); 0: P.
+  int64_t P_free = 0;
 };
 int split_segment_elems(int elem_bytes);
 int split_chunks(int vec, int elem_bytes);

@@ -402,8 +402,10 @@ hipError_t split_bwd_vec(const SplitPlan& sp, const SplitBwdIO& a, float* dotp, 
   e = launch(split_bwd_finish_kernel, (a.M + 255) / 256, 256, 0, s, dotp, a.rstd, coef,
              int64_t(0), a.M, a.N, sp.nseg);
   if (e != hipSuccess) return e;
-  return launch(split_bwd_apply_kernel<DX, DY, VEC, DH>, grid, kSplitBlock, 0, s, a.dy, a.x,
-                a.gamma, a.rstd, coef, a.dh, a.dx, a.M, a.N, sp.nseg, sp.P, a.offset, a.lddy,
+  // The apply pass keeps no column sums, so it may cut the rows finer.
+  const int64_t Pa = sp.P_free > 0 ? sp.P_free : sp.P;
+  return launch(split_bwd_apply_kernel<DX, DY, VEC, DH>, Pa * sp.nseg, kSplitBlock, 0, s, a.dy,
+                a.x, a.gamma, a.rstd, coef, a.dh, a.dx, a.M, a.N, sp.nseg, Pa, a.offset, a.lddy,
                 a.ldx, a.lddh, a.lddx);
 }
 
