@@ -15,10 +15,15 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in (
-    "rmsnorm_api.hip", "rmsnorm_fast_f32.hip", "rmsnorm_fast_f16.hip",
-    "rmsnorm_fast_bf16.hip", "rmsnorm_split.hip", "layernorm.hip", "layernorm_split.hip",
-    "fused_add.hip", "fused_cast.hip")]
+# Translation units: (source, extra hipcc arguments, object name).  The
+# full-width kernel instantiations compile once per dtype from one source.
+UNITS = [(os.path.join(CSRC, "rmsnorm_api.hip"), [], "rmsnorm_api.o")]
+UNITS += [(os.path.join(CSRC, "rmsnorm_fast_inst.hip"), [f"-DRMSNORM_INST_DT={dt}"],
+           f"rmsnorm_fast_inst_{dt}.o") for dt in ("kF32", "kF16", "kBF16")]
+UNITS += [(os.path.join(CSRC, f), [], f.replace(".hip", ".o")) for f in (
+    "rmsnorm_split.hip", "layernorm.hip", "layernorm_split.hip", "fused_add.hip",
+    "fused_cast.hip")]
+SOURCES = sorted({src for src, _, _ in UNITS})
 LIB = os.path.join(HERE, "librmsnorm.so")
 ARCH = "gfx950"
 
@@ -53,13 +58,13 @@ def build(verbose=False, resource_usage=False, jobs=None):
 
     Each translation unit compiles in its own hipcc process (in parallel);
     the objects are then linked into one shared library."""
-    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+    jobs = jobs or min(len(UNITS), max(1, os.cpu_count() or 1))
     inc = ["-I", os.path.join(ROOT, "include")]
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
     with tempfile.TemporaryDirectory(prefix="rmsnorm_build_") as tmp:
-        objs = [os.path.join(tmp, os.path.basename(src) + ".o") for src in SOURCES]
-        cmds = [[hipcc(), *FLAGS, *extra, *inc, "-c", src, "-o", obj]
-                for src, obj in zip(SOURCES, objs)]
+        objs = [os.path.join(tmp, name) for _, _, name in UNITS]
+        cmds = [[hipcc(), *FLAGS, *extra, *inc, *defs, "-c", src, "-o", obj]
+                for (src, defs, _), obj in zip(UNITS, objs)]
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             results = list(ex.map(lambda c: _run(c, verbose), cmds))
         logs = []

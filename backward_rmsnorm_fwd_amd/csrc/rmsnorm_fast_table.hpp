@@ -1,6 +1,6 @@
 // Instantiated full-width (16-byte vector) kernel configurations, shared by
 // the host plan (which may only pick a listed configuration) and by the
-// per-dtype translation units that instantiate them.
+// per-dtype objects of rmsnorm_fast_inst.hip that instantiate them.
 //
 // Forward entries:  X(WPR, CH, BLOCK, GREG)
 // Backward entries: X(WPR, CH, BLOCK, GREG, XLDS)

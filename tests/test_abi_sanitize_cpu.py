@@ -36,10 +36,10 @@ def test_host_validation_under_sanitizers(tmp_path):
     inc = ["-I", os.path.join(ROOT, "include")]
     common = [f"--offload-arch={lib_build.ARCH}", "-O1", "-g", "-std=c++17", *SAN, *inc]
     objs, cmds = [], []
-    for src in lib_build.SOURCES + [DRIVER]:
-        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+    for src, defs, name in lib_build.UNITS + [(DRIVER, [], "driver.o")]:
+        obj = str(tmp_path / name)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([hipcc, *common, *lang, "-c", src, "-o", obj])
+        cmds.append([hipcc, *common, *lang, *defs, "-c", src, "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         for rc, cmd, out in ex.map(_compile, cmds):
