@@ -49,7 +49,7 @@ KERNEL_NAMES = {1: "fwd_wave", 2: "fwd_block", 3: "bwd_wave", 4: "bwd_block",
                 16: "ln_bwd", 17: "add_fwd", 18: "add_bwd", 19: "cast_fwd", 20: "cast_bwd",
                 21: "ln_fwd_split", 22: "ln_bwd_split", 23: "add_fwd_split",
                 24: "add_bwd_split", 25: "cast_fwd_split", 26: "cast_bwd_split",
-                27: "add_fwd_long", 28: "add_bwd_long"}
+                27: "add_fwd_long", 28: "add_bwd_long", 29: "ln_bwd_rows"}
 LAYERNORM_MAX_N = 1 << 24
 LAYERNORM_RESIDENT_MAX_N = 16384
 RMSNORM_ADD_MAX_N = 1 << 24

@@ -21,7 +21,8 @@ UNITS = [(os.path.join(CSRC, "rmsnorm_api.hip"), [], "rmsnorm_api.o")]
 UNITS += [(os.path.join(CSRC, "rmsnorm_fast_inst.hip"), [f"-DRMSNORM_INST_DT={dt}"],
            f"rmsnorm_fast_inst_{dt}.o") for dt in ("kF32", "kF16", "kBF16")]
 UNITS += [(os.path.join(CSRC, f), [], f.replace(".hip", ".o")) for f in (
-    "rmsnorm_split.hip", "layernorm.hip", "layernorm_split.hip", "fused_add.hip",
+    "rmsnorm_split.hip", "layernorm.hip", "layernorm_rows.hip", "layernorm_split.hip",
+    "fused_add.hip",
     "fused_cast.hip")]
 SOURCES = sorted({src for src, _, _ in UNITS})
 LIB = os.path.join(HERE, "librmsnorm.so")

@@ -1052,6 +1052,38 @@ int64_t ln_partials(int64_t M, int64_t N, int es) {
   return ln_plan(M, N, es, true, 16).grid;
 }
 
+// LayerNorm backward rows of 4-8 KiB (257 to 512 16-byte vectors) take
+// layernorm_rows.hip's kernel, on RMSNorm's bwd_rows geometry: four
+// wavefronts x two chunks per row, two rows per 512-thread workgroup, x in
+// LDS, rows swept back to front, P = min(ceil(M/2), 512).  bf16 32768 x 4096
+// stage 1: see the LayerNorm notes.  A layout that is not 16-byte aligned
+// runs the row-resident kernel on the same P.
+constexpr int kLnRowsWpr = 4, kLnRowsChunks = 2, kLnRowsBlock = 512;
+constexpr int64_t kLnRowsWorkgroups = 512;
+
+bool ln_rows_fast(int64_t N, int es, int align) {
+  if (ln_split_rows(N)) return false;
+  const int vec = pick_vec(N, es, align);
+  if (vec * es != 16) return false;
+  const int64_t nvec = N / vec;
+  return nvec > 256 && nvec <= 512;
+}
+
+int64_t ln_rows_lds(int64_t N, int es) {
+  const int64_t groups = kLnRowsBlock / (kWave * kLnRowsWpr);
+  const int64_t sweep = int64_t(kWave) * kLnRowsWpr * (16 / es);
+  return std::max(groups * N * es, groups * sweep * 4);
+}
+
+// LayerNorm's P, a function of (M, N, dtype) only.
+int64_t layernorm_partials(int64_t M, int64_t N, int es) {
+  if (M > 0 && ln_rows_fast(N, es, 16)) {
+    const int64_t groups = kLnRowsBlock / (kWave * kLnRowsWpr);
+    return std::min(ceil_div(M, groups), kLnRowsWorkgroups);
+  }
+  return ln_partials(M, N, es);
+}
+
 struct LnSplitWorkspace {
   int64_t sums_offset, coef_offset, total_floats;  // in floats
 };
@@ -1132,7 +1164,7 @@ size_t ln_workspace_bytes(int64_t M, int64_t N, int dtype) {
   if (M <= 0) return 0;
   const int es = elem_bytes(dtype);
   if (ln_split_rows(N)) return static_cast<size_t>(ln_split_workspace(M, N, es).total_floats * 4);
-  return static_cast<size_t>(2 * ln_partials(M, N, es) * N * 4);
+  return static_cast<size_t>(2 * layernorm_partials(M, N, es) * N * 4);
 }
 
 // Stage-1 argument checks (dy, x, gamma, mean, rstd, dx, workspace).
@@ -1177,13 +1209,17 @@ int ln_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, con
     return status_of(ln_split_bwd_launch(dtype, sp, a, part + w.sums_offset,
                                          part + w.coef_offset, stream));
   }
-  const LnPlan p = ln_plan(M, N, es, true, align);
+  const int64_t P = layernorm_partials(M, N, es);
+  if (ln_rows_fast(N, es, align))
+    return status_of(ln_bwd_rows_launch(dtype, P, ln_rows_lds(N, es), a, stream));
+  LnPlan p = ln_plan(M, N, es, true, align);
+  p.grid = P;
   return status_of(ln_bwd_launch(dtype, p, a, stream));
 }
 
 int ln_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
                      uint32_t flags, void* dgamma, void* dbeta, hipStream_t stream) {
-  const int64_t P = ln_partials(M, N, elem_bytes(dtype));
+  const int64_t P = layernorm_partials(M, N, elem_bytes(dtype));
   const float* part = static_cast<const float*>(workspace);
   int st = reduce_columns(part, P, N, dtype, flags, dgamma, stream);
   if (st != RMSNORM_OK || !dbeta) return st;
@@ -1234,10 +1270,23 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
   std::memset(out, 0, sizeof(*out));
   const int es = elem_bytes(dtype);
   if (pass == RMSNORM_PASS_BWD_REDUCE) {
-    fill_reduce_plan(ln_partials(M, N, es), N, out);
+    fill_reduce_plan(layernorm ? layernorm_partials(M, N, es) : ln_partials(M, N, es), N, out);
     return;
   }
   const bool bwd = pass == RMSNORM_PASS_BWD_ROWS;
+  if (layernorm && bwd && ln_rows_fast(N, es, align)) {
+    out->kernel = LAYERNORM_KERNEL_BWD_ROWS;
+    out->vec = 16 / es;
+    out->threads_per_row = kWave * kLnRowsWpr;
+    out->block_threads = kLnRowsBlock;
+    out->chunks = kLnRowsChunks;
+    out->x_in_lds = 1;
+    out->weight_in_regs = 1;
+    out->partials = layernorm_partials(M, N, es);
+    out->grid = out->partials;
+    out->lds_bytes = ln_rows_lds(N, es);
+    return;
+  }
   if (layernorm && !bwd && ln_long_fwd(N, es, pick_vec(N, es, align))) {
     const LnPlan p = ln_long_fwd_plan(M, N, pick_vec(N, es, align));
     out->kernel = LAYERNORM_KERNEL_FWD;
@@ -1276,8 +1325,8 @@ void fill_ln_plan(int64_t M, int64_t N, int dtype, int pass, int align, rmsnorm_
   out->block_threads = p.block;
   out->chunks = p.chunks;
   out->weight_in_regs = 1;
-  out->grid = p.grid;
-  out->partials = bwd ? p.grid : 0;
+  out->grid = bwd && layernorm ? layernorm_partials(M, N, es) : p.grid;
+  out->partials = bwd ? out->grid : 0;
   out->lds_bytes = bwd ? p.lds : 0;
 }
 

@@ -207,6 +207,10 @@ template <int DT>
 hipError_t add_long_bwd_launch(int ch, int64_t P, int64_t lds, const AddBwdArgs& a,
                                hipStream_t s);
 hipError_t ln_bwd_launch(int dtype, const LnPlan& p, const LnBwdArgs& a, hipStream_t s);
+// Backward stage 1 for full-width rows of 4-8 KiB (layernorm_rows.hip):
+// grid P, 512 threads, `lds` bytes of dynamic LDS.
+hipError_t ln_bwd_rows_launch(int dtype, int64_t P, int64_t lds, const LnBwdArgs& a,
+                              hipStream_t s);
 
 // RMSNorm with its output cast to a narrower dtype (fused_cast.hip): float32
 // x, gamma and dx; y and dy in the output dtype.  Row-resident plan of

@@ -65,6 +65,12 @@ extern "C" {
  * the workspace. */
 #define LAYERNORM_KERNEL_FWD_SPLIT 21 /* forward, four kernels */
 #define LAYERNORM_KERNEL_BWD_SPLIT 22 /* backward stage 1, three kernels */
+/* Backward stage 1 for rows of 257 to 512 16-byte vectors (bf16/fp16
+ * 2048 < N <= 4096, float32 1024 < N <= 2048) when every pointer and row
+ * pitch is 16-byte aligned: two rows per 512-thread workgroup, x staged in
+ * LDS, P = min(ceil(M/2), 512).  Other layouts of the same N run
+ * LAYERNORM_KERNEL_BWD on the same P. */
+#define LAYERNORM_KERNEL_BWD_ROWS 29
 
 /*
  * Forward.

@@ -91,6 +91,13 @@ def _ceil(a, b):
     return -(-a // b)
 
 
+def _bwd_rows(n, es, align):
+    """Backward rows of 257 to 512 16-byte vectors with a 16-byte layout run
+    the two-rows-per-workgroup kernel with x in LDS."""
+    vec = 16 // es
+    return align >= 16 and n % vec == 0 and 256 < n // vec <= 512
+
+
 @pytest.mark.parametrize("dt", [0, 1, 2])
 def test_plans_cover_rows(dt):
     """Every N gets a plan whose lanes cover the row with no empty chunk,
@@ -108,19 +115,27 @@ def test_plans_cover_rows(dt):
                 for which, target in ((rn.PASS_FWD, lambda v: min(4, 32 // v)),
                                       (rn.PASS_BWD_ROWS, lambda v: min(8, 16 // v))):
                     p = rn.layernorm_query_plan(m, n, dt, which=which, align_bytes=align)
-                    assert p["kernel_name"] == ("ln_fwd" if which == rn.PASS_FWD else "ln_bwd")
                     vec, tpr, ch = p["vec"], p["threads_per_row"], p["chunks"]
                     assert n % vec == 0 and vec * es <= align
                     assert tpr * ch * vec >= n > tpr * (ch - 1) * vec
-                    assert p["block_threads"] == max(256, tpr) and 64 <= tpr <= 1024
-                    cap = max(target(vec), 16 // vec)
-                    assert ch <= cap
+                    rows = which == rn.PASS_BWD_ROWS and _bwd_rows(n, es, align)
+                    if rows:
+                        assert p["kernel_name"] == "ln_bwd_rows"
+                        assert (tpr, ch, p["block_threads"], p["x_in_lds"]) == (256, 2, 512, 1)
+                        assert p["lds_bytes"] == max(2 * n * es, 2 * tpr * vec * 4)
+                    else:
+                        assert p["kernel_name"] == ("ln_fwd" if which == rn.PASS_FWD
+                                                    else "ln_bwd")
+                        assert p["block_threads"] == max(256, tpr) and 64 <= tpr <= 1024
+                        cap = max(target(vec), 16 // vec)
+                        assert ch <= cap
                     if which == rn.PASS_BWD_ROWS:
                         if P is None:
                             P = p["partials"]
                         assert p["partials"] == P == p["grid"]
                         bt = p["block_threads"]
-                        assert p["lds_bytes"] == (0 if tpr == bt else bt * vec * 4)
+                        if not rows:
+                            assert p["lds_bytes"] == (0 if tpr == bt else bt * vec * 4)
             base = rn.layernorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)
             assert P == min(512, _ceil(m, base["block_threads"] // base["threads_per_row"]))
             assert rn.layernorm_bwd_workspace_bytes(m, n, dt) == 2 * P * n * 4
@@ -147,7 +162,8 @@ def test_backward_exact_fit(dt, n, tpr, ch):
     plan would leave partly idle take the fewest wavefronts (over four) that
     divide them exactly; the forward keeps its power-of-two plan."""
     p = rn.layernorm_query_plan(65536, n, dt, which=rn.PASS_BWD_ROWS)
-    assert (p["threads_per_row"], p["chunks"], p["block_threads"]) == (tpr, ch, max(256, tpr))
+    block = 512 if _bwd_rows(n, 4 if dt == 0 else 2, 16) else max(256, tpr)
+    assert (p["threads_per_row"], p["chunks"], p["block_threads"]) == (tpr, ch, block)
     assert p["threads_per_row"] * p["chunks"] * p["vec"] == n
     a = rn.rmsnorm_add_query_plan(65536, n, dt, which=rn.PASS_BWD_ROWS)
     assert (a["threads_per_row"], a["chunks"]) == (tpr, ch)

@@ -139,6 +139,45 @@ def test_degenerate_rows(cuda, scale, shift, dtype):
         assert torch.equal(out["y"].cpu(), inp["b"].expand(16, 5120))
 
 
+# Backward rows of 257-512 16-byte vectors with a 16-byte layout: the
+# two-rows-per-workgroup kernel with x in LDS (one row, an odd row count
+# leaving the second row group of a workgroup idle, more row groups than
+# workgroups, a ragged last chunk, every dtype).
+BWD_ROWS = [((1, 4096), torch.bfloat16), ((2, 2056), torch.bfloat16),
+            ((3, 3000), torch.bfloat16), ((1025, 4096), torch.bfloat16),
+            ((777, 2056), torch.float16), ((5, 4088), torch.float16),
+            ((513, 2048), torch.float32), ((64, 1500), torch.float32), ((2, 1028), torch.float32)]
+
+
+@pytest.mark.parametrize("shape,dtype", BWD_ROWS)
+def test_bwd_rows_kernel(cuda, shape, dtype):
+    M, N = shape
+    plan = rn.layernorm_query_plan(M, N, dtype, which=rn.PASS_BWD_ROWS)
+    assert plan["kernel_name"] == "ln_bwd_rows" and plan["partials"] == min(512, -(-M // 2))
+    inp = workloads.make_layernorm_tile_case(shape, dtype, 53 + N % 89)
+    log(f"case ln bwd rows {shape} {dtype}")
+    out = run_ln_target(inp, cuda)
+    assert_pass(gate_ln_full(inp, out), f"ln bwd rows {shape} {dtype}")
+    x, w, dy = (inp[k].to(cuda) for k in ("x", "w", "dy"))
+    again = rn.ln_bwd(dy, x, w, out["mean"], out["rstd"], poison=True)
+    torch.cuda.synchronize()
+    for k, t in zip(("dx", "dgamma", "dbeta"), again):
+        assert torch.equal(out[k], t), k
+
+
+@pytest.mark.parametrize("scale,shift,dtype", [(1e-3, 50.0, torch.float32),
+                                               (1e-2, 8.0, torch.bfloat16),
+                                               (0.0, 3.0, torch.float16)])
+def test_bwd_rows_degenerate(cuda, scale, shift, dtype):
+    """The cancelling-mean and constant rows on the two-rows kernel."""
+    N = 2048 if dtype == torch.float32 else 4096
+    inp = workloads.make_layernorm_tile_case((16, N), dtype, 43, scale=scale, shift_std=shift)
+    assert rn.layernorm_query_plan(16, N, dtype, which=rn.PASS_BWD_ROWS)["kernel_name"] == \
+        "ln_bwd_rows"
+    log(f"case ln bwd rows degenerate scale={scale} shift={shift} {dtype}")
+    assert_pass(gate_ln_full(inp, run_ln_target(inp, cuda)), f"ln bwd rows degenerate {dtype}")
+
+
 def test_no_bias(cuda):
     inp = workloads.make_layernorm_inputs("c2", M=300, N=4096)
     out = run_ln_target(inp, cuda, bias=False)
