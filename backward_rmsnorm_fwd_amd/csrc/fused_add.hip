@@ -91,7 +91,8 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_fwd_kernel(
         for (int k = 0; k < VEC; ++k) sum[k] = xv[j][c].get(k) + rv[j][c].get(k);
         hv[j][c].set(sum);
         const int e = (c * rg.tpr + rg.t) * VEC;
-        if (active[j] && c < chunks && e < N) st<DT, VEC>(hv[j][c], hr, e);
+        // h is stored cacheably: the backward reads it again
+        if (active[j] && c < chunks && e < N) st<DT, VEC, false>(hv[j][c], hr, e);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
           const float f = hv[j][c].get(k);
@@ -137,8 +138,10 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_bwd_kernel(
   const float n_f = static_cast<float>(N);
   int parity = 0;
   // Steps of G*R consecutive rows; workgroup w takes steps w, w+P, w+2P, ...
-  // (one contiguous window of the matrices at a time across the grid), and
-  // each row group adds its rows to the column sums in row order.
+  // counted from the last step (one contiguous window of the matrices at a
+  // time across the grid, from the rows whose h the forward wrote last and
+  // left in cache back to the first), and each row group adds its rows to
+  // the column sums in step order, row order within a step.
   const int64_t w = blockIdx.x;
   const int64_t step = static_cast<int64_t>(rg.G) * R;
   const int64_t nsteps = (M + step - 1) / step;
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(BLK, BLK == 256 ? 3 : 1) void add_rms_bwd_kernel(
     PK dv[R][MAXC], hv[R][MAXC], ev[R][MAXC];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      row[j] = (it * P + w) * step + j * rg.G + rg.group;
+      row[j] = (nsteps - 1 - (it * P + w)) * step + j * rg.G + rg.group;
       active[j] = row[j] < M;
       r[j] = active[j] ? rstd[row[j]] : 0.f;
       const char* dyr = row_base<DT>(dy, row[j], lddy);

@@ -157,12 +157,16 @@ __device__ __forceinline__ void ld(Pack<DT, VEC>& v, const char* row, int e) {
   else v.raw = *a;
 }
 
-template <int DT, int VEC>
+// NT: streaming store (the default); without it the line is cached as
+// usual, for data a later kernel reads back.
+template <int DT, int VEC, bool NT = true>
 __device__ __forceinline__ void st(const Pack<DT, VEC>& v, const char* row, int e) {
   uint32_t off = static_cast<uint32_t>(e) * ElemBytes<DT>::value;
   asm volatile("" : "+v"(off));
   using R = typename Pack<DT, VEC>::raw_t;
-  __builtin_nontemporal_store(v.raw, reinterpret_cast<R*>(const_cast<char*>(row) + off));
+  R* a = reinterpret_cast<R*>(const_cast<char*>(row) + off);
+  if constexpr (NT) __builtin_nontemporal_store(v.raw, a);
+  else *a = v.raw;
 }
 
 // Rows each row group takes per step: two when the rows' data fits in 16
