@@ -211,6 +211,13 @@ __global__ __launch_bounds__(BLOCK) void ln_bwd_rows_kernel(
 
 template <int DT>
 hipError_t ln_bwd_rows_dt(int64_t P, int64_t lds, const LnBwdArgs& a, hipStream_t s) {
+  // 16-byte rows that fill more than the first of the two chunk sweeps (only
+  // the last may be partial), and LDS for both rows of x.
+  constexpr int64_t kSweepBytes = 4 * kWave * 16;
+  const int64_t row_bytes = int64_t(a.N) * ElemBytes<DT>::value;
+  if (row_bytes % 16 != 0 || row_bytes <= kSweepBytes || row_bytes > 2 * kSweepBytes ||
+      lds < 2 * row_bytes || P < 1)
+    return hipErrorInvalidValue;
   return launch(ln_bwd_rows_kernel<DT, 2, 4, 512, kRowsReverse>, P, 512,
                 static_cast<size_t>(lds), s, a.dy, a.x, a.gamma, a.mean, a.rstd, a.dx, a.part,
                 a.M, a.N, P, a.dy_pitch, a.x_pitch, a.dx_pitch);
