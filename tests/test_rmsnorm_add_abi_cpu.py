@@ -85,6 +85,12 @@ def test_plans_follow_the_row_resident_plan(dt):
                 b = rn.layernorm_query_plan(m, n, dt, which=which)
                 keys = ["vec", "threads_per_row", "block_threads", "chunks", "partials",
                         "lds_bytes"] + ([] if which == rn.PASS_FWD else ["grid"])
+                lnb = rn.layernorm_query_plan(m, n, dt, which=rn.PASS_BWD_ROWS)
+                if which != rn.PASS_FWD and lnb["kernel_name"] == "ln_bwd_rows":
+                    # LayerNorm's own two-rows backward (and its P) for 4-8 KiB
+                    # rows; the fused add keeps the row-resident plan
+                    keys = ["vec", "block_threads", "grid"] if which == rn.PASS_BWD_REDUCE else []
+                    assert a["partials"] == min(512, m)
                 for k in keys:
                     assert a[k] == b[k], (n, m, which, k)
                 if which == rn.PASS_FWD:
