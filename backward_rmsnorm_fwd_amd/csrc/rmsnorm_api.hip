@@ -924,7 +924,8 @@ int bwd_rows_launch(const void* dy, int64_t lddy, const void* x, int64_t ldx, co
 // input dtype with RMSNORM_FLAG_DGAMMA_IN_DTYPE), with the stage-2 kernel
 // fill_plan picks for (P, N).
 int reduce_columns(const float* part, int64_t P, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
-                   void* dst, hipStream_t stream);
+                   void* dst, hipStream_t stream, const float* part_b = nullptr,
+                   void* dst_b = nullptr);
 
 // Stage 2 after its arguments were checked.
 int bwd_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_t dtype,
@@ -933,23 +934,26 @@ int bwd_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype
                         flags, dgamma, stream);
 }
 
+// part_b / dst_b: a second [P, N] block reduced in the same launch (the
+// grid doubles; its second half takes the second block).
 int reduce_columns(const float* part, int64_t P, int64_t N, rmsnorm_dtype_t dtype, uint32_t flags,
-                   void* dgamma, hipStream_t stream) {
+                   void* dgamma, hipStream_t stream, const float* part_b, void* dst_b) {
   rmsnorm_plan_t p;
   fill_reduce_plan(P, N, &p);
+  if (part_b) p.grid *= 2;
   const int n = static_cast<int>(N);
   const int out = (flags & RMSNORM_FLAG_DGAMMA_IN_DTYPE) ? static_cast<int>(dtype) : kOutF32;
 #define RMSNORM_REDUCE(OUT)                                                                   \
   switch (p.kernel) {                                                                         \
     case RMSNORM_KERNEL_BWD_REDUCE16:                                                         \
       return status_of(launch(bwd_reduce16_kernel<OUT>, p.grid, p.block_threads, 0, stream,   \
-                              part, dgamma, p.partials, n));                                  \
+                              part, dgamma, p.partials, n, part_b, dst_b));                   \
     case RMSNORM_KERNEL_BWD_REDUCE_WIDE:                                                      \
       return status_of(launch(bwd_reduce_wide_kernel<OUT>, p.grid, p.block_threads, 0, stream, \
-                              part, dgamma, p.partials, n));                                  \
+                              part, dgamma, p.partials, n, part_b, dst_b));                   \
     default:                                                                                  \
       return status_of(launch(bwd_reduce_kernel<OUT>, p.grid, p.block_threads, 0, stream,     \
-                              part, dgamma, p.partials, n));                                  \
+                              part, dgamma, p.partials, n, part_b, dst_b));                   \
   }
   switch (out) {
     case kF32: RMSNORM_REDUCE(kF32);
@@ -1221,9 +1225,12 @@ int ln_reduce_launch(const void* workspace, int64_t M, int64_t N, rmsnorm_dtype_
                      uint32_t flags, void* dgamma, void* dbeta, hipStream_t stream) {
   const int64_t P = layernorm_partials(M, N, elem_bytes(dtype));
   const float* part = static_cast<const float*>(workspace);
+  // dgamma and dbeta in one launch
+  if (dbeta && M > 0)
+    return reduce_columns(part, P, N, dtype, flags, dgamma, stream, part + P * N, dbeta);
   int st = reduce_columns(part, P, N, dtype, flags, dgamma, stream);
   if (st != RMSNORM_OK || !dbeta) return st;
-  return reduce_columns(M > 0 ? part + P * N : part, P, N, dtype, flags, dbeta, stream);
+  return reduce_columns(part, P, N, dtype, flags, dbeta, stream);
 }
 
 int check_ln_reduce_args(const void* workspace, size_t workspace_bytes, int64_t M, int64_t N,

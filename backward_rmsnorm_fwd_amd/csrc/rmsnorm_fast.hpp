@@ -1111,12 +1111,21 @@ constexpr int64_t bwd_fast_lds_bytes(int N) {
 // ---------------------------------------------------------------------------
 template <int OUT>
 static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce16_kernel(
-    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N,
+    const float* __restrict__ part_b, void* __restrict__ dgamma_b) {
+  // A second [P, N] block (part_b, for LayerNorm's dbeta): the grid's
+  // second half reduces it into dgamma_b, the same way.
+  int bx = static_cast<int>(blockIdx.x);
+  if (part_b != nullptr && bx >= static_cast<int>(gridDim.x / 2)) {
+    bx -= static_cast<int>(gridDim.x / 2);
+    part = part_b;
+    dgamma = dgamma_b;
+  }
   constexpr int kQuads = 4, kSlices = 64;
   __shared__ double sums[kSlices][kQuads * 4 + 1];
   const int q = threadIdx.x % kQuads;
   const int s = threadIdx.x / kQuads;
-  const int col = blockIdx.x * (kQuads * 4) + q * 4;
+  const int col = bx * (kQuads * 4) + q * 4;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   if (col < N) {
     // Unrolled so that a thread's loads are in flight together; the adds
@@ -1136,7 +1145,7 @@ static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce
   sums[s][q * 4 + 3] = a3;
   __syncthreads();
   if (threadIdx.x < kQuads * 4) {
-    const int c = blockIdx.x * (kQuads * 4) + threadIdx.x;
+    const int c = bx * (kQuads * 4) + threadIdx.x;
     if (c < N) {
       double tot = 0.0;
       for (int i = 0; i < kSlices; ++i) tot += sums[i][threadIdx.x];
@@ -1154,13 +1163,22 @@ static __global__ __launch_bounds__(256) __attribute__((unused)) void bwd_reduce
 // ---------------------------------------------------------------------------
 template <int OUT>
 static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduce_wide_kernel(
-    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N,
+    const float* __restrict__ part_b, void* __restrict__ dgamma_b) {
+  // A second [P, N] block (part_b, for LayerNorm's dbeta): the grid's
+  // second half reduces it into dgamma_b, the same way.
+  int bx = static_cast<int>(blockIdx.x);
+  if (part_b != nullptr && bx >= static_cast<int>(gridDim.x / 2)) {
+    bx -= static_cast<int>(gridDim.x / 2);
+    part = part_b;
+    dgamma = dgamma_b;
+  }
   constexpr int kCols = 256;
   __shared__ double sums[kMaxWavesPerBlock][kCols];
   const int lane = threadIdx.x & (kWave - 1);
   const int s = threadIdx.x / kWave;
   const int S = blockDim.x / kWave;
-  const int64_t col = static_cast<int64_t>(blockIdx.x) * kCols + lane * 4;
+  const int64_t col = static_cast<int64_t>(bx) * kCols + lane * 4;
   double a[4] = {0.0, 0.0, 0.0, 0.0};
   if (col < N) {
 #pragma unroll 8
@@ -1182,7 +1200,7 @@ static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduc
   __syncthreads();
   // blockDim.x is 128 .. 1024: each thread finishes every blockDim.x-th column.
   for (int j = threadIdx.x; j < kCols; j += blockDim.x) {
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * kCols + j;
+    const int64_t c = static_cast<int64_t>(bx) * kCols + j;
     if (c < N) {
       double tot = 0.0;
       for (int i = 0; i < S; ++i) tot += sums[i][j];

@@ -615,12 +615,21 @@ __device__ __forceinline__ void store_dgamma(void* dgamma, int64_t j, double tot
 
 template <int OUT>
 static __global__ __launch_bounds__(1024) __attribute__((unused)) void bwd_reduce_kernel(
-    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N) {
+    const float* __restrict__ part, void* __restrict__ dgamma, int64_t P, int N,
+    const float* __restrict__ part_b, void* __restrict__ dgamma_b) {
   __shared__ double sums[kMaxWavesPerBlock][kWave];
+  // A second [P, N] block (part_b, for LayerNorm's dbeta): the grid's
+  // second half reduces it into dgamma_b, the same way.
+  int bx = static_cast<int>(blockIdx.x);
+  if (part_b != nullptr && bx >= static_cast<int>(gridDim.x / 2)) {
+    bx -= static_cast<int>(gridDim.x / 2);
+    part = part_b;
+    dgamma = dgamma_b;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int s = threadIdx.x / kWave;
   const int S = blockDim.x / kWave;
-  const int col = blockIdx.x * kWave + lane;
+  const int col = bx * kWave + lane;
   double acc = 0.0;
   if (col < N) {
     for (int64_t p = s; p < P; p += S)
