@@ -170,6 +170,38 @@ def gate_ln_full(inp, out, bias=True):
     return rows
 
 
+def gate_ln_full_chunked(inp, out, chunk_rows=8192):
+    """Gate every element of a full-size LayerNorm run, a block of rows at a
+    time: y and dx through gate.TensorGate (golden and reference computed
+    per block), mean and rstd whole from the per-block statistics, dgamma
+    and dbeta whole (their golden accumulated in row blocks)."""
+    x, w, b, dy, eps, T = inp["x"], inp["w"], inp["b"], inp["dy"], inp["eps"], inp["x"].dtype
+    M, n = x.shape[0], x.shape[-1]
+    gy = gate.TensorGate("y", T, (M, n))
+    gdx = gate.TensorGate("dx", T, (M, n))
+    mu_g, r_g, xmax = np.empty(M), np.empty(M), np.empty(M)
+    r_r = torch.empty(M, dtype=torch.float32)
+    for a in range(0, M, chunk_rows):
+        e = min(M, a + chunk_rows)
+        xs, dys = x[a:e], dy[a:e]
+        y_r, _, r_r[a:e] = lnref.reference_ln_forward(xs, w, b, eps)
+        dx_r, _, _ = lnref.reference_ln_backward(dys, xs, w, eps)
+        y_g, mu_g[a:e], r_g[a:e] = lnref.golden_ln_forward(xs, w, b, eps)
+        dx_g = lnref.golden_ln_dx(dys, xs, w, eps)
+        xmax[a:e] = xs.abs().amax(1).double().numpy()
+        gy.add(out["y"][a:e].cpu(), y_r, y_g)
+        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
+    dg_g, db_g = lnref.golden_ln_param_grads(dy, x, eps)
+    dg_r, db_r = lnref.reference_ln_param_grads(dy, x, eps)
+    dg_t = out["dgamma"].cpu()
+    worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
+    cg, _ = lnref.ln_param_condition(dy, x, eps, worst)
+    return [gy.finish(), gate.gate_mean(out["mean"].cpu(), mu_g, xmax),
+            gate.gate_rstd(out["rstd"].cpu(), r_g, r_r), gdx.finish(),
+            gate.gate_tensor("dgamma", dg_t, dg_r, dg_g, torch.float32, condition=cg),
+            gate.gate_tensor("dbeta", out["dbeta"].cpu(), db_r, db_g, torch.float32)]
+
+
 def gate_ln_sampled(inp, out, rows, cols):
     """Sampled rows of y, mean, rstd, dx; sampled columns of dgamma and dbeta
     (still sums over all M rows)."""

@@ -3,15 +3,16 @@ against the LayerNorm oracle (oracle.layernorm): every element of y, mean,
 rstd, dx, dgamma and dbeta at reduced sizes of each recipe, tile-boundary
 and degenerate rows, misaligned and strided layouts, rows longer than the
 row-resident limit (the split-row plan), and the c2, c3, c4 and c5 shapes at
-full size on sampled rows and columns."""
+full size on every element (the oracle a block of rows at a time) and on
+sampled rows and columns."""
 import numpy as np
 import pytest
 import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from backward_rmsnorm_fwd_amd import workloads
-from parity import (assert_pass, gate_ln_full, gate_ln_sampled, log, run_ln_target,
-                    sample_cols, sample_rows)
+from parity import (assert_pass, gate_ln_full, gate_ln_full_chunked, gate_ln_sampled, log,
+                    run_ln_target, sample_cols, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -197,6 +198,22 @@ def test_full_size_sampled(cuda, name, M, N, nrows):
     assert_pass(gate_ln_sampled(inp, out, rows, cols), f"ln {name} full size, sampled")
     for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
         assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
+@pytest.mark.parametrize("name,kernel", [("c2", "ln_bwd_rows"), ("c3", "ln_bwd"),
+                                         ("c4", "ln_bwd_split"), ("c5", "ln_bwd")])
+def test_full_size_every_element(cuda, name, kernel):
+    """Each workload at full size in the plan bench.py --op layernorm times
+    (c2's two-rows backward, c3 and c5 row-resident, c4 split rows): every
+    element of y, mean, rstd, dx, dgamma and dbeta gated, the oracle
+    evaluated a block of rows at a time."""
+    inp = workloads.make_layernorm_inputs(name)
+    log(f"case ln {name} full size M={inp['M']} N={inp['N']} generated")
+    assert rn.layernorm_query_plan(inp["M"], inp["N"], inp["x"].dtype,
+                                   which=rn.PASS_BWD_ROWS)["kernel_name"] == kernel
+    out = run_ln_target(inp, cuda)
+    log(f"case ln {name} device run done")
+    assert_pass(gate_ln_full_chunked(inp, out), f"ln {name} full size, every element")
 
 
 # Rows longer than the row-resident limit: 16 KiB segments (4096 float32 or
