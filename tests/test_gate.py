@@ -258,3 +258,30 @@ def test_page_allclose_logged_as_information():
     b = torch.tensor(g, dtype=torch.bfloat16)
     assert "allclose" not in gate.gate_tensor("t", b, b, g, torch.bfloat16).extra
     assert "Page allclose" in gate.report([row])
+
+
+@pytest.mark.parametrize("mutation", [None, "dx_scaled", "y_unwritten"])
+def test_layernorm_chunked_gate_equals_whole_gate(mutation):
+    """The row-chunked LayerNorm gate (y and dx a block of rows at a time)
+    gives the same rows as the whole-tensor gate: same verdicts and errors."""
+    from oracle import layernorm as lnref
+    from parity import gate_ln_full, gate_ln_full_chunked
+    inp = workloads.make_layernorm_inputs("c2", M=50, N=512)
+    x, w, b, dy, eps = inp["x"], inp["w"], inp["b"], inp["dy"], inp["eps"]
+    y, mu, r = lnref.reference_ln_forward(x, w, b, eps)
+    dx, dg, db = lnref.reference_ln_backward(dy, x, w, eps)
+    if mutation == "dx_scaled":
+        dx = (dx.float() * 1.01).to(dx.dtype)
+    elif mutation == "y_unwritten":
+        y = y.clone()
+        y[13, 7] = float("nan")
+    out = {"y": y, "mean": mu, "rstd": r, "dx": dx, "dgamma": dg, "dbeta": db}
+    whole = gate_ln_full(inp, out)
+    part = gate_ln_full_chunked(inp, out, chunk_rows=7)
+    assert [p.tensor for p in part] == [w_.tensor for w_ in whole]
+    for p, w_ in zip(part, whole):
+        assert p.verdict == w_.verdict, (p.tensor, mutation)
+        a_, b_ = p.target_error, w_.target_error
+        assert a_ == b_ or (a_ != a_ and b_ != b_), (p.tensor, a_, b_)
+    if mutation:
+        assert gate.overall_verdict(part) == "FAIL"
