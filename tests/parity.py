@@ -266,6 +266,41 @@ def gate_add_full(inp, out, with_dh=True):
     ]
 
 
+def gate_add_full_chunked(inp, out, chunk_rows=8192):
+    """Every element of a full-size fused-add run: h bit-exact whole, y and
+    dx a block of rows at a time (gate.TensorGate), rstd and dgamma whole."""
+    x, res, w, dy, dh = inp["x"], inp["res"], inp["w"], inp["dy"], inp["dh"]
+    eps, off, T = inp["eps"], inp["offset"], inp["x"].dtype
+    M, n = x.shape[0], x.shape[-1]
+    h_o = fusedref.residual_sum(x, res)
+    h_t = out["h"].cpu()
+    h_row = gate.GateRow(tensor="h", dtype=str(T).replace("torch.", ""), shape=tuple(h_o.shape))
+    h_row.gate_valid = True
+    h_row.target_error = float((h_t.double() - h_o.double()).abs().max())
+    h_row.verdict = "PASS" if torch.equal(h_t, h_o) else "FAIL"
+    h_row.note = "bitwise equal to the dtype's add"
+    gy = gate.TensorGate("y", T, (M, n))
+    gdx = gate.TensorGate("dx", T, (M, n))
+    r_g = np.empty(M)
+    r_r = torch.empty(M, dtype=torch.float32)
+    for a in range(0, M, chunk_rows):
+        e = min(M, a + chunk_rows)
+        xs, rs, dys, dhs, hs = x[a:e], res[a:e], dy[a:e], dh[a:e], h_o[a:e]
+        _, y_r, r_r[a:e] = fusedref.reference_add_forward(xs, rs, w, eps, off)
+        _, y_g, r_g[a:e] = fusedref.golden_add_forward(xs, rs, w, eps, off)
+        dx_r, _ = fusedref.reference_add_backward(dys, dhs, hs, w, eps, off)
+        dx_g = fusedref.golden_add_dx(dys, dhs, hs, w, eps, off)
+        gy.add(out["y"][a:e].cpu(), y_r, y_g)
+        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
+    dg_g = golden.golden_dgamma(dy, h_o, eps)
+    dg_r = reference.reference_dgamma(dy, h_o, eps)
+    dg_t = out["dgamma"].cpu()
+    worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
+    cond = golden.dgamma_condition(dy, h_o, eps, worst)
+    return [h_row, gy.finish(), gate.gate_rstd(out["rstd"].cpu(), r_g, r_r), gdx.finish(),
+            gate.gate_tensor("dgamma", dg_t, dg_r, dg_g, torch.float32, condition=cond)]
+
+
 def gate_add_sampled(inp, out, rows, cols):
     """Sampled rows of h (bit-exact), y, rstd and dx, and sampled columns of
     dgamma (sums over all rows), against the fused-add oracle."""
@@ -327,6 +362,34 @@ def gate_cast_full(inp, out):
         gate.gate_tensor("dgamma", out["dgamma"].cpu(), dg_r, dg_g, torch.float32,
                          condition=cond),
     ]
+
+
+def gate_cast_full_chunked(inp, out, chunk_rows=8192):
+    """Every element of a full-size cast run, y and dx a block of rows at a
+    time (gate.TensorGate), rstd and dgamma whole."""
+    x, w, dy, eps, off = inp["x"], inp["w"], inp["dy"], inp["eps"], inp["offset"]
+    To = inp["out_dtype"]
+    M, n = x.shape[0], x.shape[-1]
+    gy = gate.TensorGate("y", To, (M, n))
+    gdx = gate.TensorGate("dx", torch.float32, (M, n))
+    r_g = np.empty(M)
+    r_r = torch.empty(M, dtype=torch.float32)
+    for a in range(0, M, chunk_rows):
+        e = min(M, a + chunk_rows)
+        xs, dys = x[a:e], dy[a:e]
+        y_r, r_r[a:e] = fusedref.reference_cast_forward(xs, w, To, eps, off)
+        y_g, r_g[a:e] = fusedref.golden_cast_forward(xs, w, eps, off)
+        dx_r, _ = fusedref.reference_cast_backward(dys, xs, w, eps, off)
+        dx_g = fusedref.golden_cast_dx(dys, xs, w, eps, off)
+        gy.add(out["y"][a:e].cpu(), y_r, y_g)
+        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
+    dg_g = golden.golden_dgamma(dy, x, eps)
+    dg_r = reference.reference_dgamma(dy.float(), x, eps)
+    dg_t = out["dgamma"].cpu()
+    worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
+    cond = golden.dgamma_condition(dy, x, eps, worst)
+    return [gy.finish(), gate.gate_rstd(out["rstd"].cpu(), r_g, r_r), gdx.finish(),
+            gate.gate_tensor("dgamma", dg_t, dg_r, dg_g, torch.float32, condition=cond)]
 
 
 def gate_cast_sampled(inp, out, rows, cols):

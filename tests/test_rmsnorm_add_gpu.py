@@ -4,15 +4,15 @@ bitwise equal to the dtype's add, y, rstd, dx (RMSNorm's gradient plus dh)
 and dgamma through the gate, at reduced sizes of each recipe, tile and edge
 shapes, rows longer than the row-resident limit (full-width rows of up to
 128 KiB on the long-row kernels, other layouts on the split-row plan),
-misaligned and strided layouts, without dh, c2 at full size on every
-element and c3, c4, c5 at full size on sampled rows and columns."""
+misaligned and strided layouts, without dh, and c2, c3, c4, c5 at full size
+on every element (c3-c5 also on sampled rows and columns)."""
 import pytest
 import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from backward_rmsnorm_fwd_amd import workloads
-from parity import (assert_pass, gate_add_full, gate_add_sampled, log, run_add_target,
-                    sample_cols, sample_rows)
+from parity import (assert_pass, gate_add_full, gate_add_full_chunked, gate_add_sampled, log,
+                    run_add_target, sample_cols, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,18 @@ def test_full_size_sampled(cuda, name, nrows):
     assert_pass(gate_add_sampled(inp, out, rows, cols), f"add {name} full size, sampled")
     for k in ("y", "h", "dx", "rstd", "dgamma"):
         assert not torch.isnan(out[k]).any(), f"{k} has unwritten (NaN) elements"
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_full_size_every_element_chunked(cuda, name):
+    """The c3, c4 and c5 shapes at full size in the default plan: h
+    bit-exact and every element of y, rstd, dx and dgamma gated, the oracle
+    a block of rows at a time."""
+    inp = workloads.make_add_inputs(name)
+    log(f"case add {name} full size M={inp['M']} N={inp['N']} generated")
+    out = run_add_target(inp, cuda)
+    log(f"case add {name} device run done")
+    assert_pass(gate_add_full_chunked(inp, out), f"add {name} full size, every element")
 
 
 def test_reproducible_offset_and_dgamma_in_dtype(cuda):

@@ -4,15 +4,16 @@ bfloat16 or float16 (gated at that dtype's rounding floor), rstd, dx and
 dgamma (float32, from dy in the narrow dtype) through the gate, at reduced
 sizes of each recipe, edge shapes, rows longer than the row-resident limit
 (the split-row plan), misaligned and strided layouts, the offset weight,
-the c2, c3, c4 and c5 shapes at full size on sampled rows and columns, and
-against the unfused pair (float32 RMSNorm, then PyTorch's cast)."""
+the c2, c3, c4 and c5 shapes at full size on every element and on sampled
+rows and columns, and against the unfused pair (float32 RMSNorm, then
+PyTorch's cast)."""
 import pytest
 import torch
 
 import backward_rmsnorm_fwd_amd as rn
 from backward_rmsnorm_fwd_amd import workloads
-from parity import (assert_pass, gate_cast_full, gate_cast_sampled, log, run_cast_target,
-                    sample_cols, sample_rows)
+from parity import (assert_pass, gate_cast_full, gate_cast_full_chunked, gate_cast_sampled, log,
+                    run_cast_target, sample_cols, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +72,19 @@ def test_full_size_shape_sampled(cuda, name, out_dtype):
     rows = sample_rows(inp, 64)
     cols = sample_cols(inp["N"], 96)
     assert_pass(gate_cast_sampled(inp, out, rows, cols), f"cast {name} shape full size, sampled")
+
+
+@pytest.mark.parametrize("name,out_dtype", [("c2", torch.bfloat16), ("c3", torch.float16),
+                                            ("c4", torch.bfloat16), ("c5", torch.bfloat16)])
+def test_full_size_every_element(cuda, name, out_dtype):
+    """Each benchmarked shape at full size in the default plan: every
+    element of y, rstd, dx and dgamma gated, the oracle a block of rows at
+    a time."""
+    inp = workloads.make_cast_inputs(name, out_dtype=out_dtype)
+    log(f"case cast {name} full size generated")
+    out = run_cast_target(inp, cuda)
+    log(f"case cast {name} device run done")
+    assert_pass(gate_cast_full_chunked(inp, out), f"cast {name} full size, every element")
 
 
 def test_reproducible_offset(cuda):
