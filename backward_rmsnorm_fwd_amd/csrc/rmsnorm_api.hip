@@ -1060,8 +1060,9 @@ int64_t ln_partials(int64_t M, int64_t N, int es) {
 // layernorm_rows.hip's kernel, on RMSNorm's bwd_rows geometry: four
 // wavefronts x two chunks per row, two rows per 512-thread workgroup, x in
 // LDS, rows swept back to front, P = min(ceil(M/2), 512).  bf16 32768 x 4096
-// stage 1: see the LayerNorm notes.  A layout that is not 16-byte aligned
-// runs the row-resident kernel on the same P.
+// in a forward -> stage 1 loop: stage 1 121 against 127 us for the
+// row-resident kernel (the forward loading x cacheably in both).  A layout
+// that is not 16-byte aligned runs the row-resident kernel on the same P.
 constexpr int kLnRowsWpr = 4, kLnRowsChunks = 2, kLnRowsBlock = 512;
 constexpr int64_t kLnRowsWorkgroups = 512;
 
