@@ -3,6 +3,7 @@ oracle (golden + reference) on the same seeded inputs."""
 from __future__ import annotations
 
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -50,6 +51,28 @@ def gate_full(inp, out):
     ]
 
 
+def blocks_in_order(M, chunk_rows, work, workers=4):
+    """Yield (a, b, work(a, b)) for the row blocks [a, b) of [0, M) in
+    order.  The blocks' oracle work runs a few at a time in threads (NumPy
+    and torch release the interpreter lock in their array loops), and at
+    most `workers` blocks' results are held; the caller consumes them in
+    block order, so everything it accumulates is as in a serial loop."""
+    spans = [(a, min(M, a + chunk_rows)) for a in range(0, M, chunk_rows)]
+    with ThreadPoolExecutor(workers) as ex:
+        for i in range(0, len(spans), workers):
+            futures = [(a, b, ex.submit(work, a, b)) for a, b in spans[i:i + workers]]
+            for a, b, f in futures:
+                yield a, b, f.result()
+
+
+def add_together(*feeds):
+    """Feed independent TensorGates one block each at the same time, each in
+    a thread of its own (every gate still sees its blocks in order)."""
+    with ThreadPoolExecutor(len(feeds)) as ex:
+        for f in [ex.submit(g.add, *args) for g, args in feeds]:
+            f.result()
+
+
 def gate_full_chunked(inp, out, chunk_rows=8192):
     """Gate every element of a full-size run, a block of rows at a time.
 
@@ -65,17 +88,22 @@ def gate_full_chunked(inp, out, chunk_rows=8192):
     gdx = gate.TensorGate("dx", T, (M, n))
     r_g = np.empty(M)
     r_r = torch.empty(M, dtype=torch.float32)
-    for a in range(0, M, chunk_rows):
-        b = min(M, a + chunk_rows)
+
+    def work(a, b):
         xs, dys = x[a:b], dy[a:b]
-        y_r, r_r[a:b] = reference.reference_forward(xs, w, eps, off)
+        y_r, rr = reference.reference_forward(xs, w, eps, off)
         dx_r, _ = reference.reference_backward(dys, xs, w, eps, off)
-        y_g, r_g[a:b] = golden.golden_forward(xs, w, eps, off)
-        dx_g = golden.golden_dx(dys, xs, w, eps, off)
-        gy.add(out["y"][a:b].cpu(), y_r, y_g)
-        gdx.add(out["dx"][a:b].cpu(), dx_r, dx_g)
-    dg_g = golden.golden_dgamma(dy, x, eps)
-    dg_r = reference.reference_dgamma(dy, x, eps)
+        y_g, rg = golden.golden_forward(xs, w, eps, off)
+        return y_r, rr, dx_r, y_g, rg, golden.golden_dx(dys, xs, w, eps, off)
+
+    with ThreadPoolExecutor(1) as side:  # the column sums meanwhile
+        dg = side.submit(lambda: (golden.golden_dgamma(dy, x, eps),
+                                  reference.reference_dgamma(dy, x, eps)))
+        for a, b, (y_r, rr, dx_r, y_g, rg, dx_g) in blocks_in_order(M, chunk_rows, work):
+            r_r[a:b], r_g[a:b] = rr, rg
+            add_together((gy, (out["y"][a:b].cpu(), y_r, y_g)),
+                         (gdx, (out["dx"][a:b].cpu(), dx_r, dx_g)))
+        dg_g, dg_r = dg.result()
     dg_t = out["dgamma"].cpu()
     worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
     cond = golden.dgamma_condition(dy, x, eps, worst)
@@ -181,18 +209,24 @@ def gate_ln_full_chunked(inp, out, chunk_rows=8192):
     gdx = gate.TensorGate("dx", T, (M, n))
     mu_g, r_g, xmax = np.empty(M), np.empty(M), np.empty(M)
     r_r = torch.empty(M, dtype=torch.float32)
-    for a in range(0, M, chunk_rows):
-        e = min(M, a + chunk_rows)
+
+    def work(a, e):
         xs, dys = x[a:e], dy[a:e]
-        y_r, _, r_r[a:e] = lnref.reference_ln_forward(xs, w, b, eps)
+        y_r, _, rr = lnref.reference_ln_forward(xs, w, b, eps)
         dx_r, _, _ = lnref.reference_ln_backward(dys, xs, w, eps)
-        y_g, mu_g[a:e], r_g[a:e] = lnref.golden_ln_forward(xs, w, b, eps)
+        y_g, mg, rg = lnref.golden_ln_forward(xs, w, b, eps)
         dx_g = lnref.golden_ln_dx(dys, xs, w, eps)
-        xmax[a:e] = xs.abs().amax(1).double().numpy()
-        gy.add(out["y"][a:e].cpu(), y_r, y_g)
-        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
-    dg_g, db_g = lnref.golden_ln_param_grads(dy, x, eps)
-    dg_r, db_r = lnref.reference_ln_param_grads(dy, x, eps)
+        return y_r, rr, dx_r, y_g, mg, rg, dx_g, xs.abs().amax(1).double().numpy()
+
+    with ThreadPoolExecutor(1) as side:  # the column sums meanwhile
+        pg = side.submit(lambda: (lnref.golden_ln_param_grads(dy, x, eps),
+                                  lnref.reference_ln_param_grads(dy, x, eps)))
+        for a, e, (y_r, rr, dx_r, y_g, mg, rg, dx_g, xm) in blocks_in_order(M, chunk_rows,
+                                                                             work):
+            r_r[a:e], mu_g[a:e], r_g[a:e], xmax[a:e] = rr, mg, rg, xm
+            add_together((gy, (out["y"][a:e].cpu(), y_r, y_g)),
+                         (gdx, (out["dx"][a:e].cpu(), dx_r, dx_g)))
+        (dg_g, db_g), (dg_r, db_r) = pg.result()
     dg_t = out["dgamma"].cpu()
     worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
     cg, _ = lnref.ln_param_condition(dy, x, eps, worst)
@@ -283,17 +317,22 @@ def gate_add_full_chunked(inp, out, chunk_rows=8192):
     gdx = gate.TensorGate("dx", T, (M, n))
     r_g = np.empty(M)
     r_r = torch.empty(M, dtype=torch.float32)
-    for a in range(0, M, chunk_rows):
-        e = min(M, a + chunk_rows)
+
+    def work(a, e):
         xs, rs, dys, dhs, hs = x[a:e], res[a:e], dy[a:e], dh[a:e], h_o[a:e]
-        _, y_r, r_r[a:e] = fusedref.reference_add_forward(xs, rs, w, eps, off)
-        _, y_g, r_g[a:e] = fusedref.golden_add_forward(xs, rs, w, eps, off)
+        _, y_r, rr = fusedref.reference_add_forward(xs, rs, w, eps, off)
+        _, y_g, rg = fusedref.golden_add_forward(xs, rs, w, eps, off)
         dx_r, _ = fusedref.reference_add_backward(dys, dhs, hs, w, eps, off)
-        dx_g = fusedref.golden_add_dx(dys, dhs, hs, w, eps, off)
-        gy.add(out["y"][a:e].cpu(), y_r, y_g)
-        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
-    dg_g = golden.golden_dgamma(dy, h_o, eps)
-    dg_r = reference.reference_dgamma(dy, h_o, eps)
+        return y_r, rr, y_g, rg, dx_r, fusedref.golden_add_dx(dys, dhs, hs, w, eps, off)
+
+    with ThreadPoolExecutor(1) as side:  # the column sums meanwhile
+        dg = side.submit(lambda: (golden.golden_dgamma(dy, h_o, eps),
+                                  reference.reference_dgamma(dy, h_o, eps)))
+        for a, e, (y_r, rr, y_g, rg, dx_r, dx_g) in blocks_in_order(M, chunk_rows, work):
+            r_r[a:e], r_g[a:e] = rr, rg
+            add_together((gy, (out["y"][a:e].cpu(), y_r, y_g)),
+                         (gdx, (out["dx"][a:e].cpu(), dx_r, dx_g)))
+        dg_g, dg_r = dg.result()
     dg_t = out["dgamma"].cpu()
     worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
     cond = golden.dgamma_condition(dy, h_o, eps, worst)
@@ -374,17 +413,22 @@ def gate_cast_full_chunked(inp, out, chunk_rows=8192):
     gdx = gate.TensorGate("dx", torch.float32, (M, n))
     r_g = np.empty(M)
     r_r = torch.empty(M, dtype=torch.float32)
-    for a in range(0, M, chunk_rows):
-        e = min(M, a + chunk_rows)
+
+    def work(a, e):
         xs, dys = x[a:e], dy[a:e]
-        y_r, r_r[a:e] = fusedref.reference_cast_forward(xs, w, To, eps, off)
-        y_g, r_g[a:e] = fusedref.golden_cast_forward(xs, w, eps, off)
+        y_r, rr = fusedref.reference_cast_forward(xs, w, To, eps, off)
+        y_g, rg = fusedref.golden_cast_forward(xs, w, eps, off)
         dx_r, _ = fusedref.reference_cast_backward(dys, xs, w, eps, off)
-        dx_g = fusedref.golden_cast_dx(dys, xs, w, eps, off)
-        gy.add(out["y"][a:e].cpu(), y_r, y_g)
-        gdx.add(out["dx"][a:e].cpu(), dx_r, dx_g)
-    dg_g = golden.golden_dgamma(dy, x, eps)
-    dg_r = reference.reference_dgamma(dy.float(), x, eps)
+        return y_r, rr, y_g, rg, dx_r, fusedref.golden_cast_dx(dys, xs, w, eps, off)
+
+    with ThreadPoolExecutor(1) as side:  # the column sums meanwhile
+        dg = side.submit(lambda: (golden.golden_dgamma(dy, x, eps),
+                                  reference.reference_dgamma(dy.float(), x, eps)))
+        for a, e, (y_r, rr, y_g, rg, dx_r, dx_g) in blocks_in_order(M, chunk_rows, work):
+            r_r[a:e], r_g[a:e] = rr, rg
+            add_together((gy, (out["y"][a:e].cpu(), y_r, y_g)),
+                         (gdx, (out["dx"][a:e].cpu(), dx_r, dx_g)))
+        dg_g, dg_r = dg.result()
     dg_t = out["dgamma"].cpu()
     worst = int(np.argmax(np.abs(dg_t.double().numpy() - dg_g)))
     cond = golden.dgamma_condition(dy, x, eps, worst)
